@@ -1,0 +1,389 @@
+/*
+ * tria_oracle.c -- plain CPU reference of the TriAttention KV-cache eviction
+ * pass (score -> aggregate -> select -> compact).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The product path
+ * (the HIP library) never calls it and shares no code with it.
+ *
+ * Everything is computed in fp64, one (layer, KV head) unit at a time, in the
+ * order the sources describe it, with no blocking or fusion.  The only
+ * parallelism is an OpenMP loop over independent units.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [WL]  "TriAttention Native C++ Worklog" (TensorRT-Model-Connect).
+ *   [LC]  llama.cpp docs page "TriAttention KV-Cache Eviction (--triattention)".
+ *
+ * Notation: L layers, Hkv KV heads, Hq query heads, G = Hq/Hkv, hd head dim,
+ * F = hd/2 RoPE frequency pairs, n cached rows of one unit, B budget, S sink,
+ * W window, D offset set, p reference position.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_KV_F16 0
+#define ORC_KV_Q8_0 1
+
+/* ------------------------------------------------------------------------ */
+/* Key-row decoding.                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16 -> double, written out from the format definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits). Exact. */
+double orc_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)m, -24); /* subnormal (or zero): m * 2^-24 */
+    } else if (e == 31) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* Size in bytes of one stored row of head_dim values.
+ * f16: 2 bytes per value.  q8_0: blocks of 32 values, each block stored as an
+ * fp16 scale followed by 32 signed 8-bit integers (34 bytes) -- the K cache
+ * type the HIP/Vulkan scorers of [LC] read (section 4, "GPU scoring
+ * requirements"; section 5, "Phase C"). */
+int64_t orc_row_bytes(int kv_type, int hd)
+{
+    if (kv_type == ORC_KV_F16) return 2 * (int64_t)hd;
+    if (kv_type == ORC_KV_Q8_0) return 34 * (int64_t)(hd / 32);
+    return -1;
+}
+
+/* Decode one stored key row into hd doubles.  q8_0 value = scale * q. */
+int orc_decode_row(int kv_type, const uint8_t *row, int hd, double *out)
+{
+    if (kv_type == ORC_KV_F16) {
+        for (int d = 0; d < hd; d++) {
+            uint16_t h = (uint16_t)(row[2 * d] | (row[2 * d + 1] << 8));
+            out[d] = orc_half_to_double(h);
+        }
+        return 0;
+    }
+    if (kv_type == ORC_KV_Q8_0) {
+        for (int b = 0; b < hd / 32; b++) {
+            const uint8_t *blk = row + 34 * b;
+            double scale = orc_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+            for (int i = 0; i < 32; i++) out[32 * b + i] = scale * (double)(int8_t)blk[2 + i];
+        }
+        return 0;
+    }
+    return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Query-side trigonometric term.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* RoPE frequency of pair f: theta^(-2f/hd). */
+double orc_omega(double theta, int hd, int f)
+{
+    return pow(theta, -2.0 * (double)f / (double)hd);
+}
+
+/* Mean over the offset set D of the future-query phase, per pair:
+ *   A_f = (1/|D|) * sum_{delta in D} exp(i * omega_f * (p + delta)).
+ * p is the absolute position of the newest cached token, never the cached
+ * row count ([WL], "2026-04-18: later-compaction absolute-position bug
+ * isolated and fixed").  The phase is applied to the query side only
+ * ([WL], "Phase 9: final root cause - native scorer used the wrong
+ * formulation"). */
+void orc_offset_mean(double theta, int hd, int64_t p, const int64_t *offsets, int n_off,
+                     double *a_re, double *a_im)
+{
+    int F = hd / 2;
+    for (int f = 0; f < F; f++) {
+        double w = orc_omega(theta, hd, f);
+        double sr = 0.0, si = 0.0;
+        for (int t = 0; t < n_off; t++) {
+            double ang = w * (double)(p + offsets[t]);
+            sr += cos(ang);
+            si += sin(ang);
+        }
+        a_re[f] = sr / (double)n_off;
+        a_im[f] = si / (double)n_off;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Raw per-query-head score of one unit.                                      */
+/* ------------------------------------------------------------------------ */
+
+/* For the G query heads that share one KV head, and every cached row r:
+ *
+ *   s_j(r) = sum_f Re( qbar_{j,f} * A_f * conj(K_f(r)) ) + sum_f w_{j,f} |K_f(r)|
+ *
+ * with K_f = k[f] + i*k[f+F] (rotate-half / NEOX pairing of the stored,
+ * already-rotated key).  The first sum scores the stored rotated key directly
+ * against the phase-shifted mean query; the second is the additive term on
+ * |K_rot| ([WL], "Phase 9 ..."; [LC] section 5, "Phase C": per-head q_mean
+ * and q_abs statistics).
+ *
+ * k_rows: n rows of row_stride bytes; q_re/q_im/w: [G][F] statistics of the
+ * unit's query heads; raw: output [n][G]. */
+int orc_raw_scores_unit(int kv_type, const uint8_t *k_rows, int64_t row_stride, int64_t n,
+                        int hd, int G, const float *q_re, const float *q_im, const float *w,
+                        double theta, int64_t p, const int64_t *offsets, int n_off, double *raw)
+{
+    int F = hd / 2;
+    double *a_re = (double *)malloc(sizeof(double) * F);
+    double *a_im = (double *)malloc(sizeof(double) * F);
+    double *c_re = (double *)malloc(sizeof(double) * F * G);
+    double *c_im = (double *)malloc(sizeof(double) * F * G);
+    double *k = (double *)malloc(sizeof(double) * hd);
+    if (!a_re || !a_im || !c_re || !c_im || !k) {
+        free(a_re); free(a_im); free(c_re); free(c_im); free(k);
+        return -1;
+    }
+    orc_offset_mean(theta, hd, p, offsets, n_off, a_re, a_im);
+    /* C_{j,f} = qbar_{j,f} * A_f (complex product). */
+    for (int j = 0; j < G; j++) {
+        for (int f = 0; f < F; f++) {
+            double qr = q_re[j * F + f], qi = q_im[j * F + f];
+            c_re[j * F + f] = qr * a_re[f] - qi * a_im[f];
+            c_im[j * F + f] = qr * a_im[f] + qi * a_re[f];
+        }
+    }
+    for (int64_t r = 0; r < n; r++) {
+        orc_decode_row(kv_type, k_rows + r * row_stride, hd, k);
+        for (int j = 0; j < G; j++) {
+            double trig = 0.0, norm = 0.0;
+            for (int f = 0; f < F; f++) {
+                double kre = k[f], kim = k[f + F];
+                /* Re(C * conj(K)) = Cre*Kre + Cim*Kim */
+                trig += c_re[j * F + f] * kre + c_im[j * F + f] * kim;
+                norm += (double)w[j * F + f] * sqrt(kre * kre + kim * kim);
+            }
+            raw[r * G + j] = trig + norm;
+        }
+    }
+    free(a_re); free(a_im); free(c_re); free(c_im); free(k);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GQA aggregation: per-head z-normalisation, then max over the group.        */
+/* ------------------------------------------------------------------------ */
+
+/* [LC] section 5, "Phase C": each query head's scores are z-normalised on
+ * their own, then the KV head's score is the max over its query heads.
+ * Population statistics over every cached row of the unit whose score is
+ * finite; sigma = 0 gives z = 0.  A row with any non-finite head score gets
+ * agg = -inf (evicted unless protected).  mu/sigma: optional [G] outputs. */
+void orc_aggregate_unit(const double *raw, int64_t n, int G, double *agg, double *mu_out,
+                        double *sigma_out)
+{
+    double *mu = (double *)malloc(sizeof(double) * (G > 0 ? G : 1));
+    double *sg = (double *)malloc(sizeof(double) * (G > 0 ? G : 1));
+    for (int j = 0; j < G; j++) {
+        double sum = 0.0;
+        int64_t cnt = 0;
+        for (int64_t r = 0; r < n; r++) {
+            double s = raw[r * G + j];
+            if (isfinite(s)) { sum += s; cnt++; }
+        }
+        double m = cnt ? sum / (double)cnt : 0.0;
+        double ss = 0.0;
+        for (int64_t r = 0; r < n; r++) {
+            double s = raw[r * G + j];
+            if (isfinite(s)) ss += (s - m) * (s - m);
+        }
+        mu[j] = m;
+        sg[j] = cnt ? sqrt(ss / (double)cnt) : 0.0;
+        if (mu_out) mu_out[j] = mu[j];
+        if (sigma_out) sigma_out[j] = sg[j];
+    }
+    for (int64_t r = 0; r < n; r++) {
+        double best = -INFINITY;
+        int bad = 0;
+        for (int j = 0; j < G; j++) {
+            double s = raw[r * G + j];
+            if (!isfinite(s)) { bad = 1; break; }
+            double z = sg[j] > 0.0 ? (s - mu[j]) / sg[j] : 0.0;
+            if (j == 0 || z > best) best = z;
+        }
+        agg[r] = bad ? -INFINITY : best;
+    }
+    free(mu);
+    free(sg);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Selection.                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Protected rows: the first S rows (attention sinks) and the last W rows
+ * (recent window) ([LC] section 5, "Phase B", step 2; section 1 flag table).
+ * Returns the number of protected rows and the candidate range
+ * [*cand_lo, *cand_hi). */
+int64_t orc_protected(int64_t n, int64_t sink, int64_t window, int64_t *cand_lo, int64_t *cand_hi)
+{
+    int64_t s_end = sink < n ? sink : n;
+    int64_t w_start = n - window;
+    if (w_start < s_end) w_start = s_end;
+    *cand_lo = s_end;
+    *cand_hi = w_start;
+    return s_end + (n - w_start);
+}
+
+/* Rows kept by one pass.  Budget >= n keeps everything.  Otherwise the budget
+ * counts the protected rows, so kept = budget ([WL], "Compaction schedule"
+ * logs: kept rows equal the KV budget), but never fewer than the protected
+ * rows.  Returns -1 on negative arguments. */
+int64_t orc_kept_count(int64_t n, int64_t budget, int64_t sink, int64_t window)
+{
+    if (n < 0 || budget < 0 || sink < 0 || window < 0) return -1;
+    if (budget >= n) return n;
+    int64_t lo, hi;
+    int64_t np = orc_protected(n, sink, window, &lo, &hi);
+    return budget > np ? budget : np;
+}
+
+typedef struct {
+    double key;
+    int64_t idx;
+} orc_cand;
+
+/* Sort order: score descending, then row index ascending (lower row wins a
+ * tie). */
+static int orc_cand_cmp(const void *a, const void *b)
+{
+    const orc_cand *x = (const orc_cand *)a, *y = (const orc_cand *)b;
+    if (x->key > y->key) return -1;
+    if (x->key < y->key) return 1;
+    if (x->idx < y->idx) return -1;
+    if (x->idx > y->idx) return 1;
+    return 0;
+}
+
+/* [LC] section 5, "Phase B", steps 2-3: protect sink and window, sort the
+ * remaining rows by score and evict the lowest down to the budget.
+ * keep_idx: output, ascending row indices; returns the kept count. */
+int64_t orc_select_unit(const double *agg, int64_t n, int64_t budget, int64_t sink,
+                        int64_t window, int32_t *keep_idx)
+{
+    int64_t K = orc_kept_count(n, budget, sink, window);
+    if (K < 0) return -1;
+    if (K == n) {
+        for (int64_t r = 0; r < n; r++) keep_idx[r] = (int32_t)r;
+        return n;
+    }
+    int64_t lo, hi;
+    int64_t np = orc_protected(n, sink, window, &lo, &hi);
+    int64_t k = K - np; /* candidates to keep */
+    int64_t nc = hi - lo;
+    unsigned char *keep = (unsigned char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(nc > 0 ? nc : 1));
+    if (!keep || !c) { free(keep); free(c); return -1; }
+    for (int64_t r = 0; r < lo; r++) keep[r] = 1;
+    for (int64_t r = hi; r < n; r++) keep[r] = 1;
+    for (int64_t i = 0; i < nc; i++) {
+        c[i].key = agg[lo + i];
+        c[i].idx = lo + i;
+    }
+    qsort(c, (size_t)nc, sizeof(orc_cand), orc_cand_cmp);
+    for (int64_t i = 0; i < k; i++) keep[c[i].idx] = 1;
+    int64_t out = 0;
+    for (int64_t r = 0; r < n; r++)
+        if (keep[r]) keep_idx[out++] = (int32_t)r;
+    free(keep);
+    free(c);
+    return out;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compaction.                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Order-preserving gather of the kept rows to the front of the unit's
+ * storage, no gaps ([LC] section 5, "Phase B", step 4; [WL], "What was
+ * implemented": GPU gather/repack, and the exact-gather checks).  Done
+ * through a temporary copy: dst[d] = src[keep_idx[d]]. */
+int orc_compact_rows(uint8_t *rows, int64_t row_bytes, const int32_t *keep_idx, int64_t K)
+{
+    uint8_t *tmp = (uint8_t *)malloc((size_t)(K * row_bytes > 0 ? K * row_bytes : 1));
+    if (!tmp) return -1;
+    for (int64_t d = 0; d < K; d++)
+        memcpy(tmp + d * row_bytes, rows + (int64_t)keep_idx[d] * row_bytes, (size_t)row_bytes);
+    memcpy(rows, tmp, (size_t)(K * row_bytes));
+    free(tmp);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole pass over a contiguous cache [L][Hkv][cap][row].                     */
+/* ------------------------------------------------------------------------ */
+
+/* One eviction pass over every (layer, KV head) unit, each unit on its own.
+ *   k, v, pos : host copies, [L][Hkv][cap] rows; compacted in place.
+ *   q_re, q_im, w : statistics [L][Hq][F]; query head h = g*G + j belongs to
+ *                   KV head g (contiguous GQA grouping).
+ *   keep_idx  : output [L][Hkv][K] (may be NULL)
+ *   raw       : output [L][Hkv][n][G] (may be NULL)
+ *   agg       : output [L][Hkv][n]   (may be NULL)
+ * Returns the kept count K, or -1. */
+int64_t orc_evict(int k_type, int v_type, int L, int Hkv, int Hq, int hd, double theta,
+                  const int64_t *offsets, int n_off, uint8_t *k, uint8_t *v, int32_t *pos,
+                  int64_t cap, int64_t n, int64_t budget, int64_t sink, int64_t window,
+                  const float *q_re, const float *q_im, const float *w, int32_t *keep_idx,
+                  double *raw, double *agg, int do_compact)
+{
+    int G = Hq / Hkv;
+    int F = hd / 2;
+    int64_t kb = orc_row_bytes(k_type, hd), vb = orc_row_bytes(v_type, hd);
+    int64_t K = orc_kept_count(n, budget, sink, window);
+    if (K < 0 || kb < 0 || vb < 0 || n > cap) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < L * Hkv; u++) {
+        int l = u / Hkv, g = u % Hkv;
+        double *rs = raw ? raw + (int64_t)u * n * G : (double *)malloc(sizeof(double) * (size_t)(n * G + 1));
+        double *ag = agg ? agg + (int64_t)u * n : (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        int32_t *ki = keep_idx ? keep_idx + (int64_t)u * K : (int32_t *)malloc(sizeof(int32_t) * (size_t)(n + 1));
+        uint8_t *ku = k + (int64_t)u * cap * kb;
+        uint8_t *vu = v + (int64_t)u * cap * vb;
+        int32_t *pu = pos + (int64_t)u * cap;
+        int64_t stat = ((int64_t)l * Hq + (int64_t)g * G) * F;
+        int bad = 0;
+        if (n > 0) {
+            int64_t p = pu[n - 1];
+            bad |= orc_raw_scores_unit(k_type, ku, kb, n, hd, G, q_re + stat, q_im + stat,
+                                       w + stat, theta, p, offsets, n_off, rs);
+            orc_aggregate_unit(rs, n, G, ag, NULL, NULL);
+            if (orc_select_unit(ag, n, budget, sink, window, ki) != K) bad = 1;
+            if (do_compact && !bad) {
+                bad |= orc_compact_rows(ku, kb, ki, K);
+                bad |= orc_compact_rows(vu, vb, ki, K);
+                bad |= orc_compact_rows((uint8_t *)pu, 4, ki, K);
+            }
+        }
+        if (!raw) free(rs);
+        if (!agg) free(ag);
+        if (!keep_idx) free(ki);
+        if (bad) {
+#pragma omp atomic write
+            failed = 1;
+        }
+    }
+    return failed ? -1 : K;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
