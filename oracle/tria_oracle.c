@@ -186,17 +186,28 @@ void orc_aggregate_unit(const double *raw, int64_t n, int G, double *agg, double
     double *mu = (double *)malloc(sizeof(double) * (G > 0 ? G : 1));
     double *sg = (double *)malloc(sizeof(double) * (G > 0 ? G : 1));
     for (int j = 0; j < G; j++) {
-        double sum = 0.0;
+        double sum = 0.0, lo = INFINITY, hi = -INFINITY;
         int64_t cnt = 0;
         for (int64_t r = 0; r < n; r++) {
             double s = raw[r * G + j];
-            if (isfinite(s)) { sum += s; cnt++; }
+            if (isfinite(s)) {
+                sum += s;
+                cnt++;
+                lo = s < lo ? s : lo;
+                hi = s > hi ? s : hi;
+            }
         }
         double m = cnt ? sum / (double)cnt : 0.0;
         double ss = 0.0;
         for (int64_t r = 0; r < n; r++) {
             double s = raw[r * G + j];
             if (isfinite(s)) ss += (s - m) * (s - m);
+        }
+        /* Equal scores have sigma = 0 exactly; the rounding of the mean must not
+         * turn them into a tiny sigma (which would give z = +-1). */
+        if (cnt && lo == hi) {
+            m = lo;
+            ss = 0.0;
         }
         mu[j] = m;
         sg[j] = cnt ? sqrt(ss / (double)cnt) : 0.0;
