@@ -1,0 +1,191 @@
+/*
+ * tria.h -- C ABI of the MI355X (gfx950) TriAttention KV-cache eviction pass.
+ *
+ * The pass, for every (layer, KV head) of a cache (one "unit"):
+ *   1. scores every cached key by calibrated RoPE-direction importance,
+ *   2. z-normalises each query head's scores and takes the max over the query
+ *      heads that share the KV head,
+ *   3. keeps the top-budget rows while always keeping the sink prefix and the
+ *      recent window,
+ *   4. compacts K, V and positions in place, in order, with no gaps.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [WL] "TriAttention Native C++ Worklog" (TensorRT-Model-Connect).
+ *   [LC] llama.cpp docs "TriAttention KV-Cache Eviction (--triattention)".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Device pointers are HIP device memory owned by the caller; host pointers
+ *   are ordinary host memory, read during the call only.  The library keeps no
+ *   pointer to caller memory after a call returns.
+ * - Every call only enqueues work on `stream` (0 = the null stream) and never
+ *   synchronises it.  Kept counts are computed on the host from the sizes, so
+ *   they are returned without waiting for the GPU.
+ * - A context is not thread-safe: use one context per stream.  Calls on one
+ *   context must be stream-ordered (they share the context's scratch).
+ * - Errors: a negative TRIA_E_* code.  Argument and eligibility errors are
+ *   detected before anything is enqueued, so caller buffers are untouched.  A
+ *   HIP failure during a pass (TRIA_E_HIP) can leave a cache partly compacted;
+ *   treat it as invalid.  No C++ exception crosses this interface.
+ * - Key rows are stored already rotated (RoPE applied, rotate-half layout:
+ *   pair f is (x[f], x[f + head_dim/2])).  Row n-1 of every unit must hold the
+ *   newest token when a pass starts (its position is the phase reference).
+ *
+ * Layouts
+ * -------
+ *   contiguous cache  k, v : [L][Hkv][cap] rows of tria_row_bytes(type, hd)
+ *                     pos  : [L][Hkv][cap] int32 absolute positions
+ *   paged cache       k, v : [L][n_blocks][Hkv][16] rows (16-token blocks)
+ *                     pos  : [L][n_blocks][Hkv][16] int32
+ *                     block_table : [n_seq][max_blocks] int32 physical block
+ *                     ids; logical row r of a sequence lives in block
+ *                     block_table[seq][r / 16], slot r % 16, for every
+ *                     (layer, KV head).
+ *   statistics        [L][Hq][hd/2] fp32; query head h = g*G + j (j < G,
+ *                     G = Hq/Hkv) belongs to KV head g.
+ *   raw scores        [L][Hkv][n][G] fp32
+ *   agg               [L][Hkv][n] fp32
+ *   keep_idx          [L][Hkv][kept] int32, ascending row indices
+ */
+#ifndef TRIA_H
+#define TRIA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define TRIA_OK 0
+#define TRIA_E_INVAL (-1)       /* null pointer, size out of range, negative budget/sink/window,
+                                   offsets not strictly ascending and positive */
+#define TRIA_E_UNSUPPORTED (-2) /* shape outside the GPU scorer's eligibility gate */
+#define TRIA_E_HIP (-3)         /* a HIP runtime call failed; see tria_last_hip_error */
+#define TRIA_E_NOMEM (-4)       /* device or host allocation failed */
+
+/* Storage types of a cached row. */
+#define TRIA_KV_F16 0  /* head_dim IEEE fp16 values, 2*head_dim bytes */
+#define TRIA_KV_Q8_0 1 /* head_dim/32 blocks of {fp16 scale d, 32 x int8 q}; value = d*q;
+                          34*head_dim/32 bytes ([LC] section 4: the GPU scorers read q8_0 K) */
+
+/* Largest number of sequences in one tria_evict_paged_batch call. */
+#define TRIA_MAX_SEQ 64
+/* Rows per block of a paged cache. */
+#define TRIA_BLOCK 16
+
+typedef struct tria_ctx tria_ctx;
+
+/* Model shape and scoring constants, fixed for the life of a context. */
+typedef struct tria_model_desc {
+    int32_t n_layers;      /* L >= 1 */
+    int32_t n_kv_heads;    /* Hkv >= 1 */
+    int32_t n_q_heads;     /* Hq, a multiple of Hkv, Hq/Hkv <= 64 */
+    int32_t head_dim;      /* hd, a multiple of 32, <= 256 ([LC] section 4 gate) */
+    int32_t k_type;        /* TRIA_KV_F16 or TRIA_KV_Q8_0 */
+    int32_t v_type;        /* TRIA_KV_F16 or TRIA_KV_Q8_0 (V is only moved) */
+    double rope_theta;     /* RoPE base: omega_f = theta^(-2f/hd), > 1 */
+    int32_t n_offsets;     /* |D| >= 1 */
+    const int64_t *offsets;/* host: future query offsets, strictly ascending, > 0 */
+} tria_model_desc;
+
+/* Contiguous cache (device pointers, caller-owned). */
+typedef struct tria_cache {
+    void *k;
+    void *v;
+    int32_t *pos;
+    int64_t cap; /* rows per unit */
+} tria_cache;
+
+/* Paged cache (device pointers, caller-owned). */
+typedef struct tria_paged_cache {
+    void *k_pool;
+    void *v_pool;
+    int32_t *pos_pool;
+    int64_t n_blocks;           /* physical blocks per layer */
+    const int32_t *block_table; /* device [n_seq][max_blocks] */
+    int32_t max_blocks;         /* row stride of block_table */
+} tria_paged_cache;
+
+/* Create a context: copies the calibration statistics to the device.
+ * The score is ([WL], "Phase 9: final root cause - native scorer used the
+ * wrong formulation"; [LC] section 5, "Phase C"):
+ *   s_h(r) = sum_f Re(qbar_{h,f} A_f conj(K_f(r))) + sum_f w_{h,f} |K_f(r)|,
+ *   A_f = mean over delta in offsets of exp(i omega_f (p + delta)),
+ * with p the absolute position of the newest cached row ([WL], "2026-04-18:
+ * later-compaction absolute-position bug isolated and fixed").
+ *   q_re, q_im : host [L][Hq][hd/2], the complex mean pre-RoPE query qbar.
+ *   norm_w     : host [L][Hq][hd/2], the weight of the |K_f| term.
+ * On success *out owns device memory until tria_free. */
+int tria_load_stats(tria_ctx **out, const tria_model_desc *desc, const float *q_re,
+                    const float *q_im, const float *norm_w, hipStream_t stream);
+
+/* Release a context (waits for nothing; the caller must have synchronised the
+ * stream the context was used on).  NULL is ignored. */
+void tria_free(tria_ctx *ctx);
+
+/* Static description of an error code. */
+const char *tria_strerror(int code);
+
+/* hipError_t of the last failed HIP call made for this context (0 if none). */
+int tria_last_hip_error(const tria_ctx *ctx);
+
+/* Bytes of one stored row, or a negative code for an unknown type/shape. */
+int64_t tria_row_bytes(int32_t kv_type, int32_t head_dim);
+
+/* Rows one pass keeps: n if budget >= n, else max(budget, |protected|), where
+ * the protected rows are the first `sink` and the last `window` rows ([LC]
+ * section 5, "Phase B"; kept rows equal the budget in [WL]'s compaction
+ * logs).  Negative arguments give TRIA_E_INVAL. */
+int64_t tria_kept_count(int64_t n_tokens, int64_t budget, int64_t sink, int64_t window);
+
+/* Raw per-query-head scores of the first n_tokens rows of every unit.
+ *   raw_scores : device [L][Hkv][n_tokens][G] fp32, written.
+ * 0 <= n_tokens <= cache->cap.  Returns TRIA_OK or an error code. */
+int tria_score(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, float *raw_scores,
+               hipStream_t stream);
+
+/* Aggregate and select ([LC] section 5, "Phase B" steps 2-3 and "Phase C"):
+ * per query head, z = (s - mu)/sigma over the unit's rows with a finite score
+ * (sigma = 0 gives z = 0); agg = max over the group, or -inf if any of the
+ * row's scores is not finite; keep the protected rows plus the highest-agg
+ * candidates (ties to the lower row index) up to tria_kept_count.
+ *   raw_scores : device [L][Hkv][n_tokens][G], read.
+ *   keep_idx   : device [L][Hkv][kept], written (ascending rows).
+ *   agg_out    : device [L][Hkv][n_tokens] fp32, written if not NULL.
+ * Returns the kept count (>= 0) or an error code. */
+int64_t tria_select(tria_ctx *ctx, const float *raw_scores, int64_t n_tokens, int64_t budget,
+                    int64_t sink, int64_t window, int32_t *keep_idx, float *agg_out,
+                    hipStream_t stream);
+
+/* In-place, order-preserving compaction of K, V and pos ([LC] section 5,
+ * "Phase B" step 4; [WL], "What was implemented": GPU gather/repack):
+ *   row d <- row keep_idx[d] for d < kept, in every unit.  Bytes are copied
+ *   exactly; rows >= kept are left unspecified.
+ * keep_idx entries must satisfy d <= keep_idx[d] < n_tokens (ascending
+ * indices do); an entry outside that range is skipped (the row is left as it
+ * was) and never read out of bounds. */
+int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
+                 const int32_t *keep_idx, int64_t kept, hipStream_t stream);
+
+/* One whole eviction pass: tria_score, tria_select, tria_compact with the
+ * context's own scratch for the scores and kept indices.  Returns the kept
+ * count.  budget >= n_tokens enqueues nothing and returns n_tokens. */
+int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
+                   int64_t sink, int64_t window, hipStream_t stream);
+
+/* The same pass over n_seq sequences of a paged cache, one launch per kernel
+ * for all sequences.  n_tokens, budget: host [n_seq]; kept_out: host [n_seq],
+ * written with each sequence's kept count.  Each sequence's rows beyond its
+ * kept count are left unspecified; the caller may return those blocks.
+ * 1 <= n_seq <= TRIA_MAX_SEQ. */
+int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t n_seq,
+                           const int64_t *n_tokens, const int64_t *budget, int64_t sink,
+                           int64_t window, int64_t *kept_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIA_H */

@@ -1,0 +1,395 @@
+// Host side of the C ABI declared in include/tria.h: argument checks, the
+// context (device statistics and scratch), and the launch sequence of one
+// pass: prep -> score -> select -> compact, all stream-ordered.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "tria_internal.h"
+
+namespace tria {
+int64_t select_key_scratch_rows(const Batch& b, int units_per_seq);
+hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
+                              int32_t* keep, float* agg, uint32_t* key_scratch, hipStream_t s);
+}  // namespace tria
+
+using namespace tria;
+
+struct tria_ctx {
+    int L, Hkv, Hq, G, hd, F, k_type, v_type;
+    int kb, vb;
+    double theta;
+    // device
+    float* q_re = nullptr;
+    float* q_im = nullptr;
+    float* w = nullptr;
+    double* omega = nullptr;
+    double* m_re = nullptr;
+    double* m_im = nullptr;
+    // scratch, grown on demand
+    int32_t* coef = nullptr;
+    size_t coef_bytes = 0;
+    float* raw = nullptr;
+    size_t raw_bytes = 0;
+    int32_t* keep = nullptr;
+    size_t keep_bytes = 0;
+    uint32_t* keys = nullptr;
+    size_t keys_bytes = 0;
+    int last_hip = 0;
+};
+
+namespace {
+
+constexpr int64_t kMaxRows = 1024 * 256;  // rows per unit the selector handles
+
+int hip_fail(tria_ctx* ctx, hipError_t e) {
+    if (ctx) ctx->last_hip = (int)e;
+    return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
+}
+
+// Grow a scratch buffer.  Work already enqueued on `s` may still use the old
+// buffer, so the stream is drained before it is released.
+int grow(tria_ctx* ctx, void** buf, size_t* have, size_t need, hipStream_t s) {
+    if (need <= *have) return TRIA_OK;
+    if (*buf) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+        e = hipFree(*buf);
+        *buf = nullptr;
+        *have = 0;
+        if (e != hipSuccess) return hip_fail(ctx, e);
+    }
+    const size_t bytes = (need + 4095) & ~(size_t)4095;
+    hipError_t e = hipMalloc(buf, bytes);
+    if (e != hipSuccess) {
+        *buf = nullptr;
+        return hip_fail(ctx, e);
+    }
+    *have = bytes;
+    return TRIA_OK;
+}
+
+struct Protect {
+    int64_t kept, s_end, w_start;
+};
+
+Protect protect(int64_t n, int64_t budget, int64_t sink, int64_t window) {
+    Protect p;
+    if (budget >= n) {
+        p.kept = n;
+        p.s_end = p.w_start = n;  // everything kept
+        return p;
+    }
+    p.s_end = sink < n ? sink : n;
+    p.w_start = window >= n ? 0 : n - window;
+    if (p.w_start < p.s_end) p.w_start = p.s_end;
+    const int64_t np = p.s_end + (n - p.w_start);
+    p.kept = budget > np ? budget : np;
+    return p;
+}
+
+CacheView view_of(const tria_ctx* ctx, const tria_cache* c) {
+    CacheView cv;
+    cv.k = static_cast<uint8_t*>(c->k);
+    cv.v = static_cast<uint8_t*>(c->v);
+    cv.pos = c->pos;
+    cv.cap = c->cap;
+    cv.n_blocks = 0;
+    cv.bt = nullptr;
+    cv.max_blocks = 0;
+    cv.L = ctx->L;
+    cv.Hkv = ctx->Hkv;
+    cv.kb = ctx->kb;
+    cv.vb = ctx->vb;
+    return cv;
+}
+
+Batch one_seq(int64_t n, const Protect& p) {
+    Batch b;
+    memset(&b, 0, sizeof(b));
+    b.n_seq = 1;
+    b.seq[0].n = n;
+    b.seq[0].kept = p.kept;
+    b.seq[0].s_end = p.s_end;
+    b.seq[0].w_start = p.w_start;
+    b.seq[0].raw_off = 0;
+    b.seq[0].keep_off = 0;
+    return b;
+}
+
+int check_cache(const tria_cache* c, int64_t n) {
+    if (!c || !c->k || !c->v || !c->pos) return TRIA_E_INVAL;
+    if (n < 0 || c->cap < 0 || n > c->cap || n > kMaxRows) return n > kMaxRows ? TRIA_E_UNSUPPORTED : TRIA_E_INVAL;
+    return TRIA_OK;
+}
+
+int run_score(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
+              hipStream_t s) {
+    const CoefGeom cg = coef_geom(ctx->k_type, ctx->hd, ctx->G);
+    int rc = grow(ctx, reinterpret_cast<void**>(&ctx->coef), &ctx->coef_bytes,
+                  (size_t)n_units * cg.words * 4, s);
+    if (rc) return rc;
+    hipError_t e = launch_prep(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
+                               ctx->w, ctx->omega, ctx->m_re, ctx->m_im, ctx->coef, s);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    e = launch_score(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->coef, raw, s);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return TRIA_OK;
+}
+
+int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
+               hipStream_t s) {
+    const int ups = ctx->L * ctx->Hkv;
+    const int64_t krows = select_key_scratch_rows(b, ups);
+    if (krows > 0) {
+        int rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes,
+                      (size_t)krows * 4, s);
+        if (rc) return rc;
+    }
+    hipError_t e = launch_select_impl(b, ups, ctx->G, raw, keep, agg, ctx->keys, s);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return TRIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tria_strerror(int code) {
+    switch (code) {
+        case TRIA_OK: return "ok";
+        case TRIA_E_INVAL: return "invalid argument";
+        case TRIA_E_UNSUPPORTED: return "shape not supported by the gfx950 kernels";
+        case TRIA_E_HIP: return "HIP runtime error";
+        case TRIA_E_NOMEM: return "out of memory";
+        default: return "unknown error";
+    }
+}
+
+int tria_last_hip_error(const tria_ctx* ctx) { return ctx ? ctx->last_hip : 0; }
+
+int64_t tria_row_bytes(int32_t kv_type, int32_t head_dim) {
+    if (head_dim <= 0 || head_dim % 32 != 0) return TRIA_E_UNSUPPORTED;
+    if (kv_type == TRIA_KV_F16) return 2 * (int64_t)head_dim;
+    if (kv_type == TRIA_KV_Q8_0) return 34 * (int64_t)(head_dim / 32);
+    return TRIA_E_UNSUPPORTED;
+}
+
+int64_t tria_kept_count(int64_t n_tokens, int64_t budget, int64_t sink, int64_t window) {
+    if (n_tokens < 0 || budget < 0 || sink < 0 || window < 0) return TRIA_E_INVAL;
+    return protect(n_tokens, budget, sink, window).kept;
+}
+
+void tria_free(tria_ctx* ctx) {
+    if (!ctx) return;
+    void* bufs[] = {ctx->q_re, ctx->q_im, ctx->w,   ctx->omega, ctx->m_re,
+                    ctx->m_im, ctx->coef, ctx->raw, ctx->keep,  ctx->keys};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+    delete ctx;
+}
+
+int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
+                    const float* q_im, const float* norm_w, hipStream_t stream) {
+    (void)stream;
+    if (!out) return TRIA_E_INVAL;
+    *out = nullptr;
+    if (!d || !q_re || !q_im || !norm_w || !d->offsets) return TRIA_E_INVAL;
+    if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_offsets < 1)
+        return TRIA_E_INVAL;
+    if (!(d->rope_theta > 1.0) || !isfinite(d->rope_theta)) return TRIA_E_INVAL;
+    for (int i = 0; i < d->n_offsets; ++i) {
+        if (d->offsets[i] <= 0) return TRIA_E_INVAL;
+        if (i > 0 && d->offsets[i] <= d->offsets[i - 1]) return TRIA_E_INVAL;
+    }
+    // eligibility gate (llama.cpp page, section 4 "GPU scoring requirements")
+    if (d->n_q_heads % d->n_kv_heads != 0) return TRIA_E_UNSUPPORTED;
+    if (d->n_q_heads / d->n_kv_heads > 64) return TRIA_E_UNSUPPORTED;
+    if (d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0) return TRIA_E_UNSUPPORTED;
+    if (tria_row_bytes(d->k_type, d->head_dim) < 0 || tria_row_bytes(d->v_type, d->head_dim) < 0)
+        return TRIA_E_UNSUPPORTED;
+
+    tria_ctx* ctx = new (std::nothrow) tria_ctx();
+    if (!ctx) return TRIA_E_NOMEM;
+    ctx->L = d->n_layers;
+    ctx->Hkv = d->n_kv_heads;
+    ctx->Hq = d->n_q_heads;
+    ctx->G = d->n_q_heads / d->n_kv_heads;
+    ctx->hd = d->head_dim;
+    ctx->F = d->head_dim / 2;
+    ctx->k_type = d->k_type;
+    ctx->v_type = d->v_type;
+    ctx->kb = (int)tria_row_bytes(d->k_type, d->head_dim);
+    ctx->vb = (int)tria_row_bytes(d->v_type, d->head_dim);
+    ctx->theta = d->rope_theta;
+
+    const size_t nstat = (size_t)ctx->L * ctx->Hq * ctx->F;
+    const int F = ctx->F;
+    double* host = (double*)malloc(sizeof(double) * 3 * F);
+    if (!host) {
+        delete ctx;
+        return TRIA_E_NOMEM;
+    }
+    // omega_f = theta^(-2f/hd); M_f = mean over the offsets of exp(i omega_f delta)
+    for (int f = 0; f < F; ++f) {
+        const double om = pow(d->rope_theta, -2.0 * (double)f / (double)ctx->hd);
+        double sr = 0.0, si = 0.0;
+        for (int i = 0; i < d->n_offsets; ++i) {
+            sr += cos(om * (double)d->offsets[i]);
+            si += sin(om * (double)d->offsets[i]);
+        }
+        host[f] = om;
+        host[F + f] = sr / d->n_offsets;
+        host[2 * F + f] = si / d->n_offsets;
+    }
+    hipError_t e = hipSuccess;
+    float** fdst[3] = {&ctx->q_re, &ctx->q_im, &ctx->w};
+    const float* fsrc[3] = {q_re, q_im, norm_w};
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+        e = hipMalloc(reinterpret_cast<void**>(fdst[i]), nstat * sizeof(float));
+        if (e == hipSuccess) e = hipMemcpy(*fdst[i], fsrc[i], nstat * sizeof(float), hipMemcpyHostToDevice);
+    }
+    double** ddst[3] = {&ctx->omega, &ctx->m_re, &ctx->m_im};
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+        e = hipMalloc(reinterpret_cast<void**>(ddst[i]), F * sizeof(double));
+        if (e == hipSuccess) e = hipMemcpy(*ddst[i], host + i * F, F * sizeof(double), hipMemcpyHostToDevice);
+    }
+    free(host);
+    if (e != hipSuccess) {
+        const int rc = e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
+        tria_free(ctx);
+        return rc;
+    }
+    *out = ctx;
+    return TRIA_OK;
+}
+
+int tria_score(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, float* raw_scores,
+               hipStream_t stream) {
+    if (!ctx || !raw_scores) return TRIA_E_INVAL;
+    int rc = check_cache(cache, n_tokens);
+    if (rc) return rc;
+    if (n_tokens == 0) return TRIA_OK;
+    const CacheView cv = view_of(ctx, cache);
+    const Batch b = one_seq(n_tokens, protect(n_tokens, n_tokens, 0, 0));
+    return run_score(ctx, cv, b, ctx->L * ctx->Hkv, raw_scores, stream);
+}
+
+int64_t tria_select(tria_ctx* ctx, const float* raw_scores, int64_t n_tokens, int64_t budget,
+                    int64_t sink, int64_t window, int32_t* keep_idx, float* agg_out,
+                    hipStream_t stream) {
+    if (!ctx || !raw_scores || !keep_idx) return TRIA_E_INVAL;
+    if (n_tokens < 0 || budget < 0 || sink < 0 || window < 0) return TRIA_E_INVAL;
+    if (n_tokens > kMaxRows) return TRIA_E_UNSUPPORTED;
+    if (n_tokens == 0) return 0;
+    const Protect p = protect(n_tokens, budget, sink, window);
+    const Batch b = one_seq(n_tokens, p);
+    int rc = run_select(ctx, b, raw_scores, keep_idx, agg_out, stream);
+    return rc ? rc : p.kept;
+}
+
+int tria_compact(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens,
+                 const int32_t* keep_idx, int64_t kept, hipStream_t stream) {
+    if (!ctx || !keep_idx) return TRIA_E_INVAL;
+    int rc = check_cache(cache, n_tokens);
+    if (rc) return rc;
+    if (kept < 0 || kept > n_tokens) return TRIA_E_INVAL;
+    if (kept == 0 || kept == n_tokens) return TRIA_OK;
+    Protect p;
+    p.kept = kept;
+    p.s_end = p.w_start = 0;
+    const Batch b = one_seq(n_tokens, p);
+    hipError_t e = launch_compact(view_of(ctx, cache), b, ctx->L * ctx->Hkv, keep_idx, stream);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+}
+
+int64_t tria_evict(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, int64_t budget,
+                   int64_t sink, int64_t window, hipStream_t stream) {
+    if (!ctx) return TRIA_E_INVAL;
+    int rc = check_cache(cache, n_tokens);
+    if (rc) return rc;
+    if (budget < 0 || sink < 0 || window < 0) return TRIA_E_INVAL;
+    const Protect p = protect(n_tokens, budget, sink, window);
+    if (p.kept == n_tokens) return n_tokens;  // nothing to evict: no work, no writes
+    const int units = ctx->L * ctx->Hkv;
+    rc = grow(ctx, reinterpret_cast<void**>(&ctx->raw), &ctx->raw_bytes,
+              (size_t)units * n_tokens * ctx->G * sizeof(float), stream);
+    if (rc) return rc;
+    rc = grow(ctx, reinterpret_cast<void**>(&ctx->keep), &ctx->keep_bytes,
+              (size_t)units * p.kept * sizeof(int32_t), stream);
+    if (rc) return rc;
+    const CacheView cv = view_of(ctx, cache);
+    const Batch b = one_seq(n_tokens, p);
+    rc = run_score(ctx, cv, b, units, ctx->raw, stream);
+    if (rc) return rc;
+    rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, stream);
+    if (rc) return rc;
+    hipError_t e = launch_compact(cv, b, units, ctx->keep, stream);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return p.kept;
+}
+
+int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t n_seq,
+                           const int64_t* n_tokens, const int64_t* budget, int64_t sink,
+                           int64_t window, int64_t* kept_out, hipStream_t stream) {
+    if (!ctx || !cache || !n_tokens || !budget || !kept_out) return TRIA_E_INVAL;
+    if (!cache->k_pool || !cache->v_pool || !cache->pos_pool || !cache->block_table)
+        return TRIA_E_INVAL;
+    if (n_seq < 1 || n_seq > TRIA_MAX_SEQ || sink < 0 || window < 0) return TRIA_E_INVAL;
+    if (cache->n_blocks < 1 || cache->max_blocks < 1) return TRIA_E_INVAL;
+    const int units_per_seq = ctx->L * ctx->Hkv;
+    Batch b;
+    memset(&b, 0, sizeof(b));
+    b.n_seq = n_seq;
+    int64_t raw_off = 0, keep_off = 0;
+    bool any = false;
+    for (int i = 0; i < n_seq; ++i) {
+        const int64_t n = n_tokens[i];
+        if (n < 0 || budget[i] < 0) return TRIA_E_INVAL;
+        if (n > (int64_t)cache->max_blocks * TRIA_BLOCK) return TRIA_E_INVAL;
+        if (n > kMaxRows) return TRIA_E_UNSUPPORTED;
+        const Protect p = protect(n, budget[i], sink, window);
+        SeqDesc& sd = b.seq[i];
+        // a sequence with nothing to evict takes no part in the pass
+        sd.n = p.kept == n ? 0 : n;
+        sd.kept = p.kept == n ? 0 : p.kept;
+        sd.s_end = p.s_end;
+        sd.w_start = p.w_start;
+        sd.raw_off = raw_off;
+        sd.keep_off = keep_off;
+        raw_off += (int64_t)units_per_seq * sd.n * ctx->G;
+        keep_off += (int64_t)units_per_seq * sd.kept;
+        kept_out[i] = p.kept;
+        any |= sd.n > 0;
+    }
+    if (!any) return TRIA_OK;
+    int rc = grow(ctx, reinterpret_cast<void**>(&ctx->raw), &ctx->raw_bytes,
+                  (size_t)raw_off * sizeof(float), stream);
+    if (rc) return rc;
+    rc = grow(ctx, reinterpret_cast<void**>(&ctx->keep), &ctx->keep_bytes,
+              (size_t)keep_off * sizeof(int32_t), stream);
+    if (rc) return rc;
+    CacheView cv;
+    cv.k = static_cast<uint8_t*>(cache->k_pool);
+    cv.v = static_cast<uint8_t*>(cache->v_pool);
+    cv.pos = cache->pos_pool;
+    cv.cap = 0;
+    cv.n_blocks = cache->n_blocks;
+    cv.bt = cache->block_table;
+    cv.max_blocks = cache->max_blocks;
+    cv.L = ctx->L;
+    cv.Hkv = ctx->Hkv;
+    cv.kb = ctx->kb;
+    cv.vb = ctx->vb;
+    const int units = units_per_seq * n_seq;
+    rc = run_score(ctx, cv, b, units, ctx->raw, stream);
+    if (rc) return rc;
+    rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, stream);
+    if (rc) return rc;
+    hipError_t e = launch_compact(cv, b, units, ctx->keep, stream);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+}
+
+}  // extern "C"

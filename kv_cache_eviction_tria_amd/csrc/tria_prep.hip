@@ -1,0 +1,130 @@
+// prep: per-unit coefficient table of the score.
+//
+// The score's trigonometric part is sum_f Re(C_{j,f} conj(K_f)) with
+// C_{j,f} = qbar_{j,f} * A_f and A_f the mean over the offset set D of
+// exp(i omega_f (p + delta)) ("TriAttention Native C++ Worklog", section
+// "Phase 9: final root cause - native scorer used the wrong formulation":
+// the phase is applied on the query side only).  p is the absolute position
+// stored with the unit's newest row (same worklog, section "2026-04-18:
+// later-compaction absolute-position bug isolated and fixed"), read here on
+// the device so that no host round trip is needed.
+//
+// A_f factors exactly as exp(i omega_f p) * M_f with M_f the mean of
+// exp(i omega_f delta), which the host computes once in fp64; this kernel
+// evaluates the remaining phase in fp64 (omega_0 p reaches ~1e5 rad, beyond
+// what fp32 can resolve) and rounds the products to the table format the
+// score kernel reads from scalar registers.
+#include "tria_internal.h"
+
+namespace tria {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+constexpr int kDigitMax = 32639;  // |v| <= 32639 has balanced base-256 digits in [-128, 127]
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(
+    CacheView cv, Batch b, int k_type, int G, int hd, const float* __restrict__ q_re,
+    const float* __restrict__ q_im, const float* __restrict__ norm_w,
+    const double* __restrict__ omega, const double* __restrict__ m_re,
+    const double* __restrict__ m_im, int32_t* __restrict__ coef) {
+    const int u = blockIdx.x;
+    const UnitId id = unit_id(cv, u);
+    const SeqDesc& sd = b.seq[id.seq];
+    const CoefGeom cg = coef_geom(k_type, hd, G);
+    const int F = cg.F;
+    int32_t* out = coef + (int64_t)u * cg.words;
+    float* outf = reinterpret_cast<float*>(out);
+    if (sd.n <= 0) return;
+
+    __shared__ double a_re[128], a_im[128];
+    __shared__ double c_full[256];  // one head's trig coefficients, [Re C_0..F-1, Im C_0..F-1]
+    __shared__ float sig_sh[8];
+
+    const int64_t p = cv.pos[row_index(cv, id, sd.n - 1)];
+    for (int f = threadIdx.x; f < F; f += kPrepThreads) {
+        double s, c;
+        sincos(omega[f] * (double)p, &s, &c);
+        a_re[f] = c * m_re[f] - s * m_im[f];
+        a_im[f] = c * m_im[f] + s * m_re[f];
+    }
+    __syncthreads();
+
+    const int Hq = cv.Hkv * G;
+    const int64_t stat0 = ((int64_t)id.l * Hq + (int64_t)id.g * G) * F;
+
+    if (k_type == TRIA_KV_F16) {
+        for (int i = threadIdx.x; i < F * G; i += kPrepThreads) {
+            const int j = i / F, f = i - j * F;
+            const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
+            const int o = (j0 * F + f * gt + (j - j0)) * 3;
+            const int64_t s = stat0 + (int64_t)j * F + f;
+            const double qr = q_re[s], qi = q_im[s];
+            outf[o + 0] = (float)(qr * a_re[f] - qi * a_im[f]);
+            outf[o + 1] = (float)(qr * a_im[f] + qi * a_re[f]);
+            outf[o + 2] = norm_w[s];
+        }
+        return;
+    }
+
+    // q8_0: trig coefficients quantised per (head, 32-dim block) to 16-bit integers
+    // v = round(c / sig), split into balanced base-256 digits so that the score
+    // kernel can accumulate sum_d q_d * v_d with packed int8 dot products.
+    const int NB = cg.NB, W = cg.W, RB = 34 * NB;
+    for (int j = 0; j < G; ++j) {
+        const int64_t s0 = stat0 + (int64_t)j * F;
+        const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
+        for (int f = threadIdx.x; f < F; f += kPrepThreads) {
+            const double qr = q_re[s0 + f], qi = q_im[s0 + f];
+            c_full[f] = qr * a_re[f] - qi * a_im[f];
+            c_full[f + F] = qr * a_im[f] + qi * a_re[f];
+            outf[cg.w_off + j0 * F + f * gt + (j - j0)] = norm_w[s0 + f];
+        }
+        __syncthreads();
+        if (threadIdx.x < NB) {
+            double m = 0.0;
+            for (int t = 0; t < 32; ++t) m = fmax(m, fabs(c_full[32 * threadIdx.x + t]));
+            const float sg = (float)(m / kDigitMax);
+            sig_sh[threadIdx.x] = sg;
+            outf[cg.sig_off + j * NB + threadIdx.x] = sg;
+        }
+        __syncthreads();
+        for (int k = threadIdx.x; k < W; k += kPrepThreads) {
+            uint32_t hi_w = 0, lo_w = 0;
+            for (int i = 0; i < 4; ++i) {
+                const int byte = 4 * k + i;
+                if (byte >= RB) continue;
+                const int blk = byte / 34, o = byte - 34 * blk;
+                if (o < 2) continue;  // scale bytes get a zero digit
+                const float sg = sig_sh[blk];
+                int v = 0;
+                if (sg > 0.0f) {
+                    const double t = c_full[32 * blk + (o - 2)] / (double)sg;
+                    v = (int)llrint(t);
+                    v = v > kDigitMax ? kDigitMax : (v < -kDigitMax ? -kDigitMax : v);
+                }
+                const int lo = ((v + 128) & 255) - 128;
+                const int hi = (v - lo) / 256;
+                hi_w |= (uint32_t)(hi & 255) << (8 * i);
+                lo_w |= (uint32_t)(lo & 255) << (8 * i);
+            }
+            out[cg.hi_off + j * W + k] = (int32_t)hi_w;
+            out[cg.lo_off + j * W + k] = (int32_t)lo_w;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const CacheView& cv, const Batch& b, int n_units, int k_type, int G,
+                       int hd, const float* q_re, const float* q_im, const float* w,
+                       const double* omega, const double* m_re, const double* m_im,
+                       int32_t* coef, hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prep_kernel, dim3(n_units), dim3(kPrepThreads), 0, s, cv, b, k_type, G, hd,
+                       q_re, q_im, w, omega, m_re, m_im, coef);
+    return hipGetLastError();
+}
+
+}  // namespace tria

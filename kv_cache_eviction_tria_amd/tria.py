@@ -1,0 +1,234 @@
+"""ctypes binding of libtria.so: the same entry points as include/tria.h.
+
+Argument marshalling only: every step of the pass runs in the HIP kernels of
+libtria.so.  PyTorch supplies device memory (tensors are passed by data
+pointer) and the stream (torch's current stream unless one is given).  If the
+library is not built this module raises on first use; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libtria.so")
+
+TRIA_OK = 0
+TRIA_E_INVAL = -1
+TRIA_E_UNSUPPORTED = -2
+TRIA_E_HIP = -3
+TRIA_E_NOMEM = -4
+TRIA_KV_F16 = 0
+TRIA_KV_Q8_0 = 1
+TRIA_MAX_SEQ = 64
+TRIA_BLOCK = 16
+
+_lock = threading.Lock()
+_lib = None
+
+
+class TriaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (where, tria_strerror(code), code))
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k_type", ctypes.c_int32), ("v_type", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("n_offsets", ctypes.c_int32),
+                ("offsets", ctypes.POINTER(ctypes.c_int64))]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("cap", ctypes.c_int64)]
+
+
+class PagedCache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("pos_pool", ctypes.c_void_p), ("n_blocks", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32)]
+
+
+def lib():
+    """Load libtria.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError("libtria.so is not built (%s); run "
+                                  "kv_cache_eviction_tria_amd.build.build()" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            L.tria_load_stats.restype = ctypes.c_int
+            L.tria_load_stats.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ModelDesc), vp, vp,
+                                          vp, vp]
+            L.tria_free.restype = None
+            L.tria_free.argtypes = [vp]
+            L.tria_strerror.restype = ctypes.c_char_p
+            L.tria_strerror.argtypes = [ctypes.c_int]
+            L.tria_last_hip_error.restype = ctypes.c_int
+            L.tria_last_hip_error.argtypes = [vp]
+            L.tria_row_bytes.restype = i64
+            L.tria_row_bytes.argtypes = [i32, i32]
+            L.tria_kept_count.restype = i64
+            L.tria_kept_count.argtypes = [i64, i64, i64, i64]
+            L.tria_score.restype = ctypes.c_int
+            L.tria_score.argtypes = [vp, ctypes.POINTER(Cache), i64, vp, vp]
+            L.tria_select.restype = i64
+            L.tria_select.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+            L.tria_compact.restype = ctypes.c_int
+            L.tria_compact.argtypes = [vp, ctypes.POINTER(Cache), i64, vp, i64, vp]
+            L.tria_evict.restype = i64
+            L.tria_evict.argtypes = [vp, ctypes.POINTER(Cache), i64, i64, i64, i64, vp]
+            L.tria_evict_paged_batch.restype = ctypes.c_int
+            L.tria_evict_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32, vp, vp, i64,
+                                                 i64, vp, vp]
+            _lib = L
+    return _lib
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must have dtype %s" % (name, dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(code, where):
+    if code < 0:
+        raise TriaError(int(code), where)
+    return code
+
+
+def tria_strerror(code: int) -> str:
+    return lib().tria_strerror(int(code)).decode()
+
+
+def tria_row_bytes(kv_type: int, head_dim: int) -> int:
+    return int(lib().tria_row_bytes(kv_type, head_dim))
+
+
+def tria_kept_count(n_tokens: int, budget: int, sink: int, window: int) -> int:
+    return int(_check(lib().tria_kept_count(n_tokens, budget, sink, window), "tria_kept_count"))
+
+
+class TriaCtx:
+    """Owns a tria_ctx handle (device statistics and scratch)."""
+
+    def __init__(self, handle, desc):
+        self.handle = handle
+        self.n_layers = desc.n_layers
+        self.n_kv_heads = desc.n_kv_heads
+        self.n_q_heads = desc.n_q_heads
+        self.head_dim = desc.head_dim
+        self.k_type = desc.k_type
+        self.v_type = desc.v_type
+
+    @property
+    def G(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def close(self):
+        if self.handle:
+            lib().tria_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tria_load_stats(n_layers, n_kv_heads, n_q_heads, head_dim, k_type, v_type, rope_theta,
+                    offsets, q_re, q_im, norm_w, stream=None) -> TriaCtx:
+    """q_re, q_im, norm_w: host float32 arrays [L][Hq][hd/2] (numpy or CPU tensors)."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.float32)) for a in (q_re, q_im, norm_w)]
+    offs = (ctypes.c_int64 * len(offsets))(*[int(x) for x in offsets])
+    d = ModelDesc(n_layers, n_kv_heads, n_q_heads, head_dim, k_type, v_type, float(rope_theta),
+                  len(offsets), offs)
+    h = ctypes.c_void_p()
+    rc = lib().tria_load_stats(ctypes.byref(h), ctypes.byref(d),
+                               *[a.ctypes.data_as(ctypes.c_void_p) for a in arrs],
+                               _stream(stream) if torch.cuda.is_available() else None)
+    _check(rc, "tria_load_stats")
+    return TriaCtx(h, d)
+
+
+def _cache(k, v, pos):
+    return Cache(_ptr(k, "k", torch.uint8), _ptr(v, "v", torch.uint8),
+                 _ptr(pos, "pos", torch.int32), pos.shape[-1])
+
+
+def tria_score(ctx: TriaCtx, k, v, pos, n_tokens: int, raw_scores, stream=None) -> None:
+    """k, v: uint8 [L,Hkv,cap,row_bytes]; pos: int32 [L,Hkv,cap];
+    raw_scores: float32 [L,Hkv,n_tokens,G] (written)."""
+    c = _cache(k, v, pos)
+    _check(lib().tria_score(ctx.handle, ctypes.byref(c), n_tokens,
+                            _ptr(raw_scores, "raw_scores", torch.float32), _stream(stream)),
+           "tria_score")
+
+
+def tria_select(ctx: TriaCtx, raw_scores, n_tokens: int, budget: int, sink: int, window: int,
+                keep_idx, agg_out=None, stream=None) -> int:
+    """keep_idx: int32 [L,Hkv,kept] (written); agg_out: float32 [L,Hkv,n_tokens] or None."""
+    return int(_check(lib().tria_select(ctx.handle, _ptr(raw_scores, "raw_scores", torch.float32),
+                                        n_tokens, budget, sink, window,
+                                        _ptr(keep_idx, "keep_idx", torch.int32),
+                                        _ptr(agg_out, "agg_out", torch.float32),
+                                        _stream(stream)), "tria_select"))
+
+
+def tria_compact(ctx: TriaCtx, k, v, pos, n_tokens: int, keep_idx, kept: int, stream=None) -> None:
+    c = _cache(k, v, pos)
+    _check(lib().tria_compact(ctx.handle, ctypes.byref(c), n_tokens,
+                              _ptr(keep_idx, "keep_idx", torch.int32), kept, _stream(stream)),
+           "tria_compact")
+
+
+def tria_evict(ctx: TriaCtx, k, v, pos, n_tokens: int, budget: int, sink: int, window: int,
+               stream=None) -> int:
+    c = _cache(k, v, pos)
+    return int(_check(lib().tria_evict(ctx.handle, ctypes.byref(c), n_tokens, budget, sink,
+                                       window, _stream(stream)), "tria_evict"))
+
+
+def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, n_tokens,
+                           budget, sink: int, window: int, stream=None):
+    """k_pool, v_pool: uint8 [L,n_blocks,Hkv,16,row_bytes]; pos_pool: int32
+    [L,n_blocks,Hkv,16]; block_table: int32 [n_seq,max_blocks] (device);
+    n_tokens, budget: host sequences of length n_seq.  Returns kept counts."""
+    n_seq = len(n_tokens)
+    nt = (ctypes.c_int64 * n_seq)(*[int(x) for x in n_tokens])
+    bd = (ctypes.c_int64 * n_seq)(*[int(x) for x in budget])
+    kept = (ctypes.c_int64 * n_seq)()
+    pc = PagedCache(_ptr(k_pool, "k_pool", torch.uint8), _ptr(v_pool, "v_pool", torch.uint8),
+                    _ptr(pos_pool, "pos_pool", torch.int32), pos_pool.shape[1],
+                    _ptr(block_table, "block_table", torch.int32), block_table.shape[1])
+    _check(lib().tria_evict_paged_batch(ctx.handle, ctypes.byref(pc), n_seq, nt, bd, sink,
+                                        window, kept, _stream(stream)), "tria_evict_paged_batch")
+    return [int(x) for x in kept]
+
+
+def tria_free(ctx: TriaCtx) -> None:
+    ctx.close()

@@ -1,0 +1,107 @@
+"""The C-ABI library loads and exports what include/tria.h declares; host-only
+entry points (no device work) behave as documented.  Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_eviction_tria_amd import tria
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tria.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tria_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tria.LIB_PATH):
+        from kv_cache_eviction_tria_amd import build
+        build.build()
+    return tria.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"tria_load_stats", "tria_score", "tria_select", "tria_compact",
+                          "tria_evict", "tria_evict_paged_batch", "tria_free", "tria_strerror",
+                          "tria_kept_count", "tria_row_bytes", "tria_last_hip_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert tria.tria_strerror(code)
+    assert tria.tria_strerror(-99) == "unknown error"
+
+
+def test_row_bytes(lib):
+    assert tria.tria_row_bytes(tria.TRIA_KV_F16, 128) == 256
+    assert tria.tria_row_bytes(tria.TRIA_KV_Q8_0, 128) == 136
+    assert tria.tria_row_bytes(tria.TRIA_KV_Q8_0, 96) == 102
+    for hd in (32, 64, 96, 128, 160, 192, 224, 256):
+        for t in (0, 1):
+            assert tria.tria_row_bytes(t, hd) == oracle.row_bytes(t, hd)
+    assert tria.tria_row_bytes(tria.TRIA_KV_F16, 100) == tria.TRIA_E_UNSUPPORTED
+    assert tria.tria_row_bytes(7, 128) == tria.TRIA_E_UNSUPPORTED
+
+
+def test_kept_count_matches_oracle(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        n = int(rng.integers(0, 300))
+        b, s, w = (int(x) for x in rng.integers(0, 320, size=3))
+        assert tria.tria_kept_count(n, b, s, w) == oracle.kept_count(n, b, s, w)
+    assert lib.tria_kept_count(10, -1, 0, 0) == tria.TRIA_E_INVAL
+    assert lib.tria_kept_count(-1, 1, 0, 0) == tria.TRIA_E_INVAL
+
+
+def _desc(**kw):
+    d = dict(n_layers=1, n_kv_heads=1, n_q_heads=4, head_dim=128, k_type=0, v_type=0,
+             rope_theta=1e6, offsets=[1, 2, 4])
+    d.update(kw)
+    offs = (ctypes.c_int64 * len(d["offsets"]))(*d["offsets"])
+    return tria.ModelDesc(d["n_layers"], d["n_kv_heads"], d["n_q_heads"], d["head_dim"],
+                          d["k_type"], d["v_type"], d["rope_theta"], len(d["offsets"]), offs)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=100), tria.TRIA_E_UNSUPPORTED),
+    (dict(head_dim=288), tria.TRIA_E_UNSUPPORTED),
+    (dict(head_dim=16), tria.TRIA_E_UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=4), tria.TRIA_E_UNSUPPORTED),
+    (dict(n_q_heads=65 * 2, n_kv_heads=2), tria.TRIA_E_UNSUPPORTED),
+    (dict(k_type=5), tria.TRIA_E_UNSUPPORTED),
+    (dict(n_layers=0), tria.TRIA_E_INVAL),
+    (dict(offsets=[1, 1]), tria.TRIA_E_INVAL),
+    (dict(offsets=[0, 1]), tria.TRIA_E_INVAL),
+    (dict(offsets=[4, 2]), tria.TRIA_E_INVAL),
+    (dict(rope_theta=1.0), tria.TRIA_E_INVAL),
+])
+def test_load_stats_rejects_before_touching_the_device(lib, kw, code):
+    d = _desc(**kw)
+    stats = np.zeros(8 * 128 * 128, np.float32)
+    p = stats.ctypes.data_as(ctypes.c_void_p)
+    h = ctypes.c_void_p(1234)
+    rc = lib.tria_load_stats(ctypes.byref(h), ctypes.byref(d), p, p, p, None)
+    assert rc == code
+    assert not h.value
+
+
+def test_null_arguments_are_rejected(lib):
+    c = tria.Cache(None, None, None, 0)
+    assert lib.tria_score(None, ctypes.byref(c), 0, None, None) == tria.TRIA_E_INVAL
+    assert lib.tria_select(None, None, 0, 0, 0, 0, None, None, None) == tria.TRIA_E_INVAL
+    assert lib.tria_compact(None, ctypes.byref(c), 0, None, 0, None) == tria.TRIA_E_INVAL
+    assert lib.tria_evict(None, ctypes.byref(c), 0, 0, 0, 0, None) == tria.TRIA_E_INVAL
+    assert lib.tria_evict_paged_batch(None, None, 1, None, None, 0, 0, None,
+                                      None) == tria.TRIA_E_INVAL
+    lib.tria_free(None)
+    assert lib.tria_last_hip_error(None) == 0
