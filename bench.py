@@ -1,24 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the TriAttention eviction pass on one MI355X.
 
-One step = one whole pass (score -> aggregate/select -> in-place compaction)
-over a synthetic cache resident in HBM.  Between steps the cache is restored
-from a pristine device copy and the 256 MB Infinity Cache is flushed; neither
-is timed.  Each stage is timed with HIP events recorded on the stream the
-kernels are launched on.  Prints one JSON line.
+One step = one call of tria_evict (score -> aggregate/select -> in-place
+compaction of every layer and KV head) over a synthetic cache resident in
+HBM, timed with HIP events recorded on the caller's stream around the call
+(the library's second stream joins that stream before the call returns).
+Between steps the cache is restored from a pristine device copy and the
+256 MB Infinity Cache is flushed by writing 512 MB; neither is timed.
+
+Per-kernel durations come from the library's own timing events (recorded on
+the stream each kernel runs on) during the same timed steps; the kernel with
+the largest total time is reported against the HBM roofline with its
+algorithmic bytes:  score = every cached K row read once; compaction = every
+moved row (keep_idx[d] != d) read and written (K + V + pos).  A sequential
+breakdown (the three stages one after another) is reported beside it.
 
 Default workload: the full Qwen3-8B-shaped cache at 32K context (36 layers x
 8 KV / 32 query heads, head_dim 128, q8_0 K / fp16 V, budget 25%, window 512).
+The paged workload (16 sequences of 8K..64K tokens in shuffled 16-row blocks)
+runs one initial pass, then rounds of "append 128 rows to every sequence,
+evict back to its budget"; a step is one such batched round.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "KV tokens scored+compacted/sec and eviction-pass ms at 32K ctx; % of HBM peak"
+UNIT = "KV rows/s (layer x KV-head x token, scored + compacted)"
+# sources whose kernels each timed stage runs
+STAGE_SOURCES = {
+    "score": ["tria_score.hip", "tria_prep.hip", "tria_internal.h"],
+    "select": ["tria_select.hip", "tria_internal.h"],
+    "compact": ["tria_compact.hip", "tria_internal.h"],
+}
 
 
 def parse():
@@ -28,10 +51,43 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_full_32k_q8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=8,
-                    help="layers of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work the oracle baseline aims for (whole passes, at least one)")
+    ap.add_argument("--staged-steps", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true")
     return ap.parse_args()
+
+
+def sources_digest(stage):
+    h = hashlib.sha256()
+    for f in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, "kv_cache_eviction_tria_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (stage, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("sources_sha256_16") != sources_digest(stage):
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def roofline(stage, ms_total, launches, alg_bytes_total, workload):
+    """Roofline entry for one stage from its summed launch durations."""
+    avg_ms = ms_total / max(launches, 1)
+    per_launch = alg_bytes_total / max(launches, 1) if alg_bytes_total else None
+    achieved = per_launch / (avg_ms * 1e-3) / 1e9 if per_launch else None
+    return {"kernel": stage, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+            "traffic": measured_traffic(stage, workload), "alg_bytes_per_launch": per_launch,
+            "launches_per_step": launches, "avg_launch_ms": avg_ms}
 
 
 def main():
@@ -41,29 +97,33 @@ def main():
               "multi-GPU run is the same kernels on each GPU's share; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    from kv_cache_eviction_tria_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    out = bench_paged(args, wl) if wl.n_seq else bench_contiguous(args, wl)
+    print(json.dumps(out), flush=True)
 
+
+def log(msg):
+    print("# " + msg, file=sys.stderr, flush=True)
+
+
+def bench_contiguous(args, wl):
     import numpy as np
     import torch
 
     from kv_cache_eviction_tria_amd import synth, tria
 
-    wl = synth.WORKLOADS[args.workload]
-    if wl.n_seq:
-        print("paged workloads are benchmarked by bench_paged.py", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     n, B, S, W, G = wl.n, wl.budget, wl.sink, wl.window, wl.G
-    print("# workload %s: generating on the device" % wl.name, file=sys.stderr, flush=True)
+    log("workload %s: generating on the device" % wl.name)
     stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, wl.seed)
     k, v, pos = synth.gen_cache(wl.L, wl.Hkv, wl.hd, n, n, wl.k_type, wl.v_type, wl.seed, dev)
     k0, v0, p0 = k.clone(), v.clone(), pos.clone()
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
     K = tria.tria_kept_count(n, B, S, W)
-    raw = torch.empty(wl.L, wl.Hkv, n, G, dtype=torch.float32, device=dev)
-    keep = torch.empty(wl.L, wl.Hkv, K, dtype=torch.int32, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def restore():
@@ -73,9 +133,53 @@ def main():
         if not args.no_flush:
             flush.fill_(1)
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    # the kept rows of this input, for the algorithmic byte count (untimed)
+    raw = torch.empty(wl.L, wl.Hkv, n, G, dtype=torch.float32, device=dev)
+    keep = torch.empty(wl.L, wl.Hkv, K, dtype=torch.int32, device=dev)
+    tria.tria_score(ctx, k, v, pos, n, raw, stream)
+    tria.tria_select(ctx, raw, n, B, S, W, keep, None, stream)
+    moved = int((keep != torch.arange(K, device=dev, dtype=torch.int32)).sum().item())
+    kb, vb = synth.row_bytes(wl.k_type, wl.hd), synth.row_bytes(wl.v_type, wl.hd)
+    alg = {"score": wl.L * wl.Hkv * n * kb, "select": 0, "compact": moved * 2 * (kb + vb + 4)}
+    pass_bytes = alg["score"] + alg["compact"]
 
-    def step():
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        restore()
+        tria.tria_evict(ctx, k, v, pos, n, B, S, W, stream)
+    torch.cuda.synchronize()
+
+    log("timing %d steps" % args.steps)
+    tria.tria_timing_enable(ctx, True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_pass = np.zeros(args.steps)
+    st_ms = {s: 0.0 for s in tria.STAGES}
+    st_n = {s: 0 for s in tria.STAGES}
+    untimed = 0
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        restore()
+        e0.record(stream)
+        kept = tria.tria_evict(ctx, k, v, pos, n, B, S, W, stream)
+        e1.record(stream)
+        e1.synchronize()
+        t_pass[i] = e0.elapsed_time(e1)
+        ms_i, n_i, u = tria.tria_timing_read(ctx)
+        for s in tria.STAGES:
+            st_ms[s] += ms_i[s]
+            st_n[s] += n_i[s]
+        untimed += u
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    tria.tria_timing_enable(ctx, False)
+    assert kept == K
+
+    # the same pass as three sequential calls (kernels isolated from each other)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_seq = np.zeros((max(args.staged_steps, 0), 3))
+    for i in range(args.staged_steps):
+        restore()
         ev[0].record(stream)
         tria.tria_score(ctx, k, v, pos, n, raw, stream)
         ev[1].record(stream)
@@ -83,51 +187,137 @@ def main():
         ev[2].record(stream)
         tria.tria_compact(ctx, k, v, pos, n, keep, K, stream)
         ev[3].record(stream)
-
-    print("# warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        restore()
-        step()
-    torch.cuda.synchronize()
-
-    # algorithmic bytes: read K once + read and write every moved K/V/pos row
-    moved = int((keep != torch.arange(K, device=dev, dtype=torch.int32)).sum().item())
-    kb, vb = synth.row_bytes(wl.k_type, wl.hd), synth.row_bytes(wl.v_type, wl.hd)
-    score_bytes = wl.L * wl.Hkv * n * kb
-    compact_bytes = moved * 2 * (kb + vb + 4)
-
-    print("# timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    t_stage = np.zeros((args.steps, 3))
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        restore()
-        step()
         ev[3].synchronize()
-        t_stage[i] = [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
-                      ev[2].elapsed_time(ev[3])]
+        t_seq[i] = [ev[j].elapsed_time(ev[j + 1]) for j in range(3)]
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
 
-    pass_ms = t_stage.sum(axis=1)
-    ms = float(np.median(pass_ms))
-    stage_ms = t_stage.mean(axis=0)
+    ms = float(np.median(t_pass))
+    steps = args.steps
+    per_step_ms = {s: st_ms[s] / steps for s in tria.STAGES}
+    per_step_n = {s: st_n[s] // steps for s in tria.STAGES}
+    dom = max(tria.STAGES, key=lambda s: per_step_ms[s])
     rows = wl.L * wl.Hkv * n
-    names = ["score", "select", "compact"]
-    dom = int(np.argmax(stage_ms))
-    alg = {"score": score_bytes, "select": None, "compact": compact_bytes}
-    dom_bytes = alg[names[dom]]
-    achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9 if dom_bytes else None
-    pass_bytes = score_bytes + compact_bytes
+    seq_ms = {s: float(np.median(t_seq[:, j])) for j, s in enumerate(tria.STAGES)} \
+        if args.staged_steps > 0 else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_layers)
+        cpu = cpu_baseline(wl, stats, k0.cpu().numpy(), v0.cpu().numpy(), p0.cpu().numpy(),
+                           args.cpu_seconds)
 
     out = {
-        "metric": "KV tokens scored+compacted/sec and eviction-pass ms at 32K ctx; % of HBM peak",
+        "metric": METRIC,
         "value": rows / (ms * 1e-3),
-        "unit": "KV rows/s (layer x KV-head x token, scored + compacted)",
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q8_0/f16 in, f32 accumulate" if wl.k_type == synth.KV_Q8_0
+        else "f16 in, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales; "
+                "lognormal/uniform-phase statistics)",
+        "config": {"workload": wl.name, "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
+                   "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
+                   "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
+                   "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU"},
+        "pass_ms_p10_p90": [float(np.percentile(t_pass, 10)), float(np.percentile(t_pass, 90))],
+        "tokens_per_s": n / (ms * 1e-3),
+        "pass_alg_bytes": pass_bytes,
+        "pass_alg_GBs": pass_bytes / (ms * 1e-3) / 1e9,
+        "pass_frac_hbm": pass_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "moved_rows": moved,
+        "kernel_ms_per_step": per_step_ms,
+        "launches_per_step": per_step_n,
+        "untimed_launches": untimed,
+        "sequential_stage_ms": seq_ms,
+        "sequential_pass_ms": float(sum(seq_ms.values())) if seq_ms else None,
+        "wall_s_timed_loop_incl_restore": t_wall,
+        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name),
+        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name)
+                         for s in tria.STAGES},
+        "cpu_baseline": cpu,
+    }
+    ctx.close()
+    return out
+
+
+def bench_paged(args, wl):
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_tria_amd import synth, tria
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    lens = synth.paged_lengths(wl)
+    budgets = [int(wl.budget_frac * x) for x in lens]
+    m = wl.append
+    log("workload %s: %d sequences, %d..%d tokens; generating on the device" % (
+        wl.name, wl.n_seq, min(lens), max(lens)))
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, wl.seed)
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, wl.seed, dev)
+    ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
+                               list(wl.offsets), *stats)
+    pools = [pg[x] for x in ("k_pool", "v_pool", "pos_pool", "block_table")]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    log("initial pass")
+    e0.record(stream)
+    kept = tria.tria_evict_paged_batch(ctx, *pools, lens, budgets, wl.sink, wl.window, stream)
+    e1.record(stream)
+    e1.synchronize()
+    first_ms = e0.elapsed_time(e1)
+    assert kept == budgets, (kept, budgets)
+    n_now = list(budgets)
+
+    def append(r):
+        for s in range(wl.n_seq):
+            row = synth.paged_rows(pg["pos_pool"][:1, :, :1], pg["block_table"][s], n_now[s])
+            last = int(row[0, 0, n_now[s] - 1])
+            synth.append_paged(pg, s, n_now[s], m, last + 1, wl.L, wl.Hkv, wl.hd, wl.k_type,
+                               wl.v_type, wl.seed * 100003 + r * 64 + s)
+            n_now[s] += m
+
+    st_ms = {s: 0.0 for s in tria.STAGES}
+    st_n = {s: 0 for s in tria.STAGES}
+    t_round = []
+    total = args.warmup + args.steps
+    log("rounds: %d warmup + %d timed" % (args.warmup, args.steps))
+    for r in range(total):
+        append(r)
+        torch.cuda.synchronize()
+        if r == args.warmup:
+            tria.tria_timing_enable(ctx, True)
+        e0.record(stream)
+        kept = tria.tria_evict_paged_batch(ctx, *pools, n_now, budgets, wl.sink, wl.window,
+                                           stream)
+        e1.record(stream)
+        e1.synchronize()
+        if r >= args.warmup:
+            t_round.append(e0.elapsed_time(e1))
+            ms_i, n_i, _ = tria.tria_timing_read(ctx)
+            for s in tria.STAGES:
+                st_ms[s] += ms_i[s]
+                st_n[s] += n_i[s]
+        assert kept == budgets
+        n_now = list(kept)
+    tria.tria_timing_enable(ctx, False)
+    ms = float(np.median(t_round))
+    rows = sum(wl.L * wl.Hkv * (b + m) for b in budgets)
+    per_step_ms = {s: st_ms[s] / args.steps for s in tria.STAGES}
+    per_step_n = {s: st_n[s] // args.steps for s in tria.STAGES}
+    dom = max(tria.STAGES, key=lambda s: per_step_ms[s])
+    kb, vb = synth.row_bytes(wl.k_type, wl.hd), synth.row_bytes(wl.v_type, wl.hd)
+    score_bytes = rows * kb
+    out = {
+        "metric": METRIC,
+        "value": rows / (ms * 1e-3),
+        "unit": UNIT,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -135,49 +325,49 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/f16 in, f32 accumulate" if wl.k_type == synth.KV_Q8_0 else "f16 in, f32 accumulate",
-        "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales; lognormal/uniform-phase stats)",
-        "config": {"workload": wl.name, "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
-                   "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
-                   "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
-                   "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU"},
-        "pass_ms_p10_p90": [float(np.percentile(pass_ms, 10)), float(np.percentile(pass_ms, 90))],
-        "stage_ms": {nm: float(x) for nm, x in zip(names, stage_ms)},
-        "tokens_per_s": n / (ms * 1e-3),
-        "pass_alg_bytes": pass_bytes,
-        "pass_alg_GBs": pass_bytes / (ms * 1e-3) / 1e9,
-        "pass_frac_hbm": pass_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "moved_rows": moved,
-        "wall_s_timed_loop_incl_restore": t_wall,
-        "roofline": {"kernel": names[dom], "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                     "traffic": None, "alg_bytes_per_launch": dom_bytes,
-                     "avg_launch_ms": float(stage_ms[dom])},
-        "cpu_baseline": cpu,
+        "dtype": "q8_0/f16 in, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales; "
+                "lognormal/uniform-phase statistics; shuffled block order)",
+        "config": {"workload": wl.name, "sequences": wl.n_seq, "lengths": lens,
+                   "budgets": budgets, "append": m, "sink": wl.sink, "window": wl.window,
+                   "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq, "head_dim": wl.hd,
+                   "parallelism": "single GPU"},
+        "round_ms_p10_p90": [float(np.percentile(t_round, 10)), float(np.percentile(t_round, 90))],
+        "initial_pass_ms": first_ms,
+        "initial_pass_rows_per_s": sum(wl.L * wl.Hkv * x for x in lens) / (first_ms * 1e-3),
+        "kernel_ms_per_step": per_step_ms,
+        "launches_per_step": per_step_n,
+        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom],
+                             score_bytes if dom == "score" else 0, wl.name),
+        "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
     ctx.close()
+    return out
 
 
-def cpu_baseline(wl, layers):
-    """The CPU oracle on a bounded sample of the same workload (its first `layers` layers)."""
+def cpu_baseline(wl, stats, k0, v0, p0, seconds):
+    """The CPU oracle, as it stands, on whole passes over the same input (host copies of
+    the device-generated cache), repeated until about `seconds` of CPU work."""
+    import numpy as np
+
     import oracle
-    from kv_cache_eviction_tria_amd import synth
-    layers = max(1, min(layers, wl.L))
-    print("# cpu baseline: oracle on %d of %d layers" % (layers, wl.L), file=sys.stderr, flush=True)
-    case = synth.make_case(wl, device="cpu", L=layers)
-    k, v, pos = case["k"].numpy().copy(), case["v"].numpy().copy(), case["pos"].numpy().copy()
-    t = time.perf_counter()
-    oracle.evict(wl.k_type, wl.v_type, layers, wl.Hkv, wl.Hq, wl.hd, wl.theta, list(wl.offsets),
-                 k, v, pos, wl.n, wl.budget, wl.sink, wl.window, case["q_re"], case["q_im"],
-                 case["w"], want_raw=False, want_agg=False)
-    dt = time.perf_counter() - t
-    rows = layers * wl.Hkv * wl.n
-    return {"value": rows / dt, "unit": "KV rows/s (layer x KV-head x token, scored + compacted)",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d layers (%d units x %d tokens), %.2f s" % (
-                layers, wl.L, layers * wl.Hkv, wl.n, dt)}
+    log("cpu baseline: oracle on whole passes, about %.0f s" % seconds)
+    times = []
+    spent = 0.0
+    while not times or (spent < seconds and len(times) < 50):
+        k, v, pos = k0.copy(), v0.copy(), p0.copy()
+        t = time.perf_counter()
+        oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                     list(wl.offsets), k, v, pos, wl.n, wl.budget, wl.sink, wl.window, *stats,
+                     want_raw=False, want_agg=False)
+        dt = time.perf_counter() - t
+        times.append(dt)
+        spent += dt
+    rows = wl.L * wl.Hkv * wl.n
+    med = float(np.median(times))
+    return {"value": rows / med, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d whole passes (%d units x %d tokens each), %.1f s of CPU time; "
+                      "median pass %.3f s" % (len(times), wl.L * wl.Hkv, wl.n, spent, med)}
 
 
 if __name__ == "__main__":

@@ -171,7 +171,12 @@ int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
 
 /* One whole eviction pass: tria_score, tria_select, tria_compact with the
  * context's own scratch for the scores and kept indices.  Returns the kept
- * count.  budget >= n_tokens enqueues nothing and returns n_tokens. */
+ * count.  budget >= n_tokens enqueues nothing and returns n_tokens.
+ * With more than 6 layers the layers are processed in groups and the
+ * compaction of a group runs on a second stream owned by the context while
+ * the next group is scored on `stream`; the second stream waits for `stream`
+ * before its first launch and `stream` waits for it before the call returns,
+ * so the pass is ordered with respect to `stream` like a single-stream pass. */
 int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
                    int64_t sink, int64_t window, hipStream_t stream);
 
@@ -183,6 +188,25 @@ int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int
 int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t n_seq,
                            const int64_t *n_tokens, const int64_t *budget, int64_t sink,
                            int64_t window, int64_t *kept_out, hipStream_t stream);
+
+/* Per-kernel timing of the passes run through a context (a trace facility,
+ * off by default).  While enabled, every score, select and compaction launch
+ * made by the entry points above is bracketed by HIP events recorded on the
+ * stream the kernel runs on (the context's second stream for overlapped
+ * compactions).  At most TRIA_TIMED_MAX launches are recorded between two
+ * reads; later ones are counted in the read's return value and not timed.
+ * enable: 1 turns timing on, 0 off (pending records are discarded). */
+#define TRIA_TIMED_MAX 256
+#define TRIA_STAGE_SCORE 0
+#define TRIA_STAGE_SELECT 1
+#define TRIA_STAGE_COMPACT 2
+int tria_timing_enable(tria_ctx *ctx, int32_t enable);
+
+/* Wait for the recorded launches, add their durations (ms) and counts per
+ * stage into ms[3] and launches[3] (indexed by TRIA_STAGE_*; both host,
+ * written), and clear the record.  Returns the number of launches that were
+ * not timed (>= 0) or an error code. */
+int tria_timing_read(tria_ctx *ctx, double *ms, int64_t *launches);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,7 @@
 #include "tria_internal.h"
 
 namespace tria {
-int64_t select_key_scratch_rows(const Batch& b, int units_per_seq);
+int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G);
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
                               int32_t* keep, float* agg, uint32_t* key_scratch, hipStream_t s);
 }  // namespace tria
@@ -37,6 +37,16 @@ struct tria_ctx {
     size_t keep_bytes = 0;
     uint32_t* keys = nullptr;
     size_t keys_bytes = 0;
+    // second stream and events for overlapping compaction with scoring
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipEvent_t ev_group[8] = {};
+    // per-kernel timing (tria_timing_*)
+    bool timing = false;
+    hipEvent_t tev[TRIA_TIMED_MAX][2] = {};
+    int tstage[TRIA_TIMED_MAX] = {};
+    int ntimed = 0;
+    int64_t untimed = 0;
     int last_hip = 0;
 };
 
@@ -69,6 +79,35 @@ int grow(tria_ctx* ctx, void** buf, size_t* have, size_t need, hipStream_t s) {
     }
     *have = bytes;
     return TRIA_OK;
+}
+
+// Timing brackets: begin returns a record slot (or -1 when timing is off or
+// the record is full), end closes it on the same stream.
+hipError_t timed_begin(tria_ctx* ctx, int stage, hipStream_t s, int* slot) {
+    *slot = -1;
+    if (!ctx->timing) return hipSuccess;
+    if (ctx->ntimed >= TRIA_TIMED_MAX) {
+        ++ctx->untimed;
+        return hipSuccess;
+    }
+    const int i = ctx->ntimed++;
+    ctx->tstage[i] = stage;
+    *slot = i;
+    return hipEventRecord(ctx->tev[i][0], s);
+}
+
+hipError_t timed_end(tria_ctx* ctx, int slot, hipStream_t s) {
+    return slot < 0 ? hipSuccess : hipEventRecord(ctx->tev[slot][1], s);
+}
+
+// A compaction launch, timed when timing is on.
+int compact_timed(tria_ctx* ctx, const CacheView& cv, const Batch& b, int units,
+                  const int32_t* keep, hipStream_t s) {
+    int slot;
+    hipError_t e = timed_begin(ctx, TRIA_STAGE_COMPACT, s, &slot);
+    if (e == hipSuccess) e = launch_compact(cv, b, units, keep, s);
+    if (e == hipSuccess) e = timed_end(ctx, slot, s);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
 
 struct Protect {
@@ -125,32 +164,123 @@ int check_cache(const tria_cache* c, int64_t n) {
     return TRIA_OK;
 }
 
-int run_score(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
-              hipStream_t s) {
+// Coefficient tables for up to n_units units must fit before any work is queued.
+int reserve_coef(tria_ctx* ctx, int n_units, hipStream_t s) {
     const CoefGeom cg = coef_geom(ctx->k_type, ctx->hd, ctx->G);
-    int rc = grow(ctx, reinterpret_cast<void**>(&ctx->coef), &ctx->coef_bytes,
-                  (size_t)n_units * cg.words * 4, s);
+    return grow(ctx, reinterpret_cast<void**>(&ctx->coef), &ctx->coef_bytes,
+                (size_t)n_units * cg.words * 4, s);
+}
+
+// prep + score for the units of cv (layers l0 .. l0 + cv.L of the model).
+int run_score(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
+              hipStream_t s, int l0 = 0) {
+    int rc = reserve_coef(ctx, n_units, s);
     if (rc) return rc;
-    hipError_t e = launch_prep(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
-                               ctx->w, ctx->omega, ctx->m_re, ctx->m_im, ctx->coef, s);
+    const int64_t so = (int64_t)l0 * ctx->Hq * ctx->F;
+    hipError_t e = launch_prep(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re + so,
+                               ctx->q_im + so, ctx->w + so, ctx->omega, ctx->m_re, ctx->m_im,
+                               ctx->coef, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
-    e = launch_score(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->coef, raw, s);
+    int slot;
+    e = timed_begin(ctx, TRIA_STAGE_SCORE, s, &slot);
+    if (e == hipSuccess)
+        e = launch_score(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->coef, raw, s);
+    if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
     return TRIA_OK;
 }
 
 int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
-               hipStream_t s) {
-    const int ups = ctx->L * ctx->Hkv;
-    const int64_t krows = select_key_scratch_rows(b, ups);
+               hipStream_t s, int layers = -1) {
+    const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
+    const int64_t krows = select_key_scratch_rows(b, ups, ctx->G);
     if (krows > 0) {
         int rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes,
                       (size_t)krows * 4, s);
         if (rc) return rc;
     }
-    hipError_t e = launch_select_impl(b, ups, ctx->G, raw, keep, agg, ctx->keys, s);
+    int slot;
+    hipError_t e = timed_begin(ctx, TRIA_STAGE_SELECT, s, &slot);
+    if (e == hipSuccess) e = launch_select_impl(b, ups, ctx->G, raw, keep, agg, ctx->keys, s);
+    if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
     return TRIA_OK;
+}
+
+// The layers [l0, l0 + lg) of a cache as a cache of lg layers.
+CacheView sub_view(const CacheView& cv, int l0, int lg) {
+    CacheView s = cv;
+    s.L = lg;
+    const int64_t rows = cv.bt ? (int64_t)l0 * cv.n_blocks * cv.Hkv * kBlockRows
+                               : (int64_t)l0 * cv.Hkv * cv.cap;
+    s.k += rows * cv.kb;
+    s.v += rows * cv.vb;
+    s.pos += rows;
+    return s;
+}
+
+// Per-sequence offsets of the raw-score and kept-index blocks of layers l0...
+Batch sub_batch(const Batch& b, int l0, int Hkv, int G) {
+    Batch s = b;
+    for (int i = 0; i < b.n_seq; ++i) {
+        s.seq[i].raw_off += (int64_t)l0 * Hkv * b.seq[i].n * G;
+        s.seq[i].keep_off += (int64_t)l0 * Hkv * b.seq[i].kept;
+    }
+    return s;
+}
+
+constexpr int kMaxGroups = 8;
+constexpr int kLayersPerGroup = 6;
+
+// One whole pass (score -> select -> compact).  With more than one layer the
+// layers are cut into groups: score and select of group g+1 run on `s` while
+// group g is compacted on the context's second stream.  The scorer is bound by
+// the vector ALUs and the compaction by HBM, so the two overlap well.  Work
+// stays ordered with respect to `s`: the second stream waits for an event
+// recorded on `s` and `s` waits for the last compaction before returning work
+// to the caller's order.
+int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) {
+    const int L = ctx->L, n_seq = b.n_seq;
+    int ng = (L + kLayersPerGroup - 1) / kLayersPerGroup;
+    ng = ng > kMaxGroups ? kMaxGroups : ng;
+    if (ng <= 1 || !ctx->aux) {
+        const int units = n_seq * L * ctx->Hkv;
+        int rc = run_score(ctx, cv, b, units, ctx->raw, s);
+        if (rc) return rc;
+        rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, s);
+        if (rc) return rc;
+        return compact_timed(ctx, cv, b, units, ctx->keep, s);
+    }
+    const int per = (L + ng - 1) / ng;
+    // all scratch is sized for the whole pass before any work is queued
+    int rc = reserve_coef(ctx, n_seq * per * ctx->Hkv, s);
+    if (rc) return rc;
+    const int64_t krows = select_key_scratch_rows(b, L * ctx->Hkv, ctx->G);
+    if (krows > 0) {
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes, (size_t)krows * 4, s);
+        if (rc) return rc;
+    }
+    hipError_t e = hipEventRecord(ctx->ev_fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_fork, 0);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    for (int g = 0, l0 = 0; l0 < L; ++g, l0 += per) {
+        const int lg = (L - l0) < per ? (L - l0) : per;
+        const CacheView sv = sub_view(cv, l0, lg);
+        const Batch sb = sub_batch(b, l0, ctx->Hkv, ctx->G);
+        const int units = n_seq * lg * ctx->Hkv;
+        rc = run_score(ctx, sv, sb, units, ctx->raw, s, l0);
+        if (rc) return rc;
+        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, s, lg);
+        if (rc) return rc;
+        e = hipEventRecord(ctx->ev_group[g], s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_group[g], 0);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->aux);
+        if (rc) return rc;
+    }
+    e = hipEventRecord(ctx->ev_join, ctx->aux);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ctx->ev_join, 0);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
 
 }  // namespace
@@ -188,6 +318,14 @@ void tria_free(tria_ctx* ctx) {
                     ctx->m_im, ctx->coef, ctx->raw, ctx->keep,  ctx->keys};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
+    if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
+    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+    for (hipEvent_t ev : ctx->ev_group)
+        if (ev) (void)hipEventDestroy(ev);
+    for (auto& pr : ctx->tev)
+        for (hipEvent_t ev : pr)
+            if (ev) (void)hipEventDestroy(ev);
     delete ctx;
 }
 
@@ -257,6 +395,12 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
         if (e == hipSuccess) e = hipMemcpy(*ddst[i], host + i * F, F * sizeof(double), hipMemcpyHostToDevice);
     }
     free(host);
+    // second stream (default priority) and events for overlapped passes
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
+    for (int i = 0; i < kMaxGroups && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&ctx->ev_group[i], hipEventDisableTiming);
     if (e != hipSuccess) {
         const int rc = e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
         tria_free(ctx);
@@ -301,8 +445,7 @@ int tria_compact(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens,
     p.kept = kept;
     p.s_end = p.w_start = 0;
     const Batch b = one_seq(n_tokens, p);
-    hipError_t e = launch_compact(view_of(ctx, cache), b, ctx->L * ctx->Hkv, keep_idx, stream);
-    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+    return compact_timed(ctx, view_of(ctx, cache), b, ctx->L * ctx->Hkv, keep_idx, stream);
 }
 
 int64_t tria_evict(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, int64_t budget,
@@ -322,13 +465,8 @@ int64_t tria_evict(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, int
     if (rc) return rc;
     const CacheView cv = view_of(ctx, cache);
     const Batch b = one_seq(n_tokens, p);
-    rc = run_score(ctx, cv, b, units, ctx->raw, stream);
-    if (rc) return rc;
-    rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, stream);
-    if (rc) return rc;
-    hipError_t e = launch_compact(cv, b, units, ctx->keep, stream);
-    if (e != hipSuccess) return hip_fail(ctx, e);
-    return p.kept;
+    rc = run_pass(ctx, cv, b, stream);
+    return rc ? rc : p.kept;
 }
 
 int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t n_seq,
@@ -383,13 +521,38 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
     cv.Hkv = ctx->Hkv;
     cv.kb = ctx->kb;
     cv.vb = ctx->vb;
-    const int units = units_per_seq * n_seq;
-    rc = run_score(ctx, cv, b, units, ctx->raw, stream);
-    if (rc) return rc;
-    rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, stream);
-    if (rc) return rc;
-    hipError_t e = launch_compact(cv, b, units, ctx->keep, stream);
-    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+    return run_pass(ctx, cv, b, stream);
+}
+
+int tria_timing_enable(tria_ctx* ctx, int32_t enable) {
+    if (!ctx) return TRIA_E_INVAL;
+    if (enable && !ctx->tev[0][0]) {
+        for (auto& pr : ctx->tev)
+            for (hipEvent_t& ev : pr) {
+                hipError_t e = hipEventCreate(&ev);
+                if (e != hipSuccess) return hip_fail(ctx, e);
+            }
+    }
+    ctx->timing = enable != 0;
+    ctx->ntimed = 0;
+    ctx->untimed = 0;
+    return TRIA_OK;
+}
+
+int tria_timing_read(tria_ctx* ctx, double* ms, int64_t* launches) {
+    if (!ctx || !ms || !launches) return TRIA_E_INVAL;
+    for (int i = 0; i < ctx->ntimed; ++i) {
+        hipError_t e = hipEventSynchronize(ctx->tev[i][1]);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, ctx->tev[i][0], ctx->tev[i][1]);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+        ms[ctx->tstage[i]] += (double)t;
+        launches[ctx->tstage[i]] += 1;
+    }
+    const int64_t untimed = ctx->untimed;
+    ctx->ntimed = 0;
+    ctx->untimed = 0;
+    return (int)(untimed > 0x7fffffff ? 0x7fffffff : untimed);
 }
 
 }  // extern "C"

@@ -12,9 +12,10 @@
 // Mapping: one lane per cached row, 256 rows per workgroup.  Every lane of a wave needs the same coefficient at
 // the same time, so the unit's table (built by prep) is read through scalar
 // loads into SGPRs and fed to the VALU as the scalar operand; no LDS and no
-// cross-lane reduction.  Each lane streams its whole row with wide
-// non-temporal loads (K is read exactly once).  The sqrt of |K_f|^2 is shared
-// by all G heads.
+// cross-lane reduction.  Each lane reads its whole row with wide loads; one
+// load instruction touches a cache line per lane and the following loads of
+// the row hit the same lines in L1, so K crosses HBM once.  The sqrt of
+// |K_f|^2 is shared by all G heads.
 //
 // q8_0 rows: the trig part is an integer dot product per 32-value block:
 // sum_d q_d c_d = sig * sum_d q_d v_d with v the 16-bit quantised coefficient
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
         const u32x4* row = reinterpret_cast<const u32x4*>(cv.k + row_index(cv, id, r) * (HD * 2));
         u32x4 d[NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) d[i] = __builtin_nontemporal_load(row + i);
+        for (int i = 0; i < NV; ++i) d[i] = row[i];
         const uint32_t* wd = reinterpret_cast<const uint32_t*>(d);
 
         float acc[GT];
@@ -176,20 +177,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
                 const u32x4* p4 = reinterpret_cast<const u32x4*>(rp);
 #pragma unroll
                 for (int i = 0; i < W / 4; ++i) {
-                    const u32x4 t = __builtin_nontemporal_load(p4 + i);
+                    const u32x4 t = p4[i];
                     wv[4 * i] = t.x; wv[4 * i + 1] = t.y; wv[4 * i + 2] = t.z; wv[4 * i + 3] = t.w;
                 }
             } else if constexpr (RB % 8 == 0) {
                 const u32x2* p2 = reinterpret_cast<const u32x2*>(rp);
 #pragma unroll
                 for (int i = 0; i < W / 2; ++i) {
-                    const u32x2 t = __builtin_nontemporal_load(p2 + i);
+                    const u32x2 t = p2[i];
                     wv[2 * i] = t.x; wv[2 * i + 1] = t.y;
                 }
             } else {
                 const uint32_t* p1 = reinterpret_cast<const uint32_t*>(rp);
 #pragma unroll
-                for (int i = 0; i < W; ++i) wv[i] = __builtin_nontemporal_load(p1 + i);
+                for (int i = 0; i < W; ++i) wv[i] = p1[i];
             }
         } else {
             // Row starts 0 or 2 bytes past a word boundary; read only bytes of this
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
             const uint32_t* ap = reinterpret_cast<const uint32_t*>(a - sh);
             uint32_t rw[W];
 #pragma unroll
-            for (int i = 0; i < W - 1; ++i) rw[i] = __builtin_nontemporal_load(ap + i);
+            for (int i = 0; i < W - 1; ++i) rw[i] = ap[i];
             rw[W - 1] = sh ? ap[W - 1] : (uint32_t)(*reinterpret_cast<const uint16_t*>(ap + W - 1));
 #pragma unroll
             for (int i = 0; i < W - 1; ++i)

@@ -8,7 +8,8 @@
 // The budget counts the protected rows ("TriAttention Native C++ Worklog":
 // compaction logs keep exactly kv_budget rows).
 //
-// Per unit (1024 threads, thread t owns rows [t*RPT, t*RPT + RPT)):
+// Per unit (1024 threads; thread t owns rows j*1024 + t, j < RPT, so every
+// load of the raw scores is coalesced):
 //   1. moments of every head over the rows with a finite score (fp64 sums of
 //      values shifted by the head's first score, against cancellation);
 //   2. agg(r) = max_h (s_h - mu_h)/sigma_h in fp64, rounded once to fp32,
@@ -16,9 +17,11 @@
 //      order-preserving 32-bit key (-0 folded into +0);
 //   3. exact k-th-largest key among the candidates by four 8-bit radix passes
 //      over LDS histograms (one per wave; lanes that share a digit add once);
-//   4. ties at the threshold go to the lowest row indices (block scan), and
-//      the kept rows are written in ascending order (block scan).
-// Keys stay in registers for n <= 32K rows, else in a global scratch array.
+//   4. ties at the threshold go to the lowest row indices, and the kept rows
+//      are written in ascending order: ranks in row order come from wave
+//      ballots plus a prefix over the (j, wave) counts.
+// Keys live in registers for n <= 8K rows, in LDS for n <= 32K, else in a
+// global scratch array.
 #include "tria_internal.h"
 
 namespace tria {
@@ -86,7 +89,12 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d
     if (active) atomicAdd(&hist[digit], 1u);
 }
 
-template <int RPT, bool kGmemKeys>
+__device__ __forceinline__ int lane_rank(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+template <int RPT, int KM>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     Batch b, int units_per_seq, int G, const float* __restrict__ raw, int32_t* __restrict__ keep,
     float* __restrict__ agg_out, uint32_t* __restrict__ key_scratch) {
@@ -99,7 +107,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ R = raw + sd.raw_off + (int64_t)uu * n * G;
     int32_t* __restrict__ KI = keep + sd.keep_off + (int64_t)uu * sd.kept;
     float* AG = agg_out ? agg_out + (int64_t)uu * n : nullptr;
+    // KM: where the keys live -- 0 registers, 1 LDS, 2 global scratch
+    constexpr bool kGmemKeys = KM == 2;
     uint32_t* KS = kGmemKeys ? key_scratch + sd.raw_off / G + (int64_t)uu * n : nullptr;
+    __shared__ uint32_t key_lds[KM == 1 ? RPT * kSelThreads : 1];
 
     __shared__ double red[kWaves][kHeadChunk][2];
     __shared__ int redc[kWaves][kHeadChunk];
@@ -108,10 +119,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ uint32_t tot[256];
     __shared__ int scan_sh[kWaves];
     __shared__ int found_sh[2];
+    __shared__ int cnt_sh[RPT * kWaves];
 
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int64_t r0 = (int64_t)t * RPT;
-    constexpr int kUnroll = kGmemKeys ? 2 : RPT;  // register keys need constant indices
+    auto row_of = [&](int j) -> int64_t { return (int64_t)j * kSelThreads + t; };
+    // loops over owned rows are fully unrolled when keys live in registers
 
     // 1. moments per head (rows strided by 1024 for coalesced reads)
     for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
@@ -176,10 +188,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
     // 2. aggregated score -> order-preserving key
     const int64_t cand_lo = sd.s_end, cand_hi = sd.w_start;
-    uint32_t key[kGmemKeys ? 1 : RPT];
-#pragma unroll kUnroll
+    uint32_t key[KM == 0 ? RPT : 1];
+#pragma unroll (KM == 0 ? RPT : 4)
     for (int j = 0; j < RPT; ++j) {
-        const int64_t r = r0 + j;
+        const int64_t r = row_of(j);
         if (r < n) {
             double best = -INFINITY;
             bool bad = false;
@@ -192,13 +204,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const float a = bad ? -INFINITY : (float)best;
             if (AG) AG[r] = a;
             const uint32_t kk = order_key(a);
-            if constexpr (kGmemKeys) KS[r] = kk; else key[j] = kk;
+            if constexpr (KM == 2) KS[r] = kk;
+            else if constexpr (KM == 1) key_lds[j * kSelThreads + t] = kk;
+            else key[j] = kk;
         } else {
-            if constexpr (!kGmemKeys) key[j] = 0;
+            if constexpr (KM == 1) key_lds[j * kSelThreads + t] = 0;
+            else if constexpr (KM == 0) key[j] = 0;
         }
     }
     auto get_key = [&](int j) -> uint32_t {
-        if constexpr (kGmemKeys) return KS[r0 + j]; else return key[j];
+        if constexpr (KM == 2) return KS[row_of(j)];
+        else if constexpr (KM == 1) return key_lds[j * kSelThreads + t];
+        else return key[j];
     };
     auto is_cand = [&](int64_t r) -> bool { return r >= cand_lo && r < cand_hi; };
 
@@ -214,11 +231,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const int shift = 24 - 8 * pass;
             for (int i = lane; i < 256; i += 64) hist[wid][i] = 0;
             __syncthreads();
-#pragma unroll kUnroll
+#pragma unroll (KM == 0 ? RPT : 4)
             for (int j = 0; j < RPT; ++j) {
-                const int64_t r = r0 + j;
+                const int64_t r = row_of(j);
                 const uint32_t kk = get_key(j);
-                const bool act = is_cand(r) && ((kk & mask) == prefix);
+                const bool act = r < n && is_cand(r) && ((kk & mask) == prefix);
                 hist_add(hist[wid], act, (kk >> shift) & 255u);
             }
             __syncthreads();
@@ -260,58 +277,93 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     const uint32_t T = prefix;
 
-    // 4. ties at T go to the lowest rows; then write kept rows in order
+    // 4. ties at T go to the lowest rows; then write kept rows in order.
+    // Row order is (j, wave, lane); ranks = prefix over the (j, wave) counts
+    // plus the lane's rank within its wave's ballot.
     const bool radix = !take_none && !take_all;
-    int my_ties = 0;
-#pragma unroll kUnroll
-    for (int j = 0; j < RPT; ++j) {
-        const int64_t r = r0 + j;
-        if (radix && r < n && is_cand(r) && get_key(j) == T) ++my_ties;
-    }
-    int total;
-    const int tie_base0 = block_excl_scan(my_ties, scan_sh, &total);
-    auto decide = [&](int j, int& tie_rank) -> bool {
-        const int64_t r = r0 + j;
-        if (r >= n) return false;
-        if (!is_cand(r) || take_all) return true;
-        if (take_none) return false;
-        const uint32_t kk = get_key(j);
-        if (kk == T) return (tie_rank++) < krem;
-        return kk > T;
-    };
-    int my_keep = 0;
-    {
-        int tr = tie_base0;
-#pragma unroll kUnroll
-        for (int j = 0; j < RPT; ++j) my_keep += decide(j, tr) ? 1 : 0;
-    }
-    int out = block_excl_scan(my_keep, scan_sh, &total);
-    {
-        int tr = tie_base0;
-#pragma unroll kUnroll
+    auto ordered_ranks = [&](auto flag_of, auto use_rank) {
+#pragma unroll (KM == 0 ? RPT : 4)
         for (int j = 0; j < RPT; ++j) {
-            if (decide(j, tr) && out < sd.kept) KI[out++] = (int32_t)(r0 + j);
+            const uint64_t m = __ballot(flag_of(j));
+            if (lane == 0) cnt_sh[j * kWaves + wid] = __popcll(m);
+        }
+        __syncthreads();
+        int loc[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * t + q;
+            loc[q] = sum;
+            sum += e < RPT * kWaves ? cnt_sh[e] : 0;
+        }
+        int total;
+        const int base = block_excl_scan(sum, scan_sh, &total);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * t + q;
+            if (e < RPT * kWaves) cnt_sh[e] = base + loc[q];
+        }
+        __syncthreads();
+#pragma unroll (KM == 0 ? RPT : 4)
+        for (int j = 0; j < RPT; ++j) {
+            const bool f = flag_of(j);
+            const uint64_t m = __ballot(f);
+            if (f) use_rank(j, cnt_sh[j * kWaves + wid] + lane_rank(m));
+        }
+        __syncthreads();
+    };
+    // keep decision bits, one per owned row
+    uint32_t kbits[(RPT + 31) / 32];
+#pragma unroll
+    for (int q = 0; q < (RPT + 31) / 32; ++q) kbits[q] = 0;
+    auto set_keep = [&](int j) { kbits[j >> 5] |= 1u << (j & 31); };
+#pragma unroll (KM == 0 ? RPT : 4)
+    for (int j = 0; j < RPT; ++j) {
+        const int64_t r = row_of(j);
+        if (r >= n) continue;
+        if (!is_cand(r) || take_all) {
+            set_keep(j);
+        } else if (radix && get_key(j) > T) {
+            set_keep(j);
         }
     }
+    if (radix) {
+        ordered_ranks(
+            [&](int j) {
+                const int64_t r = row_of(j);
+                return r < n && is_cand(r) && get_key(j) == T;
+            },
+            [&](int j, int rank) {
+                if (rank < krem) set_keep(j);
+            });
+    }
+    ordered_ranks([&](int j) { return ((kbits[j >> 5] >> (j & 31)) & 1u) != 0; },
+                  [&](int j, int rank) {
+                      if (rank < sd.kept) KI[rank] = (int32_t)row_of(j);
+                  });
 }
 
-template <int RPT, bool GM>
+template <int RPT, int KM>
 void run_sel(int grid, hipStream_t s, const Batch& b, int ups, int G, const float* raw,
              int32_t* keep, float* agg, uint32_t* ks) {
-    hipLaunchKernelGGL((select_kernel<RPT, GM>), dim3(grid), dim3(kSelThreads), 0, s, b, ups, G,
+    hipLaunchKernelGGL((select_kernel<RPT, KM>), dim3(grid), dim3(kSelThreads), 0, s, b, ups, G,
                        raw, keep, agg, ks);
 }
 
 }  // namespace
 
-// Rows a key-scratch array must hold for a batch (0 when keys stay in registers).
-int64_t select_key_scratch_rows(const Batch& b, int units_per_seq) {
-    int64_t max_n = 0, total = 0;
+// Rows a key-scratch array must hold for a batch (0 when keys stay on chip).
+// Unit uu of sequence i uses rows raw_off/G + uu*n .. + n of the array, so the
+// size is the largest such end (the batch may describe a group of layers whose
+// offsets start past zero).
+int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G) {
+    int64_t max_n = 0, end = 0;
     for (int i = 0; i < b.n_seq; ++i) {
-        max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
-        total += b.seq[i].n * units_per_seq;
+        const SeqDesc& sd = b.seq[i];
+        max_n = sd.n > max_n ? sd.n : max_n;
+        const int64_t e = sd.raw_off / G + (int64_t)units_per_seq * sd.n;
+        end = e > end ? e : end;
     }
-    return max_n > 32 * kSelThreads ? total : 0;
+    return max_n > 32 * kSelThreads ? end : 0;
 }
 
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
@@ -321,15 +373,15 @@ hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const fl
     if (max_n <= 0) return hipSuccess;
     const int grid = units_per_seq * b.n_seq;
     const int64_t rpt = (max_n + kSelThreads - 1) / kSelThreads;
-    if (rpt <= 1) run_sel<1, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 2) run_sel<2, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 4) run_sel<4, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 8) run_sel<8, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 16) run_sel<16, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 32) run_sel<32, false>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 64) run_sel<64, true>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 128) run_sel<128, true>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 256) run_sel<256, true>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    if (rpt <= 1) run_sel<1, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 2) run_sel<2, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 4) run_sel<4, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 8) run_sel<8, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 16) run_sel<16, 1>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 32) run_sel<32, 1>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 64) run_sel<64, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 128) run_sel<128, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    else if (rpt <= 256) run_sel<256, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

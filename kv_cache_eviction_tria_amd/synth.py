@@ -209,3 +209,63 @@ def paged_lengths(wl: Workload):
 def shuffled_blocks(n_blocks: int, seed: int):
     rng = np.random.Generator(np.random.PCG64(seed * 31 + 5))
     return rng.permutation(n_blocks).astype(np.int32)
+
+
+def gen_paged(L: int, Hkv: int, hd: int, k_type: int, v_type: int, lens, seed: int,
+              device="cpu", extra_blocks: int = 0):
+    """Paged cache for sequences of the given lengths.
+
+    Pools [L][n_blocks][Hkv][16][row_bytes] (K, V) and [L][n_blocks][Hkv][16]
+    (positions 0..n-1); each sequence's blocks are a slice of one seeded random
+    permutation of the physical blocks.  block_table: int32 [n_seq][max_blocks]
+    (unused entries -1).  `extra_blocks` leaves room for appended tokens.
+    """
+    device = torch.device(device)
+    kb, vb = row_bytes(k_type, hd), row_bytes(v_type, hd)
+    nblk = [(n + extra_blocks * BLOCK + BLOCK - 1) // BLOCK for n in lens]
+    total = sum(nblk)
+    perm = torch.from_numpy(shuffled_blocks(total, seed)).to(device)
+    max_blocks = max(nblk)
+    bt = torch.full((len(lens), max_blocks), -1, dtype=torch.int32, device=device)
+    k_pool = torch.zeros(L, total, Hkv, BLOCK, kb, dtype=torch.uint8, device=device)
+    v_pool = torch.zeros(L, total, Hkv, BLOCK, vb, dtype=torch.uint8, device=device)
+    p_pool = torch.zeros(L, total, Hkv, BLOCK, dtype=torch.int32, device=device)
+    start = 0
+    for s, n in enumerate(lens):
+        blocks = perm[start:start + nblk[s]]
+        start += nblk[s]
+        bt[s, :nblk[s]] = blocks
+        cap = nblk[s] * BLOCK
+        k, v, pos = gen_cache(L, Hkv, hd, cap, n, k_type, v_type, seed * 1000 + s, device)
+        # [L][Hkv][cap][rb] -> [L][blk][Hkv][16][rb]
+        k_pool[:, blocks] = k.view(L, Hkv, nblk[s], BLOCK, kb).transpose(1, 2)
+        v_pool[:, blocks] = v.view(L, Hkv, nblk[s], BLOCK, vb).transpose(1, 2)
+        p_pool[:, blocks] = pos.view(L, Hkv, nblk[s], BLOCK).transpose(1, 2)
+    return dict(k_pool=k_pool, v_pool=v_pool, pos_pool=p_pool, block_table=bt, lens=list(lens),
+                n_blocks=total)
+
+
+def paged_rows(pool: torch.Tensor, bt_row: torch.Tensor, n: int) -> torch.Tensor:
+    """Logical rows 0..n-1 of one sequence: [L][Hkv][n][...] from a pool."""
+    nb = (n + BLOCK - 1) // BLOCK
+    blocks = bt_row[:nb].long()
+    x = pool[:, blocks]  # [L][nb][Hkv][16][...]
+    x = x.transpose(1, 2).reshape(pool.shape[0], pool.shape[2], nb * BLOCK, *pool.shape[4:])
+    return x[:, :, :n]
+
+
+def append_paged(pg: dict, s: int, n: int, m: int, first_pos: int, L: int, Hkv: int, hd: int,
+                 k_type: int, v_type: int, seed: int):
+    """Write m fresh rows (same recipe as gen_cache) at logical rows n..n+m-1 of
+    sequence s, with positions first_pos, first_pos+1, ... (decode appends)."""
+    pools = pg["k_pool"], pg["v_pool"], pg["pos_pool"]
+    device = pools[0].device
+    k, v, _ = gen_cache(L, Hkv, hd, m, m, k_type, v_type, seed, device)
+    r = torch.arange(n, n + m, device=device)
+    blk = pg["block_table"][s].to(device).long()[r >> 4]
+    within = r & (BLOCK - 1)
+    pos = (first_pos + torch.arange(m, device=device, dtype=torch.int32))
+    # advanced indices around a slice put the row dimension first: [m][L][Hkv][...]
+    pools[0][:, blk, :, within] = k.permute(2, 0, 1, 3)
+    pools[1][:, blk, :, within] = v.permute(2, 0, 1, 3)
+    pools[2][:, blk, :, within] = pos.view(m, 1, 1).expand(m, L, Hkv)

@@ -89,6 +89,10 @@ def lib():
             L.tria_evict_paged_batch.restype = ctypes.c_int
             L.tria_evict_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32, vp, vp, i64,
                                                  i64, vp, vp]
+            L.tria_timing_enable.restype = ctypes.c_int
+            L.tria_timing_enable.argtypes = [vp, i32]
+            L.tria_timing_read.restype = ctypes.c_int
+            L.tria_timing_read.argtypes = [vp, vp, vp]
             _lib = L
     return _lib
 
@@ -228,6 +232,24 @@ def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, 
     _check(lib().tria_evict_paged_batch(ctx.handle, ctypes.byref(pc), n_seq, nt, bd, sink,
                                         window, kept, _stream(stream)), "tria_evict_paged_batch")
     return [int(x) for x in kept]
+
+
+def tria_timing_enable(ctx: TriaCtx, enable: bool) -> None:
+    _check(lib().tria_timing_enable(ctx.handle, 1 if enable else 0), "tria_timing_enable")
+
+
+STAGES = ("score", "select", "compact")
+
+
+def tria_timing_read(ctx: TriaCtx):
+    """Summed kernel ms and launch counts per stage since the last read:
+    ({stage: ms}, {stage: launches}, untimed_launches)."""
+    ms = (ctypes.c_double * 3)()
+    n = (ctypes.c_int64 * 3)()
+    rc = lib().tria_timing_read(ctx.handle, ms, n)
+    _check(rc, "tria_timing_read")
+    return ({s: float(ms[i]) for i, s in enumerate(STAGES)},
+            {s: int(n[i]) for i, s in enumerate(STAGES)}, int(rc))
 
 
 def tria_free(ctx: TriaCtx) -> None:

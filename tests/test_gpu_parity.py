@@ -154,8 +154,11 @@ def test_second_pass_uses_absolute_position():
     ctx.close()
 
 
-def test_evict_equals_the_three_stages():
-    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="stages", L=2, Hkv=4, Hq=16, k_type=Q8)
+@pytest.mark.parametrize("L", [2, 14])
+def test_evict_equals_the_three_stages(L):
+    """tria_evict (layer groups overlapped on two streams when L > 6) leaves the same
+    cache as score -> select -> compact run one after the other."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="stages", L=L, Hkv=4, Hq=16, k_type=Q8)
     n, B, S, W = 9000, 2000, 4, 512
     case = synth.make_case(wl, device="cpu", n=n, cap=n + 5)
     stats = (case["q_re"], case["q_im"], case["w"])
@@ -268,3 +271,47 @@ def test_full_qwen3_8b_32k_q8():
 def test_full_hd256_48x4_128k():
     wl = WL["hd256_48x4_128k_f16"]
     _full_size(wl, [(0, 0), (47, 3), (23, 2)])
+
+
+@pytest.mark.parametrize("k_type", [Q8, F16])
+def test_paged_batch(k_type):
+    """Paged cache, 16-row blocks in shuffled physical order, several sequences of
+    different lengths (one with nothing to evict) in one batched pass; every
+    sequence checked against the oracle on its logical rows."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged", L=7, Hkv=2, Hq=8, hd=128,
+                 k_type=k_type)
+    lens = [3000, 517, 1200, 64, 2048]
+    budgets = [900, 150, 1200, 70, 600]  # seq 3: budget >= n keeps everything
+    S, W = 0, 128
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 77)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 5)
+    before = [(synth.paged_rows(pg["k_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["v_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["pos_pool"], pg["block_table"][s], n).numpy().copy())
+              for s, n in enumerate(lens)]
+    pu.say("case paged k%d lens %s" % (k_type, lens))
+    ctx = pu.make_ctx(wl, stats)
+    dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+    kept = tria.tria_evict_paged_batch(ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"],
+                                       dev["block_table"], lens, budgets, S, W)
+    torch.cuda.synchronize()
+    bt = dev["block_table"].cpu()
+    for s, n in enumerate(lens):
+        K = oracle.kept_count(n, budgets[s], S, W)
+        assert kept[s] == K
+        k0, v0, p0 = before[s]
+        o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                         list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, budgets[s], S, W,
+                         *stats, compact=False)
+        ka = synth.paged_rows(dev["k_pool"].cpu(), bt[s], n).numpy()
+        va = synth.paged_rows(dev["v_pool"].cpu(), bt[s], n).numpy()
+        pa = synth.paged_rows(dev["pos_pool"].cpu(), bt[s], n).numpy()
+        for l in range(wl.L):
+            for h in range(wl.Hkv):
+                keep = pa[l, h, :K]  # positions were 0..n-1: the kept rows
+                where = "paged seq %d unit (%d,%d)" % (s, l, h)
+                pu.check_kept(keep, o["keep_idx"][l, h], o["agg"][l, h], n, budgets[s], S, W,
+                              where)
+                pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
+                pu.check_gather(v0[l, h], va[l, h], keep, K, where + " V")
+    ctx.close()
