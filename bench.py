@@ -55,6 +55,8 @@ def parse():
                     help="CPU work the oracle baseline aims for (whole passes, at least one)")
     ap.add_argument("--staged-steps", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--layers-per-group", type=int, default=0,
+                    help="tria_set_pipeline: 0 = one group; > 0 = overlapped layer groups")
     return ap.parse_args()
 
 
@@ -123,6 +125,7 @@ def bench_contiguous(args, wl):
     k0, v0, p0 = k.clone(), v.clone(), pos.clone()
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
+    tria.tria_set_pipeline(ctx, args.layers_per_group)
     K = tria.tria_kept_count(n, B, S, W)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -173,6 +176,7 @@ def bench_contiguous(args, wl):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     tria.tria_timing_enable(ctx, False)
+    tria.tria_device_status(ctx)  # raises if a compaction gave up a wait
     assert kept == K
 
     # the same pass as three sequential calls (kernels isolated from each other)
@@ -223,7 +227,8 @@ def bench_contiguous(args, wl):
         "config": {"workload": wl.name, "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
                    "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
-                   "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU"},
+                   "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU",
+                   "layers_per_group": args.layers_per_group},
         "pass_ms_p10_p90": [float(np.percentile(t_pass, 10)), float(np.percentile(t_pass, 90))],
         "tokens_per_s": n / (ms * 1e-3),
         "pass_alg_bytes": pass_bytes,
@@ -263,6 +268,7 @@ def bench_paged(args, wl):
     pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, wl.seed, dev)
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
+    tria.tria_set_pipeline(ctx, args.layers_per_group)
     pools = [pg[x] for x in ("k_pool", "v_pool", "pos_pool", "block_table")]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -307,6 +313,7 @@ def bench_paged(args, wl):
         assert kept == budgets
         n_now = list(kept)
     tria.tria_timing_enable(ctx, False)
+    tria.tria_device_status(ctx)  # raises if a compaction gave up a wait
     ms = float(np.median(t_round))
     rows = sum(wl.L * wl.Hkv * (b + m) for b in budgets)
     per_step_ms = {s: st_ms[s] / args.steps for s in tria.STAGES}

@@ -64,6 +64,8 @@ extern "C" {
 #define TRIA_E_UNSUPPORTED (-2) /* shape outside the GPU scorer's eligibility gate */
 #define TRIA_E_HIP (-3)         /* a HIP runtime call failed; see tria_last_hip_error */
 #define TRIA_E_NOMEM (-4)       /* device or host allocation failed */
+#define TRIA_E_DEVICE (-5)      /* a compaction workgroup gave up a bounded wait (reported by
+                                   tria_device_status; the cache is then not trustworthy) */
 
 /* Storage types of a cached row. */
 #define TRIA_KV_F16 0  /* head_dim IEEE fp16 values, 2*head_dim bytes */
@@ -163,20 +165,21 @@ int64_t tria_select(tria_ctx *ctx, const float *raw_scores, int64_t n_tokens, in
  * "Phase B" step 4; [WL], "What was implemented": GPU gather/repack):
  *   row d <- row keep_idx[d] for d < kept, in every unit.  Bytes are copied
  *   exactly; rows >= kept are left unspecified.
- * keep_idx entries must satisfy d <= keep_idx[d] < n_tokens (ascending
- * indices do); an entry outside that range is skipped (the row is left as it
- * was) and never read out of bounds. */
+ * keep_idx must be strictly ascending per unit (as tria_select writes it).
+ * An entry outside [d, n_tokens) is skipped (row d is left as it was).
+ * Indices that are not ascending never cause an access out of bounds, but the
+ * result is then unspecified. */
 int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
                  const int32_t *keep_idx, int64_t kept, hipStream_t stream);
 
 /* One whole eviction pass: tria_score, tria_select, tria_compact with the
  * context's own scratch for the scores and kept indices.  Returns the kept
  * count.  budget >= n_tokens enqueues nothing and returns n_tokens.
- * With more than 6 layers the layers are processed in groups and the
- * compaction of a group runs on a second stream owned by the context while
- * the next group is scored on `stream`; the second stream waits for `stream`
- * before its first launch and `stream` waits for it before the call returns,
- * so the pass is ordered with respect to `stream` like a single-stream pass. */
+ * With layer groups (tria_set_pipeline) the selection and compaction of a
+ * group run on a second stream owned by the context while later groups are
+ * scored on `stream`; the second stream waits for an event recorded on
+ * `stream` and `stream` waits for it before the call returns, so the pass is
+ * ordered with respect to `stream` like a single-stream pass. */
 int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
                    int64_t sink, int64_t window, hipStream_t stream);
 
@@ -188,6 +191,21 @@ int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int
 int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t n_seq,
                            const int64_t *n_tokens, const int64_t *budget, int64_t sink,
                            int64_t window, int64_t *kept_out, hipStream_t stream);
+
+/* Pipelining of tria_evict / tria_evict_paged_batch.  layers_per_group = 0
+ * (the default): every layer is scored, then selected, then compacted, all on
+ * the caller's stream.  > 0: the layers are processed in groups of that many
+ * (at most 8 groups; larger groups if needed) and the selection and
+ * compaction of a group run on the context's second stream while the later
+ * groups are scored on the caller's stream (see tria_evict).  Results are
+ * identical either way.  Returns TRIA_OK or TRIA_E_INVAL. */
+int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
+
+/* Waits for the whole device, then reports and clears the context's device
+ * error word: TRIA_OK, or TRIA_E_DEVICE if a compaction launched through this
+ * context gave up one of its bounded waits since the last call (its output
+ * is then not trustworthy).  A diagnostic call: it synchronises. */
+int tria_device_status(tria_ctx *ctx);
 
 /* Per-kernel timing of the passes run through a context (a trace facility,
  * off by default).  While enabled, every score, select and compaction launch

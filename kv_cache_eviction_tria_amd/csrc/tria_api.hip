@@ -11,8 +11,12 @@
 
 namespace tria {
 int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G);
+hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float* raw,
+                          PartRec* part, hipStream_t s);
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
-                              int32_t* keep, float* agg, uint32_t* key_scratch, hipStream_t s);
+                              const PartRec* part, int32_t* keep, float* agg,
+                              uint32_t* key_scratch, int32_t* chunk_pb, uint32_t* ticket,
+                              hipStream_t s);
 }  // namespace tria
 
 using namespace tria;
@@ -37,10 +41,17 @@ struct tria_ctx {
     size_t keep_bytes = 0;
     uint32_t* keys = nullptr;
     size_t keys_bytes = 0;
+    PartRec* part = nullptr;
+    size_t part_bytes = 0;
+    int32_t* pb = nullptr;  // chunk prefix counts (selector -> compaction)
+    size_t pb_bytes = 0;
+    CompactState cst = {nullptr, 0, 0, nullptr, nullptr};
+    size_t flag_bytes = 0;
     // second stream and events for overlapping compaction with scoring
     hipStream_t aux = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    hipEvent_t ev_join = nullptr;
     hipEvent_t ev_group[8] = {};
+    int layers_per_group = 0;  // 0: one group (tria_set_pipeline)
     // per-kernel timing (tria_timing_*)
     bool timing = false;
     hipEvent_t tev[TRIA_TIMED_MAX][2] = {};
@@ -100,12 +111,29 @@ hipError_t timed_end(tria_ctx* ctx, int slot, hipStream_t s) {
     return slot < 0 ? hipSuccess : hipEventRecord(ctx->tev[slot][1], s);
 }
 
-// A compaction launch, timed when timing is on.
+// Compaction flags for a launch over these units (zeroed when allocated).
+int reserve_flags(tria_ctx* ctx, const Batch& b, int units, hipStream_t s) {
+    const int64_t words = compact_flag_words(b, units);
+    void* f = ctx->cst.flags;
+    const size_t had = ctx->flag_bytes;
+    int rc = grow(ctx, &f, &ctx->flag_bytes, (size_t)words * 4, s);
+    ctx->cst.flags = static_cast<uint32_t*>(f);
+    if (rc) return rc;
+    if (ctx->flag_bytes != had) {
+        hipError_t e = hipMemsetAsync(ctx->cst.flags, 0, ctx->flag_bytes, s);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+    }
+    ctx->cst.flag_words = (int64_t)(ctx->flag_bytes / 4);
+    return TRIA_OK;
+}
+
+// A compaction launch, timed when timing is on.  pb: the selector's chunk
+// prefix counts, or nullptr to derive them from keep into ctx->pb.
 int compact_timed(tria_ctx* ctx, const CacheView& cv, const Batch& b, int units,
-                  const int32_t* keep, hipStream_t s) {
+                  const int32_t* keep, const int32_t* pb, hipStream_t s) {
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_COMPACT, s, &slot);
-    if (e == hipSuccess) e = launch_compact(cv, b, units, keep, s);
+    if (e == hipSuccess) e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
@@ -155,6 +183,8 @@ Batch one_seq(int64_t n, const Protect& p) {
     b.seq[0].w_start = p.w_start;
     b.seq[0].raw_off = 0;
     b.seq[0].keep_off = 0;
+    b.seq[0].part_off = 0;
+    b.seq[0].pb_off = 0;
     return b;
 }
 
@@ -171,37 +201,78 @@ int reserve_coef(tria_ctx* ctx, int n_units, hipStream_t s) {
                 (size_t)n_units * cg.words * 4, s);
 }
 
-// prep + score for the units of cv (layers l0 .. l0 + cv.L of the model).
-int run_score(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
-              hipStream_t s, int l0 = 0) {
-    int rc = reserve_coef(ctx, n_units, s);
+// Coefficient tables of every unit of the batch (laid out per unit of the
+// whole model, see Batch::coef_L).
+int run_prep(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, hipStream_t s) {
+    int rc = reserve_coef(ctx, b.n_seq * ctx->L * ctx->Hkv, s);
     if (rc) return rc;
-    const int64_t so = (int64_t)l0 * ctx->Hq * ctx->F;
-    hipError_t e = launch_prep(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re + so,
-                               ctx->q_im + so, ctx->w + so, ctx->omega, ctx->m_re, ctx->m_im,
-                               ctx->coef, s);
-    if (e != hipSuccess) return hip_fail(ctx, e);
-    int slot;
-    e = timed_begin(ctx, TRIA_STAGE_SCORE, s, &slot);
-    if (e == hipSuccess)
-        e = launch_score(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->coef, raw, s);
-    if (e == hipSuccess) e = timed_end(ctx, slot, s);
-    if (e != hipSuccess) return hip_fail(ctx, e);
-    return TRIA_OK;
+    hipError_t e = launch_prep(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
+                               ctx->w, ctx->omega, ctx->m_re, ctx->m_im, ctx->coef, s);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
 
-int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
-               hipStream_t s, int layers = -1) {
-    const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
-    const int64_t krows = select_key_scratch_rows(b, ups, ctx->G);
-    if (krows > 0) {
-        int rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes,
-                      (size_t)krows * 4, s);
-        if (rc) return rc;
+// The score kernels of the units of cv, tables already prepared.
+int run_score_only(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
+                   PartRec* part, hipStream_t s) {
+    int slot;
+    hipError_t e = timed_begin(ctx, TRIA_STAGE_SCORE, s, &slot);
+    if (e == hipSuccess)
+        e = launch_score(cv, b, n_units, ctx->k_type, ctx->G, ctx->hd, ctx->coef, raw, part, s);
+    if (e == hipSuccess) e = timed_end(ctx, slot, s);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+}
+
+// prep + score.
+int run_score(tria_ctx* ctx, const CacheView& cv, const Batch& b, int n_units, float* raw,
+              PartRec* part, hipStream_t s) {
+    int rc = run_prep(ctx, cv, b, n_units, s);
+    return rc ? rc : run_score_only(ctx, cv, b, n_units, raw, part, s);
+}
+
+// Chunk prefix counts of a batch whose units are units_per_seq per sequence.
+int reserve_pb(tria_ctx* ctx, const Batch& b, int units_per_seq, hipStream_t s) {
+    int64_t words = 0;
+    for (int i = 0; i < b.n_seq; ++i) {
+        const SeqDesc& sd = b.seq[i];
+        const int64_t e = sd.pb_off + (int64_t)units_per_seq * chunk_bounds(sd.kept);
+        words = e > words ? e : words;
     }
+    return grow(ctx, reinterpret_cast<void**>(&ctx->pb), &ctx->pb_bytes, (size_t)words * 4, s);
+}
+
+// Scratch for the moment partials and the key array of a batch whose units
+// are units_per_seq per sequence (the largest end offset over the sequences).
+int reserve_select(tria_ctx* ctx, const Batch& b, int units_per_seq, hipStream_t s) {
+    int64_t recs = 0;
+    for (int i = 0; i < b.n_seq; ++i) {
+        const SeqDesc& sd = b.seq[i];
+        const int64_t e = (sd.part_off + (int64_t)units_per_seq * part_tiles(sd.n)) * ctx->G;
+        recs = e > recs ? e : recs;
+    }
+    int rc = grow(ctx, reinterpret_cast<void**>(&ctx->part), &ctx->part_bytes,
+                  (size_t)recs * sizeof(PartRec), s);
+    if (rc) return rc;
+    rc = reserve_pb(ctx, b, units_per_seq, s);
+    if (rc) return rc;
+    const int64_t krows = select_key_scratch_rows(b, units_per_seq, ctx->G);
+    if (krows > 0)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes, (size_t)krows * 4, s);
+    return rc;
+}
+
+// Select over `layers` layers per sequence (all by default).  have_part: the
+// scorer already wrote the moment partials of these scores into ctx->part.
+int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
+               bool have_part, hipStream_t s, int layers = -1) {
+    const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
+    int rc = reserve_select(ctx, b, ups, s);
+    if (rc) return rc;
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_SELECT, s, &slot);
-    if (e == hipSuccess) e = launch_select_impl(b, ups, ctx->G, raw, keep, agg, ctx->keys, s);
+    if (e == hipSuccess && !have_part) e = launch_moments(b, ups, ctx->G, raw, ctx->part, s);
+    if (e == hipSuccess)
+        e = launch_select_impl(b, ups, ctx->G, raw, ctx->part, keep, agg, ctx->keys, ctx->pb,
+                               ctx->cst.ticket, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
     return TRIA_OK;
@@ -220,62 +291,64 @@ CacheView sub_view(const CacheView& cv, int l0, int lg) {
 }
 
 // Per-sequence offsets of the raw-score and kept-index blocks of layers l0...
-Batch sub_batch(const Batch& b, int l0, int Hkv, int G) {
+Batch sub_batch(const Batch& b, int l0, int L, int Hkv, int G) {
     Batch s = b;
     for (int i = 0; i < b.n_seq; ++i) {
         s.seq[i].raw_off += (int64_t)l0 * Hkv * b.seq[i].n * G;
         s.seq[i].keep_off += (int64_t)l0 * Hkv * b.seq[i].kept;
+        s.seq[i].part_off += (int64_t)l0 * Hkv * part_tiles(b.seq[i].n);
+        s.seq[i].pb_off += (int64_t)l0 * Hkv * chunk_bounds(b.seq[i].kept);
     }
+    s.coef_L = b.coef_L ? b.coef_L : L;
+    s.coef_l0 = b.coef_l0 + l0;
     return s;
 }
 
 constexpr int kMaxGroups = 8;
-constexpr int kLayersPerGroup = 6;
 
-// One whole pass (score -> select -> compact).  With more than one layer the
-// layers are cut into groups: score and select of group g+1 run on `s` while
-// group g is compacted on the context's second stream.  The scorer is bound by
-// the vector ALUs and the compaction by HBM, so the two overlap well.  Work
-// stays ordered with respect to `s`: the second stream waits for an event
-// recorded on `s` and `s` waits for the last compaction before returning work
-// to the caller's order.
+// One whole pass (score -> select -> compact).  With more than one group of
+// layers (tria_set_pipeline): the coefficient tables of all layers are built first, then the
+// groups are scored back to back on `s`; the selection and compaction of
+// group g run on the context's second stream once g's scores are written
+// (an event), overlapping the scoring of the later groups.  The scorer is
+// bound by the vector ALUs, the compaction by HBM.  The second stream waits
+// for an event recorded on `s` before its first launch and `s` waits for the
+// last compaction, so the pass stays ordered with respect to `s`.
 int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) {
     const int L = ctx->L, n_seq = b.n_seq;
-    int ng = (L + kLayersPerGroup - 1) / kLayersPerGroup;
+    const int lpg = ctx->layers_per_group > 0 ? ctx->layers_per_group : L;
+    int ng = (L + lpg - 1) / lpg;
     ng = ng > kMaxGroups ? kMaxGroups : ng;
+    const int all_units = n_seq * L * ctx->Hkv;
+    // all scratch is sized for the whole pass before any work is queued
+    int rc = reserve_select(ctx, b, L * ctx->Hkv, s);
+    if (rc) return rc;
+    rc = reserve_flags(ctx, b, all_units, s);
+    if (rc) return rc;
+    rc = run_prep(ctx, cv, b, all_units, s);
+    if (rc) return rc;
     if (ng <= 1 || !ctx->aux) {
-        const int units = n_seq * L * ctx->Hkv;
-        int rc = run_score(ctx, cv, b, units, ctx->raw, s);
+        rc = run_score_only(ctx, cv, b, all_units, ctx->raw, ctx->part, s);
         if (rc) return rc;
-        rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, s);
+        rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, true, s);
         if (rc) return rc;
-        return compact_timed(ctx, cv, b, units, ctx->keep, s);
+        return compact_timed(ctx, cv, b, all_units, ctx->keep, ctx->pb, s);
     }
     const int per = (L + ng - 1) / ng;
-    // all scratch is sized for the whole pass before any work is queued
-    int rc = reserve_coef(ctx, n_seq * per * ctx->Hkv, s);
-    if (rc) return rc;
-    const int64_t krows = select_key_scratch_rows(b, L * ctx->Hkv, ctx->G);
-    if (krows > 0) {
-        rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes, (size_t)krows * 4, s);
-        if (rc) return rc;
-    }
-    hipError_t e = hipEventRecord(ctx->ev_fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_fork, 0);
-    if (e != hipSuccess) return hip_fail(ctx, e);
+    hipError_t e = hipSuccess;
     for (int g = 0, l0 = 0; l0 < L; ++g, l0 += per) {
         const int lg = (L - l0) < per ? (L - l0) : per;
         const CacheView sv = sub_view(cv, l0, lg);
-        const Batch sb = sub_batch(b, l0, ctx->Hkv, ctx->G);
+        const Batch sb = sub_batch(b, l0, L, ctx->Hkv, ctx->G);
         const int units = n_seq * lg * ctx->Hkv;
-        rc = run_score(ctx, sv, sb, units, ctx->raw, s, l0);
-        if (rc) return rc;
-        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, s, lg);
+        rc = run_score_only(ctx, sv, sb, units, ctx->raw, ctx->part, s);
         if (rc) return rc;
         e = hipEventRecord(ctx->ev_group[g], s);
         if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_group[g], 0);
         if (e != hipSuccess) return hip_fail(ctx, e);
-        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->aux);
+        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, true, ctx->aux, lg);
+        if (rc) return rc;
+        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->pb, ctx->aux);
         if (rc) return rc;
     }
     e = hipEventRecord(ctx->ev_join, ctx->aux);
@@ -294,6 +367,7 @@ const char* tria_strerror(int code) {
         case TRIA_E_UNSUPPORTED: return "shape not supported by the gfx950 kernels";
         case TRIA_E_HIP: return "HIP runtime error";
         case TRIA_E_NOMEM: return "out of memory";
+        case TRIA_E_DEVICE: return "a compaction workgroup gave up a bounded wait";
         default: return "unknown error";
     }
 }
@@ -314,12 +388,12 @@ int64_t tria_kept_count(int64_t n_tokens, int64_t budget, int64_t sink, int64_t 
 
 void tria_free(tria_ctx* ctx) {
     if (!ctx) return;
-    void* bufs[] = {ctx->q_re, ctx->q_im, ctx->w,   ctx->omega, ctx->m_re,
-                    ctx->m_im, ctx->coef, ctx->raw, ctx->keep,  ctx->keys};
+    void* bufs[] = {ctx->q_re, ctx->q_im, ctx->w,    ctx->omega, ctx->m_re,      ctx->m_im,
+                    ctx->coef, ctx->raw,  ctx->keep, ctx->keys,  ctx->part,      ctx->pb,
+                    ctx->cst.flags,       ctx->cst.err,          ctx->cst.ticket};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
-    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     for (hipEvent_t ev : ctx->ev_group)
         if (ev) (void)hipEventDestroy(ev);
@@ -395,9 +469,13 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
         if (e == hipSuccess) e = hipMemcpy(*ddst[i], host + i * F, F * sizeof(double), hipMemcpyHostToDevice);
     }
     free(host);
+    // error word of the compaction's bounded waits, and its task ticket
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.err), sizeof(int));
+    if (e == hipSuccess) e = hipMemset(ctx->cst.err, 0, sizeof(int));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, sizeof(uint32_t));
     // second stream (default priority) and events for overlapped passes
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
     for (int i = 0; i < kMaxGroups && e == hipSuccess; ++i)
         e = hipEventCreateWithFlags(&ctx->ev_group[i], hipEventDisableTiming);
@@ -418,7 +496,7 @@ int tria_score(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, float* 
     if (n_tokens == 0) return TRIA_OK;
     const CacheView cv = view_of(ctx, cache);
     const Batch b = one_seq(n_tokens, protect(n_tokens, n_tokens, 0, 0));
-    return run_score(ctx, cv, b, ctx->L * ctx->Hkv, raw_scores, stream);
+    return run_score(ctx, cv, b, ctx->L * ctx->Hkv, raw_scores, nullptr, stream);
 }
 
 int64_t tria_select(tria_ctx* ctx, const float* raw_scores, int64_t n_tokens, int64_t budget,
@@ -430,7 +508,7 @@ int64_t tria_select(tria_ctx* ctx, const float* raw_scores, int64_t n_tokens, in
     if (n_tokens == 0) return 0;
     const Protect p = protect(n_tokens, budget, sink, window);
     const Batch b = one_seq(n_tokens, p);
-    int rc = run_select(ctx, b, raw_scores, keep_idx, agg_out, stream);
+    int rc = run_select(ctx, b, raw_scores, keep_idx, agg_out, false, stream);
     return rc ? rc : p.kept;
 }
 
@@ -445,7 +523,12 @@ int tria_compact(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens,
     p.kept = kept;
     p.s_end = p.w_start = 0;
     const Batch b = one_seq(n_tokens, p);
-    return compact_timed(ctx, view_of(ctx, cache), b, ctx->L * ctx->Hkv, keep_idx, stream);
+    const int units = ctx->L * ctx->Hkv;
+    rc = reserve_pb(ctx, b, units, stream);
+    if (rc) return rc;
+    rc = reserve_flags(ctx, b, units, stream);
+    if (rc) return rc;
+    return compact_timed(ctx, view_of(ctx, cache), b, units, keep_idx, nullptr, stream);
 }
 
 int64_t tria_evict(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, int64_t budget,
@@ -481,7 +564,7 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
     Batch b;
     memset(&b, 0, sizeof(b));
     b.n_seq = n_seq;
-    int64_t raw_off = 0, keep_off = 0;
+    int64_t raw_off = 0, keep_off = 0, part_off = 0, pb_off = 0;
     bool any = false;
     for (int i = 0; i < n_seq; ++i) {
         const int64_t n = n_tokens[i];
@@ -497,7 +580,11 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
         sd.w_start = p.w_start;
         sd.raw_off = raw_off;
         sd.keep_off = keep_off;
+        sd.part_off = part_off;
+        sd.pb_off = pb_off;
         raw_off += (int64_t)units_per_seq * sd.n * ctx->G;
+        part_off += (int64_t)units_per_seq * part_tiles(sd.n);
+        pb_off += (int64_t)units_per_seq * chunk_bounds(sd.kept);
         keep_off += (int64_t)units_per_seq * sd.kept;
         kept_out[i] = p.kept;
         any |= sd.n > 0;
@@ -522,6 +609,22 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
     cv.kb = ctx->kb;
     cv.vb = ctx->vb;
     return run_pass(ctx, cv, b, stream);
+}
+
+int tria_set_pipeline(tria_ctx* ctx, int32_t layers_per_group) {
+    if (!ctx || layers_per_group < 0) return TRIA_E_INVAL;
+    ctx->layers_per_group = layers_per_group;
+    return TRIA_OK;
+}
+
+int tria_device_status(tria_ctx* ctx) {
+    if (!ctx) return TRIA_E_INVAL;
+    hipError_t e = hipDeviceSynchronize();
+    int flag = 0;
+    if (e == hipSuccess) e = hipMemcpy(&flag, ctx->cst.err, sizeof(int), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && flag) e = hipMemset(ctx->cst.err, 0, sizeof(int));
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return flag ? TRIA_E_DEVICE : TRIA_OK;
 }
 
 int tria_timing_enable(tria_ctx* ctx, int32_t enable) {

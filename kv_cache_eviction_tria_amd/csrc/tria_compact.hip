@@ -8,367 +8,331 @@
 //
 //   row d <- row keep_idx[d], d < kept, for K, V and positions.
 //
-// In place and race-free without a second buffer: keep_idx[d] >= d, so a row
-// is only ever overwritten by a destination at or below it.  Each workgroup
-// owns one independent byte column ("slice") of one array of one unit and
-// walks the destination rows in increasing chunks.  A chunk's stores are
-// issued only after a workgroup barrier that every thread reaches after its
-// loads of that chunk's sources have returned.  Every source of a later chunk
-// lies at or above that chunk's first destination, i.e. above everything an
-// earlier chunk writes, so the loads of the next chunk are issued before the
-// current chunk's stores (a one-chunk read-ahead, indices two chunks ahead):
-// each chunk costs one overlapped memory round trip instead of two serial
-// ones.  Rows whose source is the row itself are skipped, so a leading kept
-// run costs nothing but its index read.  Slices of <= 128 bytes spread one
-// unit over several workgroups; each thread of a slice moves one fixed column.
+// In place without a second buffer.  keep_idx is ascending with
+// keep_idx[d] >= d, so a row is overwritten only by a destination at or below
+// it, and the only hazard is a write landing on a row that a smaller
+// destination still has to read.
+//
+// The destinations of a unit are cut into chunks of 64 rows; a task moves
+// one chunk of one unit (K, V and positions).  A task
+//   1. loads the source rows of its chunk into registers,
+//   2. once they have arrived, publishes that (flag[unit][chunk] = epoch),
+//   3. waits until every earlier chunk that reads a row of its own
+//      destination range has published, and
+//   4. stores.
+// The chunks that read rows [64c, 64c+64) are exactly those holding the ranks
+// P(64c) .. P(64c+64)-1, P(x) = number of kept rows below x (the selector
+// writes P at chunk boundaries); a later chunk never reads them, because its
+// sources lie above its own destinations.  So every read sees the original
+// row and no task waits on anything but loads that are already in flight.
+//
+// Tasks are handed out in increasing order from a ticket counter (a few at a
+// time), task = chunk * units + unit, so the chunks of a unit are taken in
+// order and a task only waits on smaller tasks, all of which are held by
+// workgroups that are already running.  The smallest unfinished task never
+// waits, whatever subset of the grid is resident (other kernels may share
+// the GPU).  Each wait is also bounded: a workgroup that gives up records an
+// error (see tria_device_status) and stores anyway.  The counter is reset by
+// the kernel that runs before the compaction on the same stream (the
+// selector, or the prefix-count kernel for caller-provided indices).
 #include "tria_internal.h"
 
 namespace tria {
 
 namespace {
 
-#ifndef TRIA_COMPACT_THREADS
-#define TRIA_COMPACT_THREADS 256
-#endif
-constexpr int kCompactThreads = TRIA_COMPACT_THREADS;
-constexpr int kMaxSlices = 16;
-// Kept indices staged in LDS up to this size (keeps >= 2 workgroups per CU).
-constexpr size_t kMaxIdxLds = 64 * 1024;
+constexpr int kMaxFlowThreads = 1024;
+constexpr int kTicketTasks = 4;  // tasks taken per ticket
+constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus a short sleep)
+// Pieces per thread and array; the launch uses 256, 512 or 1024 threads so
+// that a chunk of either array needs at most this many.
+constexpr int kItems = 8;
 
-struct Slice {
-    int32_t arr;    // 0 = K, 1 = V, 2 = positions
-    int32_t off;    // byte offset of the slice in the row
-    int32_t cw;     // bytes moved per item: 2, 4, 8 or 16
-    int32_t lg;     // log2 of the items per row (a power of two, <= 64)
-};
-
-struct SliceSet {
-    int32_t n;
-    Slice s[kMaxSlices];
-};
-
-template <int CW>
-struct Chunk;
+template <int PW>
+struct Piece;
 template <>
-struct Chunk<2> { using T = uint16_t; };
+struct Piece<16> { using T = u32x4; };
 template <>
-struct Chunk<4> { using T = uint32_t; };
+struct Piece<8> { using T = u32x2; };
 template <>
-struct Chunk<8> { using T = u32x2; };
+struct Piece<4> { using T = uint32_t; };
 template <>
-struct Chunk<16> { using T = u32x4; };
+struct Piece<2> { using T = uint16_t; };
 
 template <typename T>
-__device__ __forceinline__ void wait_loaded(const T& x) {
+__device__ __forceinline__ void hold(const T& x) {
     // A use of the register: the compiler waits for the load that fills it.
     asm volatile("" ::"v"(x));
 }
 
-// Byte offset of logical row r of the unit from the unit's base pointer.
-// Contiguous: rows are consecutive.  Paged: via the block table (64-bit).
-template <bool PAGED>
-struct RowAddr {
-    uint8_t* base;
-    int rb;
-    const int32_t* bt;  // paged: this sequence's block-table row
-    int64_t blk_stride; // paged: bytes per physical block of this layer
-    __device__ __forceinline__ uint8_t* operator()(int32_t r) const {
-        if constexpr (!PAGED) {
-            return base + (uint32_t)r * (uint32_t)rb;
-        } else {
-            const int64_t blk = bt[r >> 4];
-            return base + blk * blk_stride + (uint32_t)(r & 15) * (uint32_t)rb;
+// Item k of this thread is piece i = t + blockDim k of the chunk in row-major
+// order: row i / ppr, byte (i % ppr) * PW.  Rows and offsets advance by a
+// fixed step per item, so no division per item.
+struct ItemWalk {
+    int r, off, dr, doff, ppr_bytes;
+    __device__ __forceinline__ ItemWalk(int ppr, int pw) {
+        const int i = (int)threadIdx.x, nt = (int)blockDim.x;
+        r = i / ppr;
+        off = (i - r * ppr) * pw;
+        dr = nt / ppr;
+        doff = (nt - dr * ppr) * pw;
+        ppr_bytes = ppr * pw;
+    }
+    __device__ __forceinline__ void next() {
+        r += dr;
+        off += doff;
+        if (off >= ppr_bytes) {
+            off -= ppr_bytes;
+            ++r;
         }
     }
 };
 
-template <int CW, int IPT, bool PAGED, typename IdxT>
-__device__ __forceinline__ void compact_slice(const RowAddr<PAGED>& ra, int off, int lg,
-                                              IdxT idx, int32_t kept, int32_t n) {
-    using T = typename Chunk<CW>::T;
-    const int col = threadIdx.x & ((1 << lg) - 1);
-    const int rr0 = threadIdx.x >> lg;
-    const int rstep = kCompactThreads >> lg;  // rows between a thread's items
-    const int rpc = IPT * rstep;              // rows per chunk
-    const int32_t nchunks = (kept + rpc - 1) / rpc;
-    const int coff = off + col * CW;
+// One array's part of a task: the pieces of the chunk's rows, dealt to the
+// threads in row-major order (consecutive threads move consecutive pieces).
+template <int PW>
+struct ArrayMove {
+    using T = typename Piece<PW>::T;
+    T buf[kItems];
 
-    auto load_idx = [&](int32_t c, int32_t (&src)[IPT]) {
+    __device__ __forceinline__ void load(const uint8_t* base, int rb, const int64_t* src) {
+        ItemWalk w(rb / PW, PW);
 #pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            const int32_t d = c * rpc + rr0 + i * rstep;
-            src[i] = d < kept ? idx[d] : -1;
-        }
-    };
-    auto moves = [&](int32_t c, int i, int32_t sr) {
-        const int32_t d = c * rpc + rr0 + i * rstep;
-        return sr > d && sr < n;
-    };
-    auto load_data = [&](int32_t c, const int32_t (&src)[IPT], T (&buf)[IPT]) {
-#pragma unroll
-        for (int i = 0; i < IPT; ++i)
-            if (moves(c, i, src[i]))
-                buf[i] = __builtin_nontemporal_load(reinterpret_cast<const T*>(ra(src[i]) + coff));
-    };
-    auto store_data = [&](int32_t c, const int32_t (&src)[IPT], const T (&buf)[IPT]) {
-#pragma unroll
-        for (int i = 0; i < IPT; ++i)
-            if (moves(c, i, src[i])) {
-                const int32_t d = c * rpc + rr0 + i * rstep;
-                __builtin_nontemporal_store(buf[i], reinterpret_cast<T*>(ra(d) + coff));
+        for (int k = 0; k < kItems; ++k) {
+            if (w.r < kChunkRows) {
+                const int64_t s = src[w.r];
+                if (s >= 0) buf[k] = *reinterpret_cast<const T*>(base + s * rb + w.off);
             }
-    };
-    auto finish_loads = [&](T (&buf)[IPT]) {
+            w.next();
+        }
+    }
+    __device__ __forceinline__ void wait() {
 #pragma unroll
-        for (int i = 0; i < IPT; ++i) wait_loaded(buf[i]);
-        __syncthreads();  // every source of this chunk has been read
-    };
+        for (int k = 0; k < kItems; ++k) hold(buf[k]);
+    }
+    __device__ __forceinline__ void store(uint8_t* base, int rb, const int64_t* src,
+                                          const int64_t* dst) const {
+        ItemWalk w(rb / PW, PW);
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            if (w.r < kChunkRows && src[w.r] >= 0)
+                *reinterpret_cast<T*>(base + dst[w.r] * rb + w.off) = buf[k];
+            w.next();
+        }
+    }
+};
 
-    int32_t sA[IPT], sB[IPT];
-    T bA[IPT], bB[IPT];
-    load_idx(0, sA);
-    load_data(0, sA, bA);
-    load_idx(1, sB);
-    for (int32_t c = 0; c < nchunks; c += 2) {
-        load_data(c + 1, sB, bB);  // read-ahead: sources of c+1 lie above chunk c's rows
-        finish_loads(bA);
-        store_data(c, sA, bA);
-        load_idx(c + 2, sA);
-        if (c + 1 >= nchunks) break;
-        load_data(c + 2, sA, bA);
-        finish_loads(bB);
-        store_data(c + 1, sB, bB);
-        load_idx(c + 3, sB);
+template <int PK, int PV>
+__global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
+    CacheView cv, Batch b, const int32_t* __restrict__ keep, const int32_t* __restrict__ pb,
+    uint32_t* flags, int max_chunks, uint32_t epoch, int n_units, uint32_t* ticket, int* err) {
+    __shared__ int64_t src_row[kChunkRows];  // physical source row, -1 if the row stays
+    __shared__ int64_t dst_row[kChunkRows];
+    __shared__ uint32_t first_sh;
+    const int t = threadIdx.x;
+    const uint32_t n_tasks = (uint32_t)max_chunks * (uint32_t)n_units;
+    while (true) {
+        if (t == 0) first_sh = atomicAdd(ticket, (uint32_t)kTicketTasks);
+        __syncthreads();
+        const uint32_t first = first_sh;
+        __syncthreads();
+        if (first >= n_tasks) break;
+        const uint32_t last = first + kTicketTasks < n_tasks ? first + kTicketTasks : n_tasks;
+        for (uint32_t task = first; task < last; ++task) {
+            const int c = (int)(task / n_units);
+            const int u = (int)(task - (int64_t)c * n_units);
+            const UnitId id = unit_id(cv, u);
+            const SeqDesc& sd = b.seq[id.seq];
+            const int kept = (int)sd.kept, n = (int)sd.n;
+            if (kept <= 0 || kept >= n) continue;  // nothing evicted: no row moves
+            if (c >= (int)chunk_count(kept)) continue;
+            const int uu = id.l * cv.Hkv + id.g;
+            const int32_t* idx = keep + sd.keep_off + (int64_t)uu * kept;
+            uint32_t* F = flags + (int64_t)u * max_chunks;
+            const int d0 = c * kChunkRows;
+
+            // 1. the chunk's sources, then its loads
+            if (t < kChunkRows) {
+                int64_t sr = -1, dr = -1;
+                const int d = d0 + t;
+                if (d < kept) {
+                    const int s = idx[d];
+                    if (s > d && s < n) {
+                        sr = row_index(cv, id, s);
+                        dr = row_index(cv, id, d);
+                    }
+                }
+                src_row[t] = sr;
+                dst_row[t] = dr;
+            }
+            __syncthreads();
+            ArrayMove<PK> mk;
+            ArrayMove<PV> mv;
+            uint32_t pos = 0;
+            mk.load(cv.k, cv.kb, src_row);
+            mv.load(cv.v, cv.vb, src_row);
+            const int64_t ps = t < kChunkRows ? src_row[t] : -1;
+            if (ps >= 0) pos = reinterpret_cast<const uint32_t*>(cv.pos)[ps];
+            mk.wait();
+            mv.wait();
+            hold(pos);
+            __syncthreads();  // every source of this chunk has been read
+
+            // 2. publish, 3. wait for the earlier chunks that read this chunk's rows
+            if (t == 0) (void)__hip_atomic_exchange(&F[c], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t < 64) {
+                const int32_t* P = pb + sd.pb_off + (int64_t)uu * chunk_bounds(kept);
+                const int p0 = P[c], p1 = P[c + 1];
+                const int lo = p0 / kChunkRows;
+                const int hi = min(c - 1, (p1 - 1) / kChunkRows);
+                if (p1 > p0) {
+                    for (int base = lo; base <= hi; base += 64) {
+                        const int cc = base + t;
+                        int spins = 0;
+                        while (true) {
+                            const bool ready =
+                                cc > hi ||
+                                __hip_atomic_load(&F[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                    epoch;
+                            if (__ballot(!ready) == 0) break;
+                            if (++spins > kSpinLimit) {
+                                if (t == 0) atomicOr(err, 1);
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(2);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+
+            // 4. stores
+            mk.store(cv.k, cv.kb, src_row, dst_row);
+            mv.store(cv.v, cv.vb, src_row, dst_row);
+            if (ps >= 0) reinterpret_cast<uint32_t*>(cv.pos)[dst_row[t]] = pos;
+            __syncthreads();  // the row tables are rewritten by the next task
+        }
     }
 }
 
-// Buffer-resource loads/stores: an offset at or past the resource size is
-// dropped by the hardware (loads return 0), so items that do not move get an
-// out-of-range offset instead of a branch.  Straight-line code lets the
-// compiler wait for exactly the loads a chunk needs (not for the read-ahead).
-constexpr uint32_t kOOB = 0x80000000u;
-
-template <int CW>
-struct BufIO;
-template <>
-struct BufIO<16> {
-    using T = u32x4;
-    static __device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-        return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
-    }
-    static __device__ __forceinline__ void st(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, 0);
-    }
-};
-template <>
-struct BufIO<8> {
-    using T = u32x2;
-    static __device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-        return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
-    }
-    static __device__ __forceinline__ void st(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) {
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, 0);
-    }
-};
-template <>
-struct BufIO<4> {
-    using T = uint32_t;
-    static __device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
-    }
-    static __device__ __forceinline__ void st(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, 0);
-    }
-};
-template <>
-struct BufIO<2> {
-    using T = unsigned short;
-    static __device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t o) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
-    }
-    static __device__ __forceinline__ void st(T v, __amdgpu_buffer_rsrc_t r, uint32_t o) {
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, o, 0, 0);
-    }
-};
-
-// Contiguous cache: the unit's rows are one buffer of cap * rb bytes.
-template <int CW, int IPT, typename IdxT>
-__device__ __forceinline__ void compact_slice_buf(__amdgpu_buffer_rsrc_t rs, int rb, int off,
-                                                  int lg, IdxT idx, int32_t kept, int32_t n) {
-    using IO = BufIO<CW>;
-    using T = typename IO::T;
-    const int col = threadIdx.x & ((1 << lg) - 1);
-    const int rr0 = threadIdx.x >> lg;
-    const int rstep = kCompactThreads >> lg;
-    const int rpc = IPT * rstep;
-    const int32_t nchunks = (kept + rpc - 1) / rpc;
-    const uint32_t coff = (uint32_t)(off + col * CW);
-
-    // byte offsets of this thread's sources (OOB if the row does not move)
-    auto src_offs = [&](int32_t c, uint32_t (&so)[IPT]) {
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            const int32_t d = c * rpc + rr0 + i * rstep;
-            const int32_t v = idx[d < kept ? d : kept - 1];  // branch-free read
-            const int32_t sr = d < kept ? v : -1;
-            so[i] = (sr > d && sr < n) ? (uint32_t)sr * (uint32_t)rb + coff : kOOB;
-        }
-    };
-    // A buffer's data and offset registers stay live from its stores until it
-    // is reloaded (the empty asm uses below): otherwise the register allocator
-    // reuses them right after the stores for temporaries, and protecting the
-    // in-flight store data makes the compiler wait for everything issued
-    // before those stores -- including the read-ahead loads.
-    auto load = [&](int32_t c, uint32_t (&so)[IPT], T (&buf)[IPT]) {
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            asm volatile("" ::"v"(buf[i]));
-            asm volatile("" ::"v"(so[i]));
-        }
-        src_offs(c, so);
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) buf[i] = IO::ld(rs, so[i]);
-    };
-    auto drain_store = [&](int32_t c, uint32_t (&so)[IPT], T (&buf)[IPT]) {
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) wait_loaded(buf[i]);
-        __syncthreads();  // every source of chunk c has been read
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            const int32_t d = c * rpc + rr0 + i * rstep;
-            so[i] = so[i] == kOOB ? kOOB : (uint32_t)d * (uint32_t)rb + coff;
-            IO::st(buf[i], rs, so[i]);
-        }
-    };
-
-    // Four buffers, two chunks of read-ahead: chunk c+2 is loaded into the
-    // buffer whose stores (chunk c-2) were issued two steps earlier.
-    uint32_t o0[IPT] = {}, o1[IPT] = {}, o2[IPT] = {}, o3[IPT] = {};
-    T b0[IPT] = {}, b1[IPT] = {}, b2[IPT] = {}, b3[IPT] = {};
-    load(0, o0, b0);
-    load(1, o1, b1);
-    for (int32_t c = 0; c < nchunks; c += 4) {
-        load(c + 2, o2, b2);
-        drain_store(c, o0, b0);
-        if (c + 1 >= nchunks) break;
-        load(c + 3, o3, b3);
-        drain_store(c + 1, o1, b1);
-        if (c + 2 >= nchunks) break;
-        load(c + 4, o0, b0);
-        drain_store(c + 2, o2, b2);
-        if (c + 3 >= nchunks) break;
-        load(c + 5, o1, b1);
-        drain_store(c + 3, o3, b3);
-    }
-}
-
-template <bool PAGED, bool IDX_LDS>
-__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CacheView cv, Batch b,
-                                                                   SliceSet ss,
-                                                                   const int32_t* __restrict__ keep,
-                                                                   int n_units) {
-    extern __shared__ int32_t idx_sh[];
-    // Workgroups are dealt to the 8 XCDs round-robin by id; give all slices of a
-    // unit ids that are equal mod 8 and adjacent, so they share one L2 and run
-    // together (the halves of a row are then fetched from HBM once).
-    const int w = blockIdx.x;
-    const int q = w >> 3;
-    const int u = (q / ss.n) * 8 + (w & 7);
-    if (u >= n_units) return;
-    const Slice sl = ss.s[q % ss.n];
+// P(64 e) for caller-provided kept indices: lower bound of 64 e in the
+// ascending indices, one thread per (unit, boundary).
+__global__ __launch_bounds__(256) void chunk_bounds_kernel(CacheView cv, Batch b,
+                                                           const int32_t* __restrict__ keep,
+                                                           int32_t* __restrict__ pb, int n_units,
+                                                           int max_bounds, uint32_t* ticket) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i == 0) *ticket = 0;  // for the compaction that follows on this stream
+    if (i >= (int64_t)n_units * max_bounds) return;
+    const int u = (int)(i / max_bounds), e = (int)(i - (int64_t)u * max_bounds);
     const UnitId id = unit_id(cv, u);
     const SeqDesc& sd = b.seq[id.seq];
-    const int32_t kept = (int32_t)sd.kept, n = (int32_t)sd.n;
-    if (kept <= 0 || kept >= n) return;  // nothing evicted: no row moves
-    const int32_t* idx = keep + sd.keep_off + ((int64_t)id.l * cv.Hkv + id.g) * kept;
-    uint8_t* arr = sl.arr == 0 ? cv.k : (sl.arr == 1 ? cv.v : reinterpret_cast<uint8_t*>(cv.pos));
-    RowAddr<PAGED> ra;
-    ra.rb = sl.arr == 0 ? cv.kb : (sl.arr == 1 ? cv.vb : 4);
-    if constexpr (!PAGED) {
-        ra.base = arr + ((int64_t)id.l * cv.Hkv + id.g) * cv.cap * ra.rb;
-        ra.bt = nullptr;
-        ra.blk_stride = 0;
-    } else {
-        ra.base = arr + ((int64_t)id.l * cv.n_blocks * cv.Hkv + id.g) * kBlockRows * ra.rb;
-        ra.bt = cv.bt + (int64_t)id.seq * cv.max_blocks;
-        ra.blk_stride = (int64_t)cv.Hkv * kBlockRows * ra.rb;
+    const int64_t kept = sd.kept;
+    if (e >= chunk_bounds(kept)) return;
+    const int uu = id.l * cv.Hkv + id.g;
+    const int32_t* idx = keep + sd.keep_off + (int64_t)uu * kept;
+    const int64_t x = (int64_t)e * kChunkRows;
+    int64_t lo = 0, hi = kept;  // first position with idx >= x
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (idx[mid] < x) lo = mid + 1;
+        else hi = mid;
     }
-    auto run = [&](auto ix) {
-        if constexpr (!PAGED) {
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                ra.base, (short)0, (int)(cv.cap * ra.rb), 0x00020000);
-            switch (sl.cw) {
-                case 16: compact_slice_buf<16, 4>(rs, ra.rb, sl.off, sl.lg, ix, kept, n); break;
-                case 8: compact_slice_buf<8, 8>(rs, ra.rb, sl.off, sl.lg, ix, kept, n); break;
-                case 4: compact_slice_buf<4, 8>(rs, ra.rb, sl.off, sl.lg, ix, kept, n); break;
-                default: compact_slice_buf<2, 8>(rs, ra.rb, sl.off, sl.lg, ix, kept, n); break;
-            }
-            return;
-        }
-        switch (sl.cw) {
-            case 16: compact_slice<16, 8, PAGED>(ra, sl.off, sl.lg, ix, kept, n); break;
-            case 8: compact_slice<8, 8, PAGED>(ra, sl.off, sl.lg, ix, kept, n); break;
-            case 4: compact_slice<4, 16, PAGED>(ra, sl.off, sl.lg, ix, kept, n); break;
-            default: compact_slice<2, 16, PAGED>(ra, sl.off, sl.lg, ix, kept, n); break;
-        }
-    };
-    if constexpr (IDX_LDS) {
-        // Stage the unit's kept indices once (coalesced), so that no chunk waits
-        // on a dependent index load from memory.
-        for (int32_t i = threadIdx.x; i < kept; i += kCompactThreads) idx_sh[i] = idx[i];
-        __syncthreads();
-        run(static_cast<const int32_t*>(idx_sh));
-    } else {
-        run(idx);
+    pb[sd.pb_off + (int64_t)uu * chunk_bounds(kept) + e] = (int32_t)lo;
+}
+
+int piece_width(int rb) {
+    int pw = 16;
+    while (pw > 2 && rb % pw != 0) pw >>= 1;
+    return pw;
+}
+
+using FlowKernel = void (*)(CacheView, Batch, const int32_t*, const int32_t*, uint32_t*, int,
+                            uint32_t, int, uint32_t*, int*);
+
+template <int PK>
+FlowKernel flow_for_v(int pv) {
+    switch (pv) {
+        case 16: return compact_flow_kernel<PK, 16>;
+        case 8: return compact_flow_kernel<PK, 8>;
+        case 4: return compact_flow_kernel<PK, 4>;
+        default: return compact_flow_kernel<PK, 2>;
     }
 }
 
-// Split a row of rb bytes into slices of a power-of-two number of items of the
-// widest aligned chunk, at most 128 bytes per slice.
-#ifndef TRIA_SLICE_BYTES
-#define TRIA_SLICE_BYTES 128
-#endif
-void add_slices(SliceSet& ss, int arr, int rb) {
-    int cw = 16;
-    while (cw > 2 && (rb % cw) != 0) cw >>= 1;
-    int items = rb / cw, off = 0;
-    const int max_items = TRIA_SLICE_BYTES / cw > 0 ? TRIA_SLICE_BYTES / cw : 1;
-    while (items > 0 && ss.n < kMaxSlices) {
-        int take = max_items;
-        while (take > items) take >>= 1;
-        int lg = 0;
-        while ((1 << lg) < take) ++lg;
-        ss.s[ss.n++] = Slice{arr, off, cw, lg};
-        off += take * cw;
-        items -= take;
+FlowKernel flow_kernel(int pk, int pv) {
+    switch (pk) {
+        case 16: return flow_for_v<16>(pv);
+        case 8: return flow_for_v<8>(pv);
+        case 4: return flow_for_v<4>(pv);
+        default: return flow_for_v<2>(pv);
     }
+}
+
+// Workgroups of a kernel that are resident at once on the whole device.
+int resident_groups(FlowKernel k, int threads) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k),
+                                                     threads, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+int64_t max_chunks_of(const Batch& b) {
+    int64_t m = 0;
+    for (int i = 0; i < b.n_seq; ++i) {
+        const int64_t c = chunk_count(b.seq[i].kept);
+        m = c > m ? c : m;
+    }
+    return m;
 }
 
 }  // namespace
 
-hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units,
-                          const int32_t* keep, hipStream_t s) {
+int64_t compact_flag_words(const Batch& b, int n_units) {
+    return max_chunks_of(b) * n_units;
+}
+
+hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
+                          const int32_t* pb, int32_t* pb_scratch, CompactState& st,
+                          hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    SliceSet ss;
-    ss.n = 0;
-    add_slices(ss, 0, cv.kb);
-    add_slices(ss, 1, cv.vb);
-    add_slices(ss, 2, 4);
-    int64_t max_kept = 0;
-    for (int i = 0; i < b.n_seq; ++i) max_kept = b.seq[i].kept > max_kept ? b.seq[i].kept : max_kept;
-    const size_t lds = (size_t)max_kept * sizeof(int32_t);
-    const dim3 grid(ss.n * ((n_units + 7) / 8) * 8), blk(kCompactThreads);
-    if (lds <= kMaxIdxLds) {
-        if (cv.bt)
-            hipLaunchKernelGGL((compact_kernel<true, true>), grid, blk, lds, s, cv, b, ss, keep, n_units);
-        else
-            hipLaunchKernelGGL((compact_kernel<false, true>), grid, blk, lds, s, cv, b, ss, keep, n_units);
-    } else {
-        if (cv.bt)
-            hipLaunchKernelGGL((compact_kernel<true, false>), grid, blk, 0, s, cv, b, ss, keep, n_units);
-        else
-            hipLaunchKernelGGL((compact_kernel<false, false>), grid, blk, 0, s, cv, b, ss, keep, n_units);
+    const int64_t max_chunks = max_chunks_of(b);
+    if (max_chunks <= 0) return hipSuccess;
+    if (max_chunks * n_units > st.flag_words) return hipErrorInvalidValue;
+    if (!pb) {
+        int64_t max_bounds = 0;
+        for (int i = 0; i < b.n_seq; ++i) {
+            const int64_t e = chunk_bounds(b.seq[i].kept);
+            max_bounds = e > max_bounds ? e : max_bounds;
+        }
+        const int64_t threads = max_bounds * n_units;
+        hipLaunchKernelGGL(chunk_bounds_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                           0, s, cv, b, keep, pb_scratch, n_units, (int)max_bounds, st.ticket);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        pb = pb_scratch;
     }
+    const int pk = piece_width(cv.kb), pv = piece_width(cv.vb);
+    const FlowKernel k = flow_kernel(pk, pv);
+    // threads such that each array's chunk is at most kItems pieces per thread
+    const int64_t pieces = (int64_t)kChunkRows * (cv.kb / pk > cv.vb / pv ? cv.kb / pk : cv.vb / pv);
+    int threads = 256;
+    while ((int64_t)threads * kItems < pieces) threads *= 2;
+    if (threads > kMaxFlowThreads) return hipErrorInvalidValue;
+    const int64_t tasks = max_chunks * n_units;
+    if (tasks >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    // as many workgroups as fit at once; residency is not required
+    int grid = resident_groups(k, threads);
+    if (grid <= 0) return hipErrorInvalidValue;
+    const int64_t need = (tasks + kTicketTasks - 1) / kTicketTasks;
+    if (need < grid) grid = (int)need;
+    st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value
+    hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, s, cv, b, keep, pb, st.flags,
+                       (int)max_chunks, st.epoch, n_units, st.ticket, st.err);
     return hipGetLastError();
 }
 

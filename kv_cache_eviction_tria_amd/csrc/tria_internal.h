@@ -23,11 +23,18 @@ struct SeqDesc {
     int64_t w_start;
     int64_t raw_off;   // float offset of the sequence's [L][Hkv][n][G] raw-score block
     int64_t keep_off;  // int offset of the sequence's [L][Hkv][kept] keep-index block
+    int64_t part_off;  // tile offset of the sequence's [L][Hkv][tiles(n)] moment partials
+    int64_t pb_off;    // int offset of the sequence's [L][Hkv][chunk_bounds(kept)] prefix counts
 };
 
 struct Batch {
     int32_t n_seq;
-    int32_t max_tiles;  // score tiles of the longest sequence
+    // Coefficient tables are laid out per unit of the whole model; a batch
+    // over layers [coef_l0, coef_l0 + L) of a coef_L-layer model finds unit
+    // (seq, l, g)'s table at ((seq * coef_L + coef_l0 + l) * Hkv + g).
+    // coef_L == 0: the batch covers the whole model.
+    int32_t coef_l0;
+    int32_t coef_L;
     SeqDesc seq[kMaxSeq];
 };
 
@@ -47,6 +54,105 @@ struct CacheView {
     int32_t vb;  // V row bytes
 };
 
+// Moment partials: the raw scores of a unit are summarised per tile of
+// kPartRows rows (one wavefront) and per query head as {finite count c, shift
+// a (the tile's first finite score), sum of d = s - a, sum of d^2} in fp32
+// (exact for equal scores; d is small against the scores' common offset),
+// record ((part_off + unit*tiles + tile)*G + head).  The selector forms the
+// tile mean m = a + sum(d)/c and M2 = sum(d^2) - sum(d)^2/c, then merges the
+// tiles exactly in fp64:  N = sum c_t,  mu = sum c_t m_t / N,
+// M2 = sum (M2_t + c_t (m_t - mu)^2).
+constexpr int kPartRows = 64;
+struct PartRec {
+    float cnt, shift, sum, sumsq;
+};
+__host__ __device__ inline int64_t part_tiles(int64_t n) { return (n + kPartRows - 1) / kPartRows; }
+
+// The DPP move of v (old value 0 where the row mask excludes a row).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sums over the 64 lanes of a wavefront (fixed order), returned to every lane:
+// pairs and quads by quad permutes, rows of 8 and 16 by mirrors, then the row
+// broadcasts of lanes 15 and 31 leave the total in lane 63.
+template <typename T, T (*MOV)(T), T (*MOV2)(T), T (*MOV3)(T), T (*MOV4)(T), T (*MOV5)(T),
+          T (*MOV6)(T)>
+__device__ __forceinline__ T wave_sum_dpp(T v) {
+    v += MOV(v);
+    v += MOV2(v);
+    v += MOV3(v);
+    v += MOV4(v);
+    v += MOV5(v);
+    v += MOV6(v);
+    return v;  // total in lane 63
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = wave_sum_dpp<float, dpp_f32<0xB1, 0xf>, dpp_f32<0x4E, 0xf>, dpp_f32<0x141, 0xf>,
+                     dpp_f32<0x140, 0xf>, dpp_f32<0x142, 0xa>, dpp_f32<0x143, 0xc>>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = wave_sum_dpp<double, dpp_f64<0xB1, 0xf>, dpp_f64<0x4E, 0xf>, dpp_f64<0x141, 0xf>,
+                     dpp_f64<0x140, 0xf>, dpp_f64<0x142, 0xa>, dpp_f64<0x143, 0xc>>(v);
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Moment partial of one wavefront's rows for NH heads: lane i holds row i's
+// scores s[] (valid[] false for rows past the end and non-finite scores).
+// Lane 0 writes head j's record to out[j] for j < nh.
+template <int NH>
+__device__ __forceinline__ void wave_moments(const float (&s)[NH], const bool (&valid)[NH],
+                                             PartRec* out, int nh = NH) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+        const uint64_t m = __ballot(valid[j]);
+        const int first = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        const float a = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s[j]), first));
+        const float d = valid[j] ? s[j] - a : 0.0f;
+        const float sd = wave_sum_f32(d);
+        const float sq = wave_sum_f32(d * d);
+        if (lane == 0 && j < nh) out[j] = PartRec{(float)__popcll(m), m ? a : 0.0f, sd, sq};
+    }
+}
+
+// Mean and M2 of a tile record (fp64).
+__device__ __forceinline__ void part_stats(const PartRec& p, double* mean, double* m2) {
+    if (p.cnt > 0.0f) {
+        const double c = p.cnt, sd = p.sum;
+        *mean = (double)p.shift + sd / c;
+        const double v = (double)p.sumsq - sd * sd / c;
+        *m2 = v > 0.0 ? v : 0.0;
+    } else {
+        *mean = 0.0;
+        *m2 = 0.0;
+    }
+}
+
+// Compaction works in chunks of kChunkRows destination rows.  For every unit
+// the selector also writes P(64 e) for e < chunk_bounds(kept), where P(x) is
+// the number of kept rows below row x: the moves that read rows of chunk c are
+// exactly those with ranks P(64 c) .. P(64 c + 64) - 1.
+constexpr int kChunkRows = 64;
+__host__ __device__ inline int64_t chunk_count(int64_t kept) {
+    return (kept + kChunkRows - 1) / kChunkRows;
+}
+__host__ __device__ inline int64_t chunk_bounds(int64_t kept) { return chunk_count(kept) + 1; }
+
 struct UnitId {
     int seq, l, g;
 };
@@ -59,6 +165,11 @@ __device__ __forceinline__ UnitId unit_id(const CacheView& c, int u) {
     id.l = rem / c.Hkv;
     id.g = rem - id.l * c.Hkv;
     return id;
+}
+
+__device__ __forceinline__ int64_t coef_unit(const Batch& b, const CacheView& c, const UnitId& id) {
+    const int cl = b.coef_L ? b.coef_L : c.L;
+    return ((int64_t)id.seq * cl + b.coef_l0 + id.l) * c.Hkv + id.g;
 }
 
 // Index of logical row r of a unit in its row array (multiply by the row size).
@@ -122,11 +233,25 @@ hipError_t launch_prep(const CacheView& cv, const Batch& b, int n_units, int k_t
                        int hd, const float* q_re, const float* q_im, const float* w,
                        const double* omega, const double* m_re, const double* m_im,
                        int32_t* coef, hipStream_t s);
+// part == nullptr: no moment partials.
 hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_type, int G,
-                        int hd, const int32_t* coef, float* raw, hipStream_t s);
-hipError_t launch_select(const Batch& b, int n_units_per_seq, int G, const float* raw,
-                         int32_t* keep, float* agg, hipStream_t s);
-hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units,
-                          const int32_t* keep, hipStream_t s);
+                        int hd, const int32_t* coef, float* raw, PartRec* part, hipStream_t s);
+// Compaction state owned by a context: per-(unit, chunk) flags (zeroed once
+// when allocated, then stamped with a new epoch by every launch), the task
+// ticket counter and an error word set by a workgroup that gave up waiting.
+struct CompactState {
+    uint32_t* flags;
+    int64_t flag_words;
+    uint32_t epoch;
+    uint32_t* ticket;  // task counter, reset by the kernel before each compaction
+    int* err;
+};
+// pb: the selector's chunk prefix counts for these units, or nullptr to
+// derive them from keep (caller-provided kept indices).
+hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
+                          const int32_t* pb, int32_t* pb_scratch, CompactState& st,
+                          hipStream_t s);
+// Flags a launch over these units needs.
+int64_t compact_flag_words(const Batch& b, int n_units);
 
 }  // namespace tria

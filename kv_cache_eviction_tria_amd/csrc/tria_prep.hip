@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     const SeqDesc& sd = b.seq[id.seq];
     const CoefGeom cg = coef_geom(k_type, hd, G);
     const int F = cg.F;
-    int32_t* out = coef + (int64_t)u * cg.words;
+    int32_t* out = coef + coef_unit(b, cv, id) * cg.words;
     float* outf = reinterpret_cast<float*>(out);
     if (sd.n <= 0) return;
 
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     __syncthreads();
 
     const int Hq = cv.Hkv * G;
-    const int64_t stat0 = ((int64_t)id.l * Hq + (int64_t)id.g * G) * F;
+    const int64_t stat0 = ((int64_t)(b.coef_l0 + id.l) * Hq + (int64_t)id.g * G) * F;
 
     if (k_type == TRIA_KV_F16) {
         for (int i = threadIdx.x; i < F * G; i += kPrepThreads) {

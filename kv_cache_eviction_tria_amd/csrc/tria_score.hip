@@ -23,6 +23,10 @@
 // (v_dot4_i32_i8) straight from the stored bytes (the digit tables follow the
 // row's byte layout, scale bytes carry zero digits); the block scale d and sig
 // are applied once per block.  The |K_f| term dequantises q * d in fp32.
+//
+// Each wavefront also summarises its rows' scores per head (count, mean,
+// squared deviations; fp64) for the selector's z-normalisation, so the raw
+// scores are not read an extra time to form the head statistics.
 #include "tria_internal.h"
 
 namespace tria {
@@ -86,10 +90,24 @@ __device__ __forceinline__ void store_scores(float* dst, const float (&acc)[GT],
     }
 }
 
+// Moment partials of this wavefront's rows for heads j0 .. j0+GT-1.
+template <int GT>
+__device__ __forceinline__ void emit_moments(const float (&acc)[GT], bool in_range,
+                                             const SeqDesc& sd, const UnitId& id, int Hkv,
+                                             int64_t n, int G, int j0, PartRec* part) {
+    const int64_t wtile = (int64_t)blockIdx.x * (kScoreThreads / kPartRows) + (threadIdx.x >> 6);
+    if (wtile * kPartRows >= n) return;  // the unit has no row in this wavefront
+    bool valid[GT];
+#pragma unroll
+    for (int j = 0; j < GT; ++j) valid[j] = in_range && isfinite(acc[j]);
+    const int64_t tile = sd.part_off + ((int64_t)id.l * Hkv + id.g) * part_tiles(n) + wtile;
+    wave_moments<GT>(acc, valid, part + tile * G + j0);
+}
+
 template <int HD, int GT>
 __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
     CacheView cv, Batch b, int G, int j0, const float* __restrict__ coef, int coef_words,
-    float* __restrict__ raw) {
+    float* __restrict__ raw, PartRec* __restrict__ part) {
     constexpr int F = HD / 2;
     constexpr int NV = HD / 8;  // 16-byte chunks per row
     const int u = blockIdx.y;
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
     const int64_t n = b.seq[id.seq].n;
     const int64_t tile0 = (int64_t)blockIdx.x * kScoreThreads;
     if (tile0 >= n) return;
-    const float* __restrict__ C = coef + (int64_t)u * coef_words + j0 * F * 3;
+    const float* __restrict__ C = coef + coef_unit(b, cv, id) * coef_words + j0 * F * 3;
     float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + j0;
     const bool packed = (G == GT);
 
@@ -138,13 +156,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
             }
         }
         if (r_out < n) store_scores<GT>(rout + r_out * G, acc, packed);
+        if (part) emit_moments<GT>(acc, r_out < n, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
     }
 }
 
 template <int HD, int GT>
 __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     CacheView cv, Batch b, int G, int j0, const int32_t* __restrict__ coef, int coef_words,
-    float* __restrict__ raw) {
+    float* __restrict__ raw, PartRec* __restrict__ part) {
     constexpr int F = HD / 2;
     constexpr int NB = HD / 32;
     constexpr int RB = 34 * NB;         // row bytes
@@ -156,7 +175,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     const int64_t tile0 = (int64_t)blockIdx.x * kScoreThreads;
     if (tile0 >= n) return;
     const CoefGeom cg = coef_geom(TRIA_KV_Q8_0, HD, G);
-    const int32_t* __restrict__ T = coef + (int64_t)u * coef_words;
+    const int32_t* __restrict__ T = coef + coef_unit(b, cv, id) * coef_words;
     const int32_t* __restrict__ HI = T + cg.hi_off + j0 * W;
     const int32_t* __restrict__ LO = T + cg.lo_off + j0 * W;
     const float* __restrict__ SIG = reinterpret_cast<const float*>(T + cg.sig_off) + j0 * NB;
@@ -250,24 +269,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
             for (int j = 0; j < GT; ++j) acc[j] = fmaf(WT[z + f * GT + j], mag, acc[j]);
         }
         if (r_out < n) store_scores<GT>(rout + r_out * G, acc, packed);
+        if (part) emit_moments<GT>(acc, r_out < n, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
     }
 }
 
 template <int HD, int GT>
 void run_f16(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int G, int j0,
-             const int32_t* coef, int words, float* raw) {
+             const int32_t* coef, int words, float* raw, PartRec* part) {
     hipLaunchKernelGGL((score_f16_kernel<HD, GT>), grid, dim3(kScoreThreads), 0, s, cv, b, G, j0,
-                       reinterpret_cast<const float*>(coef), words, raw);
+                       reinterpret_cast<const float*>(coef), words, raw, part);
 }
 template <int HD, int GT>
 void run_q8(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int G, int j0,
-            const int32_t* coef, int words, float* raw) {
+            const int32_t* coef, int words, float* raw, PartRec* part) {
     hipLaunchKernelGGL((score_q8_kernel<HD, GT>), grid, dim3(kScoreThreads), 0, s, cv, b, G, j0,
-                       coef, words, raw);
+                       coef, words, raw, part);
 }
 
 using Runner = void (*)(dim3, hipStream_t, const CacheView&, const Batch&, int, int,
-                        const int32_t*, int, float*);
+                        const int32_t*, int, float*, PartRec*);
 
 template <int HD>
 Runner pick(int k_type, int gt) {
@@ -304,7 +324,8 @@ Runner pick_runner(int k_type, int hd, int gt) {
 }  // namespace
 
 hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_type, int G,
-                        int hd, const int32_t* coef, float* raw, hipStream_t s) {
+                        int hd, const int32_t* coef, float* raw, PartRec* part, hipStream_t s) {
+    static_assert(kPartRows == 64, "one moment partial per score wavefront");
     int64_t max_n = 0;
     for (int i = 0; i < b.n_seq; ++i) max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
     if (max_n <= 0 || n_units <= 0) return hipSuccess;
@@ -316,7 +337,7 @@ hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_
         const int gt = subgroup_size(G, j0);
         Runner fn = pick_runner(k_type, hd, gt);
         if (!fn) return hipErrorInvalidValue;
-        fn(grid, s, cv, b, G, j0, coef, cg.words, raw);
+        fn(grid, s, cv, b, G, j0, coef, cg.words, raw, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         j0 += gt;

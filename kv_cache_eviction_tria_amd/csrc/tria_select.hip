@@ -8,20 +8,27 @@
 // The budget counts the protected rows ("TriAttention Native C++ Worklog":
 // compaction logs keep exactly kv_budget rows).
 //
-// Per unit (1024 threads; thread t owns rows j*1024 + t, j < RPT, so every
-// load of the raw scores is coalesced):
-//   1. moments of every head over the rows with a finite score (fp64 sums of
-//      values shifted by the head's first score, against cancellation);
-//   2. agg(r) = max_h (s_h - mu_h)/sigma_h in fp64, rounded once to fp32,
-//      -inf if any of the row's scores is not finite; mapped to an
-//      order-preserving 32-bit key (-0 folded into +0);
-//   3. exact k-th-largest key among the candidates by four 8-bit radix passes
-//      over LDS histograms (one per wave; lanes that share a digit add once);
-//   4. ties at the threshold go to the lowest row indices, and the kept rows
-//      are written in ascending order: ranks in row order come from wave
-//      ballots plus a prefix over the (j, wave) counts.
-// Keys live in registers for n <= 8K rows, in LDS for n <= 32K, else in a
-// global scratch array.
+// Per unit (1024 threads; thread t owns rows j*1024 + t, j < RPT):
+//   1. head statistics: the per-tile moment partials (written by the scorer,
+//      or by moments_kernel for caller-provided scores) are merged exactly in
+//      fp64 into each head's mean and population variance over the rows with
+//      a finite score;
+//   2. one read of the raw scores, with the row's G scores in vector loads
+//      and eight rows per thread in flight: agg(r) = max_h (s_h - mu_h) /
+//      sigma_h (fp64, rounded once to fp32; -inf if any score is not finite),
+//      mapped to an order-preserving 32-bit key (-0 folded into +0), and
+//      counted into a 2048-bin histogram that is linear in agg over [-8, 8)
+//      (clamped at both ends; the bin is a monotone function of the key);
+//   3. the bin holding the k-th largest candidate comes from a suffix scan of
+//      the histogram; that bin's keys (a few hundred for the synthetic
+//      workloads) are gathered in LDS and the exact k-th largest key T and the
+//      number of rows equal to T to take are found by counting.  A bin too
+//      large for LDS (e.g. every score equal) falls back to an exact 4-pass
+//      8-bit radix select over all candidate keys;
+//   4. rows equal to T are taken lowest row first, and the kept rows are
+//      written in ascending order: ranks in row order come from wave ballots
+//      plus a prefix over the (j, wave) counts.
+// Keys live in registers for n <= 32K rows, else in a global scratch array.
 #include "tria_internal.h"
 
 namespace tria {
@@ -30,19 +37,32 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kWaves = kSelThreads / 64;
-constexpr int kHeadChunk = 4;
+constexpr int kBins = 2048;
+constexpr float kBinLo = -8.0f;
+constexpr float kBinScale = 128.0f;  // bins per unit of agg
+constexpr int kListCap = 2048;
+// rows per thread whose loads are in flight together (fewer for wide rows)
+template <int GV>
+constexpr int kBatchRows = GV >= 8 ? 4 : 8;
+// Loops over a thread's rows are fully unrolled when its keys live in registers.
+template <int RPT>
+constexpr int kRowUnroll = RPT <= 32 ? RPT : 4;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
     x = x + 0.0f;  // -0 -> +0 so that equal scores compare equal
     const uint32_t u = __float_as_uint(x);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// Histogram bin of an aggregated score: non-decreasing in x, -inf -> 0.
+__device__ __forceinline__ int bin_of(float x) {
+    float y = (x - kBinLo) * kBinScale;
+    y = fminf(fmaxf(y, 0.0f), (float)(kBins - 1));
+    return (int)y;
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -94,216 +114,300 @@ __device__ __forceinline__ int lane_rank(uint64_t mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-template <int RPT, int KM>
+// The G raw scores of row r -> aggregated score (GV: scores per vector load;
+// 0 = scalar loads for any G).
+template <int GV>
+struct RowLoad {
+    float4 v[GV == 0 ? 1 : (GV + 3) / 4];
+};
+
+template <int GV>
+__device__ __forceinline__ void load_row(RowLoad<GV>& x, const float* R, int64_t r) {
+    if constexpr (GV == 1) {
+        x.v[0].x = R[r];
+    } else if constexpr (GV == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(R + r * 2);
+        x.v[0].x = t.x;
+        x.v[0].y = t.y;
+    } else if constexpr (GV >= 4) {
+#pragma unroll
+        for (int i = 0; i < GV / 4; ++i) x.v[i] = reinterpret_cast<const float4*>(R + r * GV)[i];
+    }
+}
+
+__device__ __forceinline__ float f4_get(const float4& v, int q) {
+    return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+}
+
+template <int GV>
+__device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, int64_t r, int G,
+                                        const double* mu, const double* isg) {
+    double best = -INFINITY;
+    bool bad = false;
+    if constexpr (GV == 0) {
+        for (int h = 0; h < G; ++h) {
+            const float s = R[r * G + h];
+            if (!isfinite(s)) bad = true;
+            const double z = ((double)s - mu[h]) * isg[h];
+            best = (h == 0 || z > best) ? z : best;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < GV; ++h) {
+            const float s = f4_get(x.v[h >> 2], h & 3);
+            if (!isfinite(s)) bad = true;
+            const double z = ((double)s - mu[h]) * isg[h];
+            best = (h == 0 || z > best) ? z : best;
+        }
+    }
+    return bad ? -INFINITY : (float)best;
+}
+
+template <int RPT, int GV>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    Batch b, int units_per_seq, int G, const float* __restrict__ raw, int32_t* __restrict__ keep,
-    float* __restrict__ agg_out, uint32_t* __restrict__ key_scratch) {
+    Batch b, int units_per_seq, int G, const float* __restrict__ raw,
+    const PartRec* __restrict__ part, int32_t* __restrict__ keep, float* __restrict__ agg_out,
+    uint32_t* __restrict__ key_scratch, int32_t* __restrict__ chunk_pb, uint32_t* ticket) {
+    constexpr bool kRegKeys = RPT <= 32;
+    // the compaction that follows on this stream takes its tasks from *ticket
+    if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
     const int u = blockIdx.x;
     const int seq = u / units_per_seq;
     const int uu = u - seq * units_per_seq;
     const SeqDesc sd = b.seq[seq];
-    const int64_t n = sd.n;
+    // row indices fit in 32 bits (at most 1024 * 256 rows per unit)
+    const int n = (int)sd.n;
     if (n <= 0) return;
     const float* __restrict__ R = raw + sd.raw_off + (int64_t)uu * n * G;
     int32_t* __restrict__ KI = keep + sd.keep_off + (int64_t)uu * sd.kept;
-    float* AG = agg_out ? agg_out + (int64_t)uu * n : nullptr;
-    // KM: where the keys live -- 0 registers, 1 LDS, 2 global scratch
-    constexpr bool kGmemKeys = KM == 2;
-    uint32_t* KS = kGmemKeys ? key_scratch + sd.raw_off / G + (int64_t)uu * n : nullptr;
-    __shared__ uint32_t key_lds[KM == 1 ? RPT * kSelThreads : 1];
+    float* AG = agg_out ? agg_out + sd.raw_off / G + (int64_t)uu * n : nullptr;
+    uint32_t* KS = kRegKeys ? nullptr : key_scratch + sd.raw_off / G + (int64_t)uu * n;
+    const int64_t tiles = part_tiles(n);
+    const PartRec* __restrict__ P = part + (sd.part_off + (int64_t)uu * tiles) * G;
 
-    __shared__ double red[kWaves][kHeadChunk][2];
-    __shared__ int redc[kWaves][kHeadChunk];
     __shared__ double mu_sh[64], isg_sh[64];
-    __shared__ uint32_t hist[kWaves][256];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t list[kListCap];
+    __shared__ uint32_t rhist[kWaves][256];
     __shared__ uint32_t tot[256];
     __shared__ int scan_sh[kWaves];
-    __shared__ int found_sh[2];
+    __shared__ int found_sh[4];
     __shared__ int cnt_sh[RPT * kWaves];
 
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    auto row_of = [&](int j) -> int64_t { return (int64_t)j * kSelThreads + t; };
-    // loops over owned rows are fully unrolled when keys live in registers
+    auto row_of = [&](int j) -> int { return j * kSelThreads + t; };
 
-    // 1. moments per head (rows strided by 1024 for coalesced reads)
-    for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
-        double shift[kHeadChunk], sum[kHeadChunk], sq[kHeadChunk];
-        int cnt[kHeadChunk];
-#pragma unroll
-        for (int q = 0; q < kHeadChunk; ++q) {
-            const float s0 = (h0 + q < G) ? R[h0 + q] : 0.0f;
-            shift[q] = isfinite(s0) ? (double)s0 : 0.0;
-            sum[q] = 0.0;
-            sq[q] = 0.0;
-            cnt[q] = 0;
+    // 1. head statistics from the tile partials: wavefront w merges heads
+    //    w, w + 16, ... (lanes stride over the tiles; fixed summation order)
+    for (int h = wid; h < G; h += kWaves) {
+        double c = 0.0, a = 0.0;
+        for (int64_t i = lane; i < tiles; i += 64) {
+            const PartRec pr = P[i * G + h];
+            double mean, m2;
+            part_stats(pr, &mean, &m2);
+            c += pr.cnt;
+            a += pr.cnt * mean;
         }
-        for (int64_t r = t; r < n; r += kSelThreads) {
-#pragma unroll
-            for (int q = 0; q < kHeadChunk; ++q) {
-                if (h0 + q < G) {
-                    const float s = R[r * G + h0 + q];
-                    if (isfinite(s)) {
-                        const double d = (double)s - shift[q];
-                        sum[q] += d;
-                        sq[q] = fma(d, d, sq[q]);
-                        cnt[q] += 1;
-                    }
-                }
-            }
+        c = wave_sum_f64(c);
+        a = wave_sum_f64(a);
+        const double mu = c > 0.0 ? a / c : 0.0;
+        double m2 = 0.0;
+        for (int64_t i = lane; i < tiles; i += 64) {
+            const PartRec pr = P[i * G + h];
+            double mean, mt;
+            part_stats(pr, &mean, &mt);
+            const double d = mean - mu;
+            m2 += mt + pr.cnt * d * d;
         }
-#pragma unroll
-        for (int q = 0; q < kHeadChunk; ++q) {
-            const double a = wave_sum(sum[q]), c = wave_sum(sq[q]);
-            const int k = wave_sum_i(cnt[q]);
-            if (lane == 0) {
-                red[wid][q][0] = a;
-                red[wid][q][1] = c;
-                redc[wid][q] = k;
-            }
-        }
-        __syncthreads();
-        if (t < kHeadChunk && h0 + t < G) {
-            double a = 0.0, c = 0.0;
-            long long k = 0;
-            for (int w = 0; w < kWaves; ++w) {
-                a += red[w][t][0];
-                c += red[w][t][1];
-                k += redc[w][t];
-            }
-            double mu = 0.0, isg = 0.0;
-            if (k > 0) {
-                const float s0 = R[h0 + t];
-                const double m = a / (double)k;
-                double var = c / (double)k - m * m;
-                var = var > 0.0 ? var : 0.0;
-                mu = (isfinite(s0) ? (double)s0 : 0.0) + m;
-                const double sg = sqrt(var);
-                isg = sg > 0.0 ? 1.0 / sg : 0.0;
-            }
-            mu_sh[h0 + t] = mu;
-            isg_sh[h0 + t] = isg;
-        }
-        __syncthreads();
-    }
-
-    // 2. aggregated score -> order-preserving key
-    const int64_t cand_lo = sd.s_end, cand_hi = sd.w_start;
-    uint32_t key[KM == 0 ? RPT : 1];
-#pragma unroll (KM == 0 ? RPT : 4)
-    for (int j = 0; j < RPT; ++j) {
-        const int64_t r = row_of(j);
-        if (r < n) {
-            double best = -INFINITY;
-            bool bad = false;
-            for (int h = 0; h < G; ++h) {
-                const float s = R[r * G + h];
-                if (!isfinite(s)) bad = true;
-                const double z = ((double)s - mu_sh[h]) * isg_sh[h];
-                best = (h == 0 || z > best) ? z : best;
-            }
-            const float a = bad ? -INFINITY : (float)best;
-            if (AG) AG[r] = a;
-            const uint32_t kk = order_key(a);
-            if constexpr (KM == 2) KS[r] = kk;
-            else if constexpr (KM == 1) key_lds[j * kSelThreads + t] = kk;
-            else key[j] = kk;
-        } else {
-            if constexpr (KM == 1) key_lds[j * kSelThreads + t] = 0;
-            else if constexpr (KM == 0) key[j] = 0;
+        m2 = wave_sum_f64(m2);
+        if (lane == 0) {
+            const double var = c > 0.0 ? m2 / c : 0.0;
+            mu_sh[h] = mu;
+            isg_sh[h] = var > 0.0 ? 1.0 / sqrt(var) : 0.0;
         }
     }
+    for (int i = t; i < kBins; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+
+    // 2. aggregated score -> key, histogram of the candidates
+    const int cand_lo = (int)sd.s_end, n_cand = (int)(sd.w_start - sd.s_end);
+    // candidates: rows [s_end, w_start) (all below n)
+    auto is_cand = [&](int r) -> bool { return (unsigned)(r - cand_lo) < (unsigned)n_cand; };
+    uint32_t key[kRegKeys ? RPT : 1];
+    constexpr int kBatch = kBatchRows<GV>;
+    constexpr int kNB = (RPT + kBatch - 1) / kBatch;
+    constexpr int kUB = kRegKeys ? kNB : 1;
+#pragma unroll kUB
+    for (int j0 = 0; j0 < RPT; j0 += kBatch) {
+        RowLoad<GV> x[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int r = row_of(j0 + q);
+            if (j0 + q < RPT && r < n) load_row<GV>(x[q], R, r);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int j = j0 + q;
+            if (j >= RPT) break;
+            const int r = row_of(j);
+            uint32_t kk = 0;
+            if (r < n) {
+                const float a = agg_of<GV>(x[q], R, r, G, mu_sh, isg_sh);
+                if (AG) AG[r] = a;
+                kk = order_key(a);
+                if (is_cand(r)) atomicAdd(&hist[bin_of(a)], 1u);
+                if constexpr (!kRegKeys) KS[r] = kk;
+            }
+            if constexpr (kRegKeys) key[j] = kk;
+        }
+    }
+    __syncthreads();
     auto get_key = [&](int j) -> uint32_t {
-        if constexpr (KM == 2) return KS[row_of(j)];
-        else if constexpr (KM == 1) return key_lds[j * kSelThreads + t];
-        else return key[j];
+        if constexpr (kRegKeys) return key[j];
+        else return row_of(j) < n ? KS[row_of(j)] : 0u;
     };
-    auto is_cand = [&](int64_t r) -> bool { return r >= cand_lo && r < cand_hi; };
 
-    // 3. threshold: the k-th largest candidate key
-    const int64_t n_cand = cand_hi - cand_lo;
+    // 3. threshold: the k-th largest candidate key T; krem rows equal to T are taken
     const int64_t k_take = sd.kept - (n - n_cand);
-    const bool take_none = k_take <= 0;
+    const bool radix = k_take > 0 && k_take < n_cand;
     const bool take_all = k_take >= n_cand;
-    uint32_t prefix = 0, mask = 0;
-    int krem = (int)k_take;
-    if (!take_none && !take_all) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            for (int i = lane; i < 256; i += 64) hist[wid][i] = 0;
-            __syncthreads();
-#pragma unroll (KM == 0 ? RPT : 4)
+    uint32_t T = 0;
+    int krem = 0;
+    bool rank_ties = false;
+    if (radix) {
+        // bins from the top: thread t holds bins kBins-1-2t and kBins-2-2t
+        const int b0 = kBins - 1 - 2 * t, b1 = b0 - 1;
+        const int c0 = t < kBins / 2 ? (int)hist[b0] : 0;
+        const int c1 = t < kBins / 2 ? (int)hist[b1] : 0;
+        int total;
+        const int above = block_excl_scan(c0 + c1, scan_sh, &total);
+        const int k = (int)k_take;
+        if (t < kBins / 2) {
+            if (above < k && above + c0 >= k) {
+                found_sh[0] = b0;
+                found_sh[1] = k - above;
+            } else if (above + c0 < k && above + c0 + c1 >= k) {
+                found_sh[0] = b1;
+                found_sh[1] = k - above - c0;
+            }
+        }
+        if (t == 0) found_sh[2] = 0;
+        __syncthreads();
+        const int bstar = found_sh[0], kb = found_sh[1];
+        const int cb = (int)hist[bstar];
+        if (cb <= kListCap) {
+            // the bin's keys into LDS, then the kb-th largest by counting
+#pragma unroll kRowUnroll<RPT>
             for (int j = 0; j < RPT; ++j) {
-                const int64_t r = row_of(j);
-                const uint32_t kk = get_key(j);
-                const bool act = r < n && is_cand(r) && ((kk & mask) == prefix);
-                hist_add(hist[wid], act, (kk >> shift) & 255u);
-            }
-            __syncthreads();
-            if (t < 256) {
-                uint32_t s = 0;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) s += hist[w][t];
-                tot[t] = s;
-            }
-            __syncthreads();
-            if (wid == 0) {
-                // lane l holds bins 4l..4l+3; count of keys in bins above this lane's
-                const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1], c2 = tot[4 * lane + 2],
-                               c3 = tot[4 * lane + 3];
-                const uint32_t mine = c0 + c1 + c2 + c3;
-                uint32_t incl = mine;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t y = __shfl_down(incl, o, 64);
-                    if (lane + o < 64) incl += y;
-                }
-                uint32_t above = incl - mine;
-                const uint32_t cs[4] = {c0, c1, c2, c3};
-#pragma unroll
-                for (int q = 3; q >= 0; --q) {
-                    if (above < (uint32_t)krem && above + cs[q] >= (uint32_t)krem) {
-                        found_sh[0] = 4 * lane + q;
-                        found_sh[1] = krem - (int)above;
-                    }
-                    above += cs[q];
+                const int r = row_of(j);
+                if (is_cand(r)) {
+                    const uint32_t kk = get_key(j);
+                    if (bin_of(key_value(kk)) == bstar) list[atomicAdd(&found_sh[2], 1)] = kk;
                 }
             }
             __syncthreads();
-            prefix |= (uint32_t)found_sh[0] << shift;
-            mask |= 255u << shift;
+            for (int i = t; i < cb; i += kSelThreads) {
+                const uint32_t ki = list[i];
+                int g = 0, e = 0;
+                for (int q = 0; q < cb; ++q) {
+                    const uint32_t kq = list[q];
+                    g += kq > ki;
+                    e += kq == ki;
+                }
+                if (g < kb && kb <= g + e) {  // every thread holding T writes the same values
+                    found_sh[0] = (int)ki;
+                    found_sh[1] = kb - g;
+                    found_sh[3] = e;
+                }
+            }
+            __syncthreads();
+            T = (uint32_t)found_sh[0];
             krem = found_sh[1];
+            rank_ties = found_sh[3] > krem;
             __syncthreads();
+        } else {
+            // exact radix select over every candidate key
+            uint32_t prefix = 0, mask = 0;
+            krem = k;
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                for (int i = lane; i < 256; i += 64) rhist[wid][i] = 0;
+                __syncthreads();
+#pragma unroll kRowUnroll<RPT>
+                for (int j = 0; j < RPT; ++j) {
+                    const int r = row_of(j);
+                    const uint32_t kk = get_key(j);
+                    const bool act = is_cand(r) && ((kk & mask) == prefix);
+                    hist_add(rhist[wid], act, (kk >> shift) & 255u);
+                }
+                __syncthreads();
+                if (t < 256) {
+                    uint32_t s = 0;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) s += rhist[w][t];
+                    tot[t] = s;
+                }
+                __syncthreads();
+                if (wid == 0) {
+                    // lane l holds bins 4l..4l+3; count of keys in bins above this lane's
+                    const uint32_t e0 = tot[4 * lane], e1 = tot[4 * lane + 1],
+                                   e2 = tot[4 * lane + 2], e3 = tot[4 * lane + 3];
+                    const uint32_t mine = e0 + e1 + e2 + e3;
+                    uint32_t incl = mine;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const uint32_t y = __shfl_down(incl, o, 64);
+                        if (lane + o < 64) incl += y;
+                    }
+                    uint32_t ab = incl - mine;
+                    const uint32_t cs[4] = {e0, e1, e2, e3};
+#pragma unroll
+                    for (int q = 3; q >= 0; --q) {
+                        if (ab < (uint32_t)krem && ab + cs[q] >= (uint32_t)krem) {
+                            found_sh[0] = 4 * lane + q;
+                            found_sh[1] = krem - (int)ab;
+                        }
+                        ab += cs[q];
+                    }
+                }
+                __syncthreads();
+                prefix |= (uint32_t)found_sh[0] << shift;
+                mask |= 255u << shift;
+                krem = found_sh[1];
+                __syncthreads();
+            }
+            T = prefix;
+            rank_ties = true;
         }
     }
-    const uint32_t T = prefix;
 
     // 4. ties at T go to the lowest rows; then write kept rows in order.
     // Row order is (j, wave, lane); ranks = prefix over the (j, wave) counts
     // plus the lane's rank within its wave's ballot.
-    const bool radix = !take_none && !take_all;
     auto ordered_ranks = [&](auto flag_of, auto use_rank) {
-#pragma unroll (KM == 0 ? RPT : 4)
+#pragma unroll kRowUnroll<RPT>
         for (int j = 0; j < RPT; ++j) {
             const uint64_t m = __ballot(flag_of(j));
             if (lane == 0) cnt_sh[j * kWaves + wid] = __popcll(m);
         }
         __syncthreads();
-        int loc[4], sum = 0;
+        constexpr int kPer = (RPT * kWaves + kSelThreads - 1) / kSelThreads;
+        int loc[kPer], sum = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = 4 * t + q;
+        for (int q = 0; q < kPer; ++q) {
+            const int e = kPer * t + q;
             loc[q] = sum;
             sum += e < RPT * kWaves ? cnt_sh[e] : 0;
         }
         int total;
         const int base = block_excl_scan(sum, scan_sh, &total);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = 4 * t + q;
+        for (int q = 0; q < kPer; ++q) {
+            const int e = kPer * t + q;
             if (e < RPT * kWaves) cnt_sh[e] = base + loc[q];
         }
         __syncthreads();
-#pragma unroll (KM == 0 ? RPT : 4)
+#pragma unroll kRowUnroll<RPT>
         for (int j = 0; j < RPT; ++j) {
             const bool f = flag_of(j);
             const uint64_t m = __ballot(f);
@@ -316,21 +420,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 #pragma unroll
     for (int q = 0; q < (RPT + 31) / 32; ++q) kbits[q] = 0;
     auto set_keep = [&](int j) { kbits[j >> 5] |= 1u << (j & 31); };
-#pragma unroll (KM == 0 ? RPT : 4)
+#pragma unroll kRowUnroll<RPT>
     for (int j = 0; j < RPT; ++j) {
-        const int64_t r = row_of(j);
+        const int r = row_of(j);
         if (r >= n) continue;
         if (!is_cand(r) || take_all) {
             set_keep(j);
-        } else if (radix && get_key(j) > T) {
-            set_keep(j);
+        } else if (radix) {
+            const uint32_t kk = get_key(j);
+            if (kk > T || (kk == T && !rank_ties)) set_keep(j);
         }
     }
-    if (radix) {
+    if (rank_ties) {
         ordered_ranks(
             [&](int j) {
-                const int64_t r = row_of(j);
-                return r < n && is_cand(r) && get_key(j) == T;
+                const int r = row_of(j);
+                return is_cand(r) && get_key(j) == T;
             },
             [&](int j, int rank) {
                 if (rank < krem) set_keep(j);
@@ -340,18 +445,69 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                   [&](int j, int rank) {
                       if (rank < sd.kept) KI[rank] = (int32_t)row_of(j);
                   });
+    // The scan's prefix at (j, wave) is the number of kept rows below row
+    // 64 (16 j + wave): write it at the compaction's chunk boundaries.
+    if (chunk_pb) {
+        const int nb = (int)chunk_bounds(sd.kept);
+        int32_t* PB = chunk_pb + sd.pb_off + (int64_t)uu * nb;
+        for (int e = t; e < nb; e += kSelThreads)
+            PB[e] = e < RPT * kWaves ? cnt_sh[e] : (int32_t)sd.kept;
+    }
 }
 
-template <int RPT, int KM>
+// Moment partials of caller-provided raw scores (the scorer writes them
+// itself during a whole pass): one wavefront per tile of 64 rows.
+constexpr int kMomThreads = 256;
+__global__ __launch_bounds__(kMomThreads) void moments_kernel(Batch b, int units_per_seq, int G,
+                                                              const float* __restrict__ raw,
+                                                              PartRec* __restrict__ part) {
+    const int u = blockIdx.y;
+    const int seq = u / units_per_seq;
+    const int uu = u - seq * units_per_seq;
+    const SeqDesc sd = b.seq[seq];
+    const int64_t n = sd.n;
+    const int64_t tile = (int64_t)blockIdx.x * (kMomThreads / kPartRows) + (threadIdx.x >> 6);
+    if (tile * kPartRows >= n) return;  // whole wavefront past the end
+    const float* __restrict__ R = raw + sd.raw_off + (int64_t)uu * n * G;
+    PartRec* out = part + (sd.part_off + (int64_t)uu * part_tiles(n) + tile) * G;
+    const int64_t r = tile * kPartRows + (threadIdx.x & 63);
+    for (int h0 = 0; h0 < G; h0 += 4) {
+        float s[4];
+        bool v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s[q] = (r < n && h0 + q < G) ? R[r * G + h0 + q] : 0.0f;
+            v[q] = r < n && h0 + q < G && isfinite(s[q]);
+        }
+        wave_moments<4>(s, v, out + h0, G - h0 < 4 ? G - h0 : 4);
+    }
+}
+
+template <int RPT, int GV>
 void run_sel(int grid, hipStream_t s, const Batch& b, int ups, int G, const float* raw,
-             int32_t* keep, float* agg, uint32_t* ks) {
-    hipLaunchKernelGGL((select_kernel<RPT, KM>), dim3(grid), dim3(kSelThreads), 0, s, b, ups, G,
-                       raw, keep, agg, ks);
+             const PartRec* part, int32_t* keep, float* agg, uint32_t* ks, int32_t* pb,
+             uint32_t* ticket) {
+    hipLaunchKernelGGL((select_kernel<RPT, GV>), dim3(grid), dim3(kSelThreads), 0, s, b, ups, G,
+                       raw, part, keep, agg, ks, pb, ticket);
+}
+
+using SelRunner = void (*)(int, hipStream_t, const Batch&, int, int, const float*,
+                           const PartRec*, int32_t*, float*, uint32_t*, int32_t*, uint32_t*);
+
+template <int RPT>
+SelRunner pick_gv(int G) {
+    switch (G) {
+        case 1: return run_sel<RPT, 1>;
+        case 2: return run_sel<RPT, 2>;
+        case 4: return run_sel<RPT, 4>;
+        case 8: return run_sel<RPT, 8>;
+        default: return run_sel<RPT, 0>;
+    }
 }
 
 }  // namespace
 
-// Rows a key-scratch array must hold for a batch (0 when keys stay on chip).
+// Rows a key-scratch array must hold for a batch (0 when keys stay in registers).
 // Unit uu of sequence i uses rows raw_off/G + uu*n .. + n of the array, so the
 // size is the largest such end (the batch may describe a group of layers whose
 // offsets start past zero).
@@ -366,23 +522,39 @@ int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G) {
     return max_n > 32 * kSelThreads ? end : 0;
 }
 
+hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float* raw,
+                          PartRec* part, hipStream_t s) {
+    int64_t max_n = 0;
+    for (int i = 0; i < b.n_seq; ++i) max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
+    if (max_n <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((max_n + kMomThreads - 1) / kMomThreads),
+                    (unsigned)(units_per_seq * b.n_seq));
+    hipLaunchKernelGGL(moments_kernel, grid, dim3(kMomThreads), 0, s, b, units_per_seq, G, raw,
+                       part);
+    return hipGetLastError();
+}
+
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
-                              int32_t* keep, float* agg, uint32_t* key_scratch, hipStream_t s) {
+                              const PartRec* part, int32_t* keep, float* agg,
+                              uint32_t* key_scratch, int32_t* chunk_pb, uint32_t* ticket,
+                              hipStream_t s) {
     int64_t max_n = 0;
     for (int i = 0; i < b.n_seq; ++i) max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
     if (max_n <= 0) return hipSuccess;
     const int grid = units_per_seq * b.n_seq;
     const int64_t rpt = (max_n + kSelThreads - 1) / kSelThreads;
-    if (rpt <= 1) run_sel<1, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 2) run_sel<2, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 4) run_sel<4, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 8) run_sel<8, 0>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 16) run_sel<16, 1>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 32) run_sel<32, 1>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 64) run_sel<64, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 128) run_sel<128, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
-    else if (rpt <= 256) run_sel<256, 2>(grid, s, b, units_per_seq, G, raw, keep, agg, key_scratch);
+    SelRunner fn;
+    if (rpt <= 1) fn = pick_gv<1>(G);
+    else if (rpt <= 2) fn = pick_gv<2>(G);
+    else if (rpt <= 4) fn = pick_gv<4>(G);
+    else if (rpt <= 8) fn = pick_gv<8>(G);
+    else if (rpt <= 16) fn = pick_gv<16>(G);
+    else if (rpt <= 32) fn = pick_gv<32>(G);
+    else if (rpt <= 64) fn = pick_gv<64>(G);
+    else if (rpt <= 128) fn = pick_gv<128>(G);
+    else if (rpt <= 256) fn = pick_gv<256>(G);
     else return hipErrorInvalidValue;
+    fn(grid, s, b, units_per_seq, G, raw, part, keep, agg, key_scratch, chunk_pb, ticket);
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ TRIA_E_INVAL = -1
 TRIA_E_UNSUPPORTED = -2
 TRIA_E_HIP = -3
 TRIA_E_NOMEM = -4
+TRIA_E_DEVICE = -5
 TRIA_KV_F16 = 0
 TRIA_KV_Q8_0 = 1
 TRIA_MAX_SEQ = 64
@@ -89,6 +90,10 @@ def lib():
             L.tria_evict_paged_batch.restype = ctypes.c_int
             L.tria_evict_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32, vp, vp, i64,
                                                  i64, vp, vp]
+            L.tria_set_pipeline.restype = ctypes.c_int
+            L.tria_set_pipeline.argtypes = [vp, i32]
+            L.tria_device_status.restype = ctypes.c_int
+            L.tria_device_status.argtypes = [vp]
             L.tria_timing_enable.restype = ctypes.c_int
             L.tria_timing_enable.argtypes = [vp, i32]
             L.tria_timing_read.restype = ctypes.c_int
@@ -232,6 +237,16 @@ def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, 
     _check(lib().tria_evict_paged_batch(ctx.handle, ctypes.byref(pc), n_seq, nt, bd, sink,
                                         window, kept, _stream(stream)), "tria_evict_paged_batch")
     return [int(x) for x in kept]
+
+
+def tria_set_pipeline(ctx: TriaCtx, layers_per_group: int) -> None:
+    """0: one group (default); > 0: layer groups overlapped on two streams."""
+    _check(lib().tria_set_pipeline(ctx.handle, int(layers_per_group)), "tria_set_pipeline")
+
+
+def tria_device_status(ctx: TriaCtx) -> None:
+    """Synchronise the device; raise if a compaction gave up a bounded wait."""
+    _check(lib().tria_device_status(ctx.handle), "tria_device_status")
 
 
 def tria_timing_enable(ctx: TriaCtx, enable: bool) -> None:

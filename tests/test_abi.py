@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert tria.tria_strerror(code)
     assert tria.tria_strerror(-99) == "unknown error"
 
