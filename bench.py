@@ -26,7 +26,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,14 +35,6 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "KV tokens scored+compacted/sec and eviction-pass ms at 32K ctx; % of HBM peak"
 UNIT = "KV rows/s (layer x KV-head x token, scored + compacted)"
-# sources whose kernels each timed stage runs
-STAGE_SOURCES = {
-    "score": ["tria_score.hip", "tria_prep.hip", "tria_internal.h"],
-    "select": ["tria_select.hip", "tria_internal.h"],
-    "compact": ["tria_compact.hip", "tria_internal.h"],
-}
-
-
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,23 +46,19 @@ def parse():
                     help="CPU work the oracle baseline aims for (whole passes, at least one)")
     ap.add_argument("--staged-steps", type=int, default=5)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calibrate-bytes", type=int, default=0,
+                    help="run one plain streaming kernel (uint8 xor) over this many bytes before "
+                         "the timed steps, as the byte reference for profiler counters")
     ap.add_argument("--layers-per-group", type=int, default=0,
                     help="tria_set_pipeline: 0 = one group; > 0 = overlapped layer groups")
     return ap.parse_args()
 
 
-def sources_digest(stage):
-    h = hashlib.sha256()
-    for f in STAGE_SOURCES[stage]:
-        with open(os.path.join(ROOT, "kv_cache_eviction_tria_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(stage, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel sources; None otherwise."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (stage, workload))
+    from kv_cache_eviction_tria_amd.profile_summary import sources_digest
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (stage, workload))
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -101,8 +88,22 @@ def main():
         sys.exit(2)
     from kv_cache_eviction_tria_amd import synth
     wl = synth.WORKLOADS[args.workload]
+    if args.calibrate_bytes > 0:
+        calibrate(args.calibrate_bytes)
     out = bench_paged(args, wl) if wl.n_seq else bench_contiguous(args, wl)
     print(json.dumps(out), flush=True)
+
+
+def calibrate(nbytes):
+    """One streaming kernel that reads and writes exactly nbytes (untimed)."""
+    import torch
+    src = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_xor(src, 0x5A, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def log(msg):
