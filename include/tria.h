@@ -175,9 +175,9 @@ int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
 /* One whole eviction pass: tria_score, tria_select, tria_compact with the
  * context's own scratch for the scores and kept indices.  Returns the kept
  * count.  budget >= n_tokens enqueues nothing and returns n_tokens.
- * With layer groups (tria_set_pipeline) the selection and compaction of a
- * group run on a second stream owned by the context while later groups are
- * scored on `stream`; the second stream waits for an event recorded on
+ * With layer groups (tria_set_pipeline) the compaction of a group runs on a
+ * second stream owned by the context while later groups are scored on
+ * `stream`; the second stream waits for an event recorded on
  * `stream` and `stream` waits for it before the call returns, so the pass is
  * ordered with respect to `stream` like a single-stream pass. */
 int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
@@ -195,9 +195,9 @@ int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t
 /* Pipelining of tria_evict / tria_evict_paged_batch.  layers_per_group = 0
  * (the default): every layer is scored, then selected, then compacted, all on
  * the caller's stream.  > 0: the layers are processed in groups of that many
- * (at most 8 groups; larger groups if needed) and the selection and
- * compaction of a group run on the context's second stream while the later
- * groups are scored on the caller's stream (see tria_evict).  Results are
+ * (at most 8 groups; larger groups if needed): each group is scored and
+ * selected on the caller's stream and compacted on the context's second
+ * stream while the later groups are scored (see tria_evict).  Results are
  * identical either way.  Returns TRIA_OK or TRIA_E_INVAL. */
 int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
 

@@ -21,6 +21,10 @@ hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const fl
 
 using namespace tria;
 
+namespace {
+constexpr int kMaxGroups = 8;  // layer groups of one pass (tria_set_pipeline)
+}
+
 struct tria_ctx {
     int L, Hkv, Hq, G, hd, F, k_type, v_type;
     int kb, vb;
@@ -130,10 +134,11 @@ int reserve_flags(tria_ctx* ctx, const Batch& b, int units, hipStream_t s) {
 // A compaction launch, timed when timing is on.  pb: the selector's chunk
 // prefix counts, or nullptr to derive them from keep into ctx->pb.
 int compact_timed(tria_ctx* ctx, const CacheView& cv, const Batch& b, int units,
-                  const int32_t* keep, const int32_t* pb, hipStream_t s) {
+                  const int32_t* keep, const int32_t* pb, hipStream_t s, int group = 0) {
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_COMPACT, s, &slot);
-    if (e == hipSuccess) e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, s);
+    if (e == hipSuccess)
+        e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, ctx->cst.ticket + group, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
@@ -263,7 +268,7 @@ int reserve_select(tria_ctx* ctx, const Batch& b, int units_per_seq, hipStream_t
 // Select over `layers` layers per sequence (all by default).  have_part: the
 // scorer already wrote the moment partials of these scores into ctx->part.
 int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
-               bool have_part, hipStream_t s, int layers = -1) {
+               bool have_part, hipStream_t s, int layers = -1, int group = 0) {
     const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
     int rc = reserve_select(ctx, b, ups, s);
     if (rc) return rc;
@@ -272,7 +277,7 @@ int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, f
     if (e == hipSuccess && !have_part) e = launch_moments(b, ups, ctx->G, raw, ctx->part, s);
     if (e == hipSuccess)
         e = launch_select_impl(b, ups, ctx->G, raw, ctx->part, keep, agg, ctx->keys, ctx->pb,
-                               ctx->cst.ticket, s);
+                               ctx->cst.ticket + group, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
     return TRIA_OK;
@@ -304,16 +309,14 @@ Batch sub_batch(const Batch& b, int l0, int L, int Hkv, int G) {
     return s;
 }
 
-constexpr int kMaxGroups = 8;
 
 // One whole pass (score -> select -> compact).  With more than one group of
-// layers (tria_set_pipeline): the coefficient tables of all layers are built first, then the
-// groups are scored back to back on `s`; the selection and compaction of
-// group g run on the context's second stream once g's scores are written
-// (an event), overlapping the scoring of the later groups.  The scorer is
-// bound by the vector ALUs, the compaction by HBM.  The second stream waits
-// for an event recorded on `s` before its first launch and `s` waits for the
-// last compaction, so the pass stays ordered with respect to `s`.
+// layers (tria_set_pipeline): the coefficient tables of all layers are built
+// first, then each group is scored and selected on `s`, and its compaction
+// runs on the context's second stream (after an event recorded on `s`) while
+// the next groups are scored.  Each group's compaction takes its tasks from
+// its own ticket counter, which that group's selection resets.  `s` waits for
+// the last compaction, so the pass stays ordered with respect to `s`.
 int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) {
     const int L = ctx->L, n_seq = b.n_seq;
     const int lpg = ctx->layers_per_group > 0 ? ctx->layers_per_group : L;
@@ -343,12 +346,12 @@ int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) 
         const int units = n_seq * lg * ctx->Hkv;
         rc = run_score_only(ctx, sv, sb, units, ctx->raw, ctx->part, s);
         if (rc) return rc;
+        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, true, s, lg, g);
+        if (rc) return rc;
         e = hipEventRecord(ctx->ev_group[g], s);
         if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_group[g], 0);
         if (e != hipSuccess) return hip_fail(ctx, e);
-        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, true, ctx->aux, lg);
-        if (rc) return rc;
-        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->pb, ctx->aux);
+        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->pb, ctx->aux, g);
         if (rc) return rc;
     }
     e = hipEventRecord(ctx->ev_join, ctx->aux);
@@ -472,8 +475,9 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
     // error word of the compaction's bounded waits, and its task ticket
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.err), sizeof(int));
     if (e == hipSuccess) e = hipMemset(ctx->cst.err, 0, sizeof(int));
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), sizeof(uint32_t));
-    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, sizeof(uint32_t));
+    if (e == hipSuccess)
+        e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), kMaxGroups * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, kMaxGroups * sizeof(uint32_t));
     // second stream (default priority) and events for overlapped passes
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);

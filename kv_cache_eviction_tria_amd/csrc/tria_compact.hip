@@ -298,7 +298,7 @@ int64_t compact_flag_words(const Batch& b, int n_units) {
 
 hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
                           const int32_t* pb, int32_t* pb_scratch, CompactState& st,
-                          hipStream_t s) {
+                          uint32_t* ticket, hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
     const int64_t max_chunks = max_chunks_of(b);
     if (max_chunks <= 0) return hipSuccess;
@@ -311,7 +311,7 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
         }
         const int64_t threads = max_bounds * n_units;
         hipLaunchKernelGGL(chunk_bounds_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                           0, s, cv, b, keep, pb_scratch, n_units, (int)max_bounds, st.ticket);
+                           0, s, cv, b, keep, pb_scratch, n_units, (int)max_bounds, ticket);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         pb = pb_scratch;
@@ -332,7 +332,7 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
     if (need < grid) grid = (int)need;
     st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value
     hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, s, cv, b, keep, pb, st.flags,
-                       (int)max_chunks, st.epoch, n_units, st.ticket, st.err);
+                       (int)max_chunks, st.epoch, n_units, ticket, st.err);
     return hipGetLastError();
 }
 

@@ -243,14 +243,14 @@ struct CompactState {
     uint32_t* flags;
     int64_t flag_words;
     uint32_t epoch;
-    uint32_t* ticket;  // task counter, reset by the kernel before each compaction
+    uint32_t* ticket;  // task counters (one per layer group), reset by the selector
     int* err;
 };
 // pb: the selector's chunk prefix counts for these units, or nullptr to
 // derive them from keep (caller-provided kept indices).
 hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
                           const int32_t* pb, int32_t* pb_scratch, CompactState& st,
-                          hipStream_t s);
+                          uint32_t* ticket, hipStream_t s);
 // Flags a launch over these units needs.
 int64_t compact_flag_words(const Batch& b, int n_units);
 

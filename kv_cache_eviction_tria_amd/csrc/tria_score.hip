@@ -104,12 +104,22 @@ __device__ __forceinline__ void emit_moments(const float (&acc)[GT], bool in_ran
     wave_moments<GT>(acc, valid, part + tile * G + j0);
 }
 
+// Pieces an fp16 row is walked in: the fewest that divide its HD/16 chunks per
+// half-row into groups of at most 4 (16 registers per half-row piece).
+constexpr int f16_pieces(int hd) {
+    const int c = hd / 16;
+    for (int p = 1; p <= c; ++p)
+        if (c % p == 0 && c / p <= 4) return p;
+    return c;
+}
+
 template <int HD, int GT>
 __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
     CacheView cv, Batch b, int G, int j0, const float* __restrict__ coef, int coef_words,
     float* __restrict__ raw, PartRec* __restrict__ part) {
     constexpr int F = HD / 2;
     constexpr int NV = HD / 8;  // 16-byte chunks per row
+    constexpr int PIECES = f16_pieces(HD);
     const int u = blockIdx.y;
     const UnitId id = unit_id(cv, u);
     const int64_t n = b.seq[id.seq].n;
@@ -130,29 +140,44 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
         // of table values out of the loop into (spilled) registers.
         const float* __restrict__ Ci = C + opaque_zero_s();
         const u32x4* row = reinterpret_cast<const u32x4*>(cv.k + row_index(cv, id, r) * (HD * 2));
-        u32x4 d[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) d[i] = row[i];
-        const uint32_t* wd = reinterpret_cast<const uint32_t*>(d);
 
         float acc[GT];
 #pragma unroll
         for (int j = 0; j < GT; ++j) acc[j] = 0.0f;
+        // The row is walked in PIECES pieces (a rolled loop): piece q holds the
+        // pairs [q FP, (q+1) FP), i.e. CH 16-byte chunks of the first half of
+        // the row and the matching CH chunks of the second half.  Only one
+        // piece is live at a time, which keeps wide rows from filling the
+        // register file (hd 256 would need 128 registers for the whole row).
+        constexpr int FP = F / PIECES;
+        constexpr int CH = FP / 8;
         // Pairs in chunks whose coefficients fit the scalar register file.
         constexpr int CP = GT >= 8 ? 1 : 8 / GT;
+#pragma unroll 1
+        for (int q = 0; q < PIECES; ++q) {
+            u32x4 dre[CH], dim[CH];
 #pragma unroll
-        for (int f = 0; f < F; ++f) {
-            if (f % CP == 0) sync_acc<GT>(acc);
-            const uint32_t wr = wd[f >> 1], wi = wd[(f + F) >> 1];
-            const float kre = (f & 1) ? half_hi(wr) : half_lo(wr);
-            const float kim = ((f + F) & 1) ? half_hi(wi) : half_lo(wi);
-            const float mag = __builtin_amdgcn_sqrtf(fmaf(kre, kre, kim * kim));
-            const float* c = Ci + f * GT * 3;
+            for (int i = 0; i < CH; ++i) {
+                dre[i] = row[q * CH + i];
+                dim[i] = row[NV / 2 + q * CH + i];
+            }
+            const uint32_t* wre = reinterpret_cast<const uint32_t*>(dre);
+            const uint32_t* wim = reinterpret_cast<const uint32_t*>(dim);
+            const float* Cq = Ci + q * FP * GT * 3;
 #pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                acc[j] = fmaf(c[3 * j + 0], kre, acc[j]);
-                acc[j] = fmaf(c[3 * j + 1], kim, acc[j]);
-                acc[j] = fmaf(c[3 * j + 2], mag, acc[j]);
+            for (int f = 0; f < FP; ++f) {
+                if (f % CP == 0) sync_acc<GT>(acc);
+                const uint32_t wr = wre[f >> 1], wi = wim[f >> 1];
+                const float kre = (f & 1) ? half_hi(wr) : half_lo(wr);
+                const float kim = (f & 1) ? half_hi(wi) : half_lo(wi);
+                const float mag = __builtin_amdgcn_sqrtf(fmaf(kre, kre, kim * kim));
+                const float* c = Cq + f * GT * 3;
+#pragma unroll
+                for (int j = 0; j < GT; ++j) {
+                    acc[j] = fmaf(c[3 * j + 0], kre, acc[j]);
+                    acc[j] = fmaf(c[3 * j + 1], kim, acc[j]);
+                    acc[j] = fmaf(c[3 * j + 2], mag, acc[j]);
+                }
             }
         }
         if (r_out < n) store_scores<GT>(rout + r_out * G, acc, packed);
