@@ -295,9 +295,17 @@ def bench_paged(args, wl):
     t_round = []
     total = args.warmup + args.steps
     log("rounds: %d warmup + %d timed" % (args.warmup, args.steps))
+    def kept_positions():
+        # positions of every sequence's first B rows (all units); positions are unique
+        # within a unit, so row d moved in a pass iff its position changed
+        return [synth.paged_rows(pg["pos_pool"], pg["block_table"][s], budgets[s]).clone()
+                for s in range(wl.n_seq)]
+
+    moved_total = 0
     for r in range(total):
         append(r)
         torch.cuda.synchronize()
+        before = kept_positions() if r >= args.warmup else None
         if r == args.warmup:
             tria.tria_timing_enable(ctx, True)
         e0.record(stream)
@@ -313,6 +321,9 @@ def bench_paged(args, wl):
                 st_n[s] += n_i[s]
         assert kept == budgets
         n_now = list(kept)
+        if before is not None:
+            after = kept_positions()
+            moved_total += sum(int((a != b_).sum().item()) for a, b_ in zip(after, before))
     tria.tria_timing_enable(ctx, False)
     tria.tria_device_status(ctx)  # raises if a compaction gave up a wait
     ms = float(np.median(t_round))
@@ -321,7 +332,8 @@ def bench_paged(args, wl):
     per_step_n = {s: st_n[s] // args.steps for s in tria.STAGES}
     dom = max(tria.STAGES, key=lambda s: per_step_ms[s])
     kb, vb = synth.row_bytes(wl.k_type, wl.hd), synth.row_bytes(wl.v_type, wl.hd)
-    score_bytes = rows * kb
+    moved = moved_total / args.steps
+    alg = {"score": rows * kb, "select": 0, "compact": moved * 2 * (kb + vb + 4)}
     out = {
         "metric": METRIC,
         "value": rows / (ms * 1e-3),
@@ -345,8 +357,12 @@ def bench_paged(args, wl):
         "initial_pass_rows_per_s": sum(wl.L * wl.Hkv * x for x in lens) / (first_ms * 1e-3),
         "kernel_ms_per_step": per_step_ms,
         "launches_per_step": per_step_n,
-        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom],
-                             score_bytes if dom == "score" else 0, wl.name),
+        "moved_rows_per_round": moved,
+        "round_alg_bytes": alg["score"] + alg["compact"],
+        "round_frac_hbm": (alg["score"] + alg["compact"]) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name),
+        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name)
+                         for s in tria.STAGES},
         "cpu_baseline": None,
     }
     ctx.close()

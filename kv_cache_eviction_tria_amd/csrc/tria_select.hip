@@ -43,7 +43,7 @@ constexpr float kBinScale = 128.0f;  // bins per unit of agg
 constexpr int kListCap = 2048;
 // rows per thread whose loads are in flight together (fewer for wide rows)
 template <int GV>
-constexpr int kBatchRows = GV >= 8 ? 4 : 8;
+constexpr int kBatchRows = GV >= 8 ? 2 : 8;
 // Loops over a thread's rows are fully unrolled when its keys live in registers.
 template <int RPT>
 constexpr int kRowUnroll = RPT <= 32 ? RPT : 4;
@@ -139,16 +139,41 @@ __device__ __forceinline__ float f4_get(const float4& v, int q) {
     return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
 }
 
+// Per-head z-normalisation constants: mu as an unevaluated sum of two floats
+// (hi + lo) and 1/sigma.  z = ((s - hi) - lo) * isg in fp32: the subtraction
+// removes the head's common offset first, so z keeps ~1e-6 relative accuracy.
+struct HeadNorm {
+    float hi, lo, isg;
+};
+
+__device__ __forceinline__ float uniform_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+template <int GV>
+struct Norms {
+    HeadNorm h[GV == 0 ? 1 : GV];
+    // GV > 0: the group's constants held in scalar registers
+    __device__ __forceinline__ void load(const HeadNorm* sh) {
+        if constexpr (GV > 0) {
+#pragma unroll
+            for (int i = 0; i < GV; ++i)
+                h[i] = HeadNorm{uniform_f(sh[i].hi), uniform_f(sh[i].lo), uniform_f(sh[i].isg)};
+        }
+    }
+};
+
 template <int GV>
 __device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, int64_t r, int G,
-                                        const double* mu, const double* isg) {
-    double best = -INFINITY;
+                                        const Norms<GV>& nm, const HeadNorm* sh) {
+    float best = -INFINITY;
     bool bad = false;
     if constexpr (GV == 0) {
         for (int h = 0; h < G; ++h) {
             const float s = R[r * G + h];
             if (!isfinite(s)) bad = true;
-            const double z = ((double)s - mu[h]) * isg[h];
+            const HeadNorm c = sh[h];
+            const float z = ((s - c.hi) - c.lo) * c.isg;
             best = (h == 0 || z > best) ? z : best;
         }
     } else {
@@ -156,15 +181,20 @@ __device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, in
         for (int h = 0; h < GV; ++h) {
             const float s = f4_get(x.v[h >> 2], h & 3);
             if (!isfinite(s)) bad = true;
-            const double z = ((double)s - mu[h]) * isg[h];
+            const float z = ((s - nm.h[h].hi) - nm.h[h].lo) * nm.h[h].isg;
             best = (h == 0 || z > best) ? z : best;
         }
     }
-    return bad ? -INFINITY : (float)best;
+    return bad ? -INFINITY : best + 0.0f;
 }
 
+// With the bins in registers (up to 32K rows) the kernel fits 64 registers, so
+// two 1024-thread workgroups share a CU and 512 units are selected at once.
+template <int RPT>
+constexpr int kSelWavesPerEU = RPT <= 32 ? 8 : 4;
+
 template <int RPT, int GV>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSelWavesPerEU<RPT>))) void select_kernel(
     Batch b, int units_per_seq, int G, const float* __restrict__ raw,
     const PartRec* __restrict__ part, int32_t* __restrict__ keep, float* __restrict__ agg_out,
     uint32_t* __restrict__ key_scratch, int32_t* __restrict__ chunk_pb, uint32_t* ticket) {
@@ -185,7 +215,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int64_t tiles = part_tiles(n);
     const PartRec* __restrict__ P = part + (sd.part_off + (int64_t)uu * tiles) * G;
 
-    __shared__ double mu_sh[64], isg_sh[64];
+    __shared__ HeadNorm norm_sh[64];
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t list[kListCap];
     __shared__ uint32_t rhist[kWaves][256];
@@ -222,18 +252,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         m2 = wave_sum_f64(m2);
         if (lane == 0) {
             const double var = c > 0.0 ? m2 / c : 0.0;
-            mu_sh[h] = mu;
-            isg_sh[h] = var > 0.0 ? 1.0 / sqrt(var) : 0.0;
+            const float hi = (float)mu;
+            norm_sh[h] = HeadNorm{hi, (float)(mu - (double)hi), var > 0.0 ? (float)(1.0 / sqrt(var)) : 0.0f};
         }
     }
     for (int i = t; i < kBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
+    Norms<GV> nrm;
+    nrm.load(norm_sh);
 
     // 2. aggregated score -> key, histogram of the candidates
     const int cand_lo = (int)sd.s_end, n_cand = (int)(sd.w_start - sd.s_end);
     // candidates: rows [s_end, w_start) (all below n)
     auto is_cand = [&](int r) -> bool { return (unsigned)(r - cand_lo) < (unsigned)n_cand; };
-    uint32_t key[kRegKeys ? RPT : 1];
+    // kRegKeys: each row's histogram bin stays in registers (two per word) and
+    // the full key is recomputed from the raw scores for the few rows that
+    // need it (those in the cutoff bin); otherwise keys go to global scratch.
+    uint32_t binw[kRegKeys ? (RPT + 1) / 2 : 1];
+#pragma unroll
+    for (int i = 0; i < (kRegKeys ? (RPT + 1) / 2 : 1); ++i) binw[i] = 0;
     constexpr int kBatch = kBatchRows<GV>;
     constexpr int kNB = (RPT + kBatch - 1) / kBatch;
     constexpr int kUB = kRegKeys ? kNB : 1;
@@ -250,21 +287,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const int j = j0 + q;
             if (j >= RPT) break;
             const int r = row_of(j);
-            uint32_t kk = 0;
             if (r < n) {
-                const float a = agg_of<GV>(x[q], R, r, G, mu_sh, isg_sh);
+                const float a = agg_of<GV>(x[q], R, r, G, nrm, norm_sh);
                 if (AG) AG[r] = a;
-                kk = order_key(a);
-                if (is_cand(r)) atomicAdd(&hist[bin_of(a)], 1u);
-                if constexpr (!kRegKeys) KS[r] = kk;
+                const int bn = bin_of(a);
+                if (is_cand(r)) atomicAdd(&hist[bn], 1u);
+                if constexpr (kRegKeys) binw[j >> 1] |= (uint32_t)bn << (16 * (j & 1));
+                else KS[r] = order_key(a);
             }
-            if constexpr (kRegKeys) key[j] = kk;
         }
     }
     __syncthreads();
+    // the key of row r recomputed exactly as above
+    auto key_at = [&](int r) -> uint32_t {
+        RowLoad<GV> x;
+        load_row<GV>(x, R, r);
+        return order_key(agg_of<GV>(x, R, r, G, nrm, norm_sh));
+    };
     auto get_key = [&](int j) -> uint32_t {
-        if constexpr (kRegKeys) return key[j];
-        else return row_of(j) < n ? KS[row_of(j)] : 0u;
+        const int r = row_of(j);
+        if (r >= n) return 0u;
+        if constexpr (kRegKeys) return key_at(r);
+        else return KS[r];
+    };
+    auto bin_j = [&](int j) -> int {
+        if constexpr (kRegKeys) return (int)((binw[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+        else return bin_of(key_value(get_key(j)));
     };
 
     // 3. threshold: the k-th largest candidate key T; krem rows equal to T are taken
@@ -272,8 +320,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const bool radix = k_take > 0 && k_take < n_cand;
     const bool take_all = k_take >= n_cand;
     uint32_t T = 0;
-    int krem = 0;
+    int krem = 0, bstar = -1;
     bool rank_ties = false;
+    constexpr int kMW = (RPT + 31) / 32;
+    uint32_t cutw[kMW];
+#pragma unroll
+    for (int q = 0; q < kMW; ++q) cutw[q] = 0;
     if (radix) {
         // bins from the top: thread t holds bins kBins-1-2t and kBins-2-2t
         const int b0 = kBins - 1 - 2 * t, b1 = b0 - 1;
@@ -293,18 +345,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         if (t == 0) found_sh[2] = 0;
         __syncthreads();
-        const int bstar = found_sh[0], kb = found_sh[1];
+        bstar = found_sh[0];
+        const int kb = found_sh[1];
         const int cb = (int)hist[bstar];
+        // the candidates in the cutoff bin, one bit per owned row
+#pragma unroll kRowUnroll<RPT>
+        for (int j = 0; j < RPT; ++j)
+            if (is_cand(row_of(j)) && bin_j(j) == bstar) cutw[j >> 5] |= 1u << (j & 31);
         if (cb <= kListCap) {
             // the bin's keys into LDS, then the kb-th largest by counting
-#pragma unroll kRowUnroll<RPT>
-            for (int j = 0; j < RPT; ++j) {
-                const int r = row_of(j);
-                if (is_cand(r)) {
-                    const uint32_t kk = get_key(j);
-                    if (bin_of(key_value(kk)) == bstar) list[atomicAdd(&found_sh[2], 1)] = kk;
-                }
-            }
+            for (int w = 0; w < kMW; ++w)
+                for (uint32_t m = cutw[w]; m; m &= m - 1)
+                    list[atomicAdd(&found_sh[2], 1)] = get_key(w * 32 + __ffs(m) - 1);
             __syncthreads();
             for (int i = t; i < cb; i += kSelThreads) {
                 const uint32_t ki = list[i];
@@ -333,11 +385,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 const int shift = 24 - 8 * pass;
                 for (int i = lane; i < 256; i += 64) rhist[wid][i] = 0;
                 __syncthreads();
-#pragma unroll kRowUnroll<RPT>
+                // (rare: a cutoff bin too large for LDS) keys recomputed per pass
+#pragma unroll 1
                 for (int j = 0; j < RPT; ++j) {
                     const int r = row_of(j);
-                    const uint32_t kk = get_key(j);
-                    const bool act = is_cand(r) && ((kk & mask) == prefix);
+                    const bool c = is_cand(r);
+                    const uint32_t kk = c ? get_key(j) : 0u;
+                    const bool act = c && ((kk & mask) == prefix);
                     hist_add(rhist[wid], act, (kk >> shift) & 255u);
                 }
                 __syncthreads();
@@ -415,31 +469,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         __syncthreads();
     };
-    // keep decision bits, one per owned row
-    uint32_t kbits[(RPT + 31) / 32];
+    // keep decision bits, one per owned row; tie bits for rows equal to T
+    uint32_t kbits[kMW], tiew[kMW];
 #pragma unroll
-    for (int q = 0; q < (RPT + 31) / 32; ++q) kbits[q] = 0;
+    for (int q = 0; q < kMW; ++q) kbits[q] = tiew[q] = 0;
     auto set_keep = [&](int j) { kbits[j >> 5] |= 1u << (j & 31); };
 #pragma unroll kRowUnroll<RPT>
     for (int j = 0; j < RPT; ++j) {
         const int r = row_of(j);
         if (r >= n) continue;
-        if (!is_cand(r) || take_all) {
-            set_keep(j);
-        } else if (radix) {
-            const uint32_t kk = get_key(j);
-            if (kk > T || (kk == T && !rank_ties)) set_keep(j);
-        }
+        // bins are monotone in the key: above the cutoff bin means above T
+        if (!is_cand(r) || take_all || (radix && bin_j(j) > bstar)) set_keep(j);
+    }
+    if (radix) {
+        // rows of the cutoff bin compare their keys with T
+        for (int w = 0; w < kMW; ++w)
+            for (uint32_t m = cutw[w]; m; m &= m - 1) {
+                const int j = w * 32 + __ffs(m) - 1;
+                const uint32_t kk = get_key(j);
+                if (kk > T || (kk == T && !rank_ties)) kbits[w] |= 1u << (j & 31);
+                else if (kk == T) tiew[w] |= 1u << (j & 31);
+            }
     }
     if (rank_ties) {
-        ordered_ranks(
-            [&](int j) {
-                const int r = row_of(j);
-                return is_cand(r) && get_key(j) == T;
-            },
-            [&](int j, int rank) {
-                if (rank < krem) set_keep(j);
-            });
+        ordered_ranks([&](int j) { return ((tiew[j >> 5] >> (j & 31)) & 1u) != 0; },
+                      [&](int j, int rank) {
+                          if (rank < krem) set_keep(j);
+                      });
     }
     ordered_ranks([&](int j) { return ((kbits[j >> 5] >> (j & 31)) & 1u) != 0; },
                   [&](int j, int rank) {
