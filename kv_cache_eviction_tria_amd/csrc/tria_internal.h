@@ -55,14 +55,16 @@ struct CacheView {
 };
 
 // Moment partials: the raw scores of a unit are summarised per tile of
-// kPartRows rows (one wavefront) and per query head as {finite count c, shift
-// a (the tile's first finite score), sum of d = s - a, sum of d^2} in fp32
-// (exact for equal scores; d is small against the scores' common offset),
-// record ((part_off + unit*tiles + tile)*G + head).  The selector forms the
+// kPartRows rows and per query head as {finite count c, shift a (the tile's
+// first finite score), sum of d = s - a, sum of d^2} in fp32 (exact for equal
+// scores; d is small against the scores' common offset), record
+// ((part_off + unit*tiles + tile)*G + head).  One wavefront summarises a tile:
+// lane i holds rows i, i + 64, i + 128 and i + 192.  The selector forms the
 // tile mean m = a + sum(d)/c and M2 = sum(d^2) - sum(d)^2/c, then merges the
 // tiles exactly in fp64:  N = sum c_t,  mu = sum c_t m_t / N,
 // M2 = sum (M2_t + c_t (m_t - mu)^2).
-constexpr int kPartRows = 64;
+constexpr int kPartRows = 256;
+constexpr int kPartLaneRows = kPartRows / 64;
 struct PartRec {
     float cnt, shift, sum, sumsq;
 };
@@ -110,25 +112,49 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Moment partial of one wavefront's rows for NH heads: lane i holds row i's
-// scores s[] (valid[] false for rows past the end and non-finite scores).
-// Lane 0 writes head j's record to out[j] for j < nh.
+// Moment partial of one wavefront's tile for NH heads, fed one 64-row slice
+// at a time in row order: lane i holds row i of the slice in s[] (valid[]
+// false for rows past the end and non-finite scores).  The shift is the
+// tile's first finite score, so counts and shifts are wavefront-uniform.
 template <int NH>
-__device__ __forceinline__ void wave_moments(const float (&s)[NH], const bool (&valid)[NH],
-                                             PartRec* out, int nh = NH) {
-    const int lane = threadIdx.x & 63;
+struct WaveMoments {
+    float shift[NH], sd[NH], sq[NH];
+    int cnt[NH];
+    __device__ __forceinline__ WaveMoments() {
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
-        const uint64_t m = __ballot(valid[j]);
-        const int first = m ? __ffsll((unsigned long long)m) - 1 : 0;
-        const float a = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s[j]), first));
-        const float d = valid[j] ? s[j] - a : 0.0f;
-        const float sd = wave_sum_f32(d);
-        const float sq = wave_sum_f32(d * d);
-        if (lane == 0 && j < nh) out[j] = PartRec{(float)__popcll(m), m ? a : 0.0f, sd, sq};
+        for (int j = 0; j < NH; ++j) {
+            shift[j] = 0.0f;
+            sd[j] = 0.0f;
+            sq[j] = 0.0f;
+            cnt[j] = 0;
+        }
     }
-}
+    __device__ __forceinline__ void add(const float (&s)[NH], const bool (&valid)[NH]) {
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+            const uint64_t m = __ballot(valid[j]);
+            if (cnt[j] == 0 && m) {
+                const int first = __ffsll((unsigned long long)m) - 1;
+                shift[j] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s[j]), first));
+            }
+            cnt[j] += __popcll(m);
+            const float d = valid[j] ? s[j] - shift[j] : 0.0f;
+            sd[j] += d;
+            sq[j] = fmaf(d, d, sq[j]);
+        }
+    }
+    // Lane 0 writes head j's record to out[j] for j < nh.
+    __device__ __forceinline__ void emit(PartRec* out, int nh = NH) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+            const float a = wave_sum_f32(sd[j]);
+            const float b = wave_sum_f32(sq[j]);
+            if (lane == 0 && j < nh) out[j] = PartRec{(float)cnt[j], shift[j], a, b};
+        }
+    }
+};
 
 // Mean and M2 of a tile record (fp64).
 __device__ __forceinline__ void part_stats(const PartRec& p, double* mean, double* m2) {

@@ -9,8 +9,9 @@
 // the G query heads of the row's KV head (llama.cpp page "TriAttention
 // KV-Cache Eviction (--triattention)", section 5 "Phase C").
 //
-// Mapping: one lane per cached row, 256 rows per workgroup.  Every lane of a wave needs the same coefficient at
-// the same time, so the unit's table (built by prep) is read through scalar
+// Mapping: one lane per cached row at a time; a wavefront scores a tile of 256
+// rows (four per lane), 1024 rows per workgroup.  Every lane of a wave needs
+// the same coefficient at the same time, so the unit's table (built by prep) is read through scalar
 // loads into SGPRs and fed to the VALU as the scalar operand; no LDS and no
 // cross-lane reduction.  Each lane reads its whole row with wide loads; one
 // load instruction touches a cache line per lane and the following loads of
@@ -90,26 +91,40 @@ __device__ __forceinline__ void store_scores(float* dst, const float (&acc)[GT],
     }
 }
 
-// Moment partials of this wavefront's rows for heads j0 .. j0+GT-1.
+// First row of this wavefront's tile: each wavefront scores kPartRows rows,
+// lane i taking rows i, i + 64, ... (each load instruction still covers 64
+// consecutive rows), so the per-wavefront set-up and the moment reduction are
+// paid once per kPartRows rows.
+__device__ __forceinline__ int64_t wave_tile() {
+    return (int64_t)blockIdx.x * (kScoreThreads / 64) + (threadIdx.x >> 6);
+}
+
+// Moment partial of this wavefront's tile for heads j0 .. j0+GT-1.
 template <int GT>
-__device__ __forceinline__ void emit_moments(const float (&acc)[GT], bool in_range,
-                                             const SeqDesc& sd, const UnitId& id, int Hkv,
-                                             int64_t n, int G, int j0, PartRec* part) {
-    const int64_t wtile = (int64_t)blockIdx.x * (kScoreThreads / kPartRows) + (threadIdx.x >> 6);
-    if (wtile * kPartRows >= n) return;  // the unit has no row in this wavefront
+__device__ __forceinline__ void emit_moments(const WaveMoments<GT>& mom, const SeqDesc& sd,
+                                             const UnitId& id, int Hkv, int64_t n, int G, int j0,
+                                             PartRec* part) {
+    const int64_t tile = sd.part_off + ((int64_t)id.l * Hkv + id.g) * part_tiles(n) + wave_tile();
+    mom.emit(part + tile * G + j0);
+}
+
+template <int GT>
+__device__ __forceinline__ void add_moments(WaveMoments<GT>& mom, const float (&acc)[GT],
+                                            bool in_range) {
     bool valid[GT];
 #pragma unroll
     for (int j = 0; j < GT; ++j) valid[j] = in_range && isfinite(acc[j]);
-    const int64_t tile = sd.part_off + ((int64_t)id.l * Hkv + id.g) * part_tiles(n) + wtile;
-    wave_moments<GT>(acc, valid, part + tile * G + j0);
+    mom.add(acc, valid);
 }
 
 // Pieces an fp16 row is walked in: the fewest that divide its HD/16 chunks per
-// half-row into groups of at most 4 (16 registers per half-row piece).
+// half-row into groups of at most 8 (one 128-byte line per half-row piece, 32
+// registers).  Smaller pieces read each line in two visits, and the line is
+// often gone from L2 by the second: HBM traffic rose to 1.8x the row bytes.
 constexpr int f16_pieces(int hd) {
     const int c = hd / 16;
     for (int p = 1; p <= c; ++p)
-        if (c % p == 0 && c / p <= 4) return p;
+        if (c % p == 0 && c / p <= 8) return p;
     return c;
 }
 
@@ -123,17 +138,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
     const int u = blockIdx.y;
     const UnitId id = unit_id(cv, u);
     const int64_t n = b.seq[id.seq].n;
-    const int64_t tile0 = (int64_t)blockIdx.x * kScoreThreads;
-    if (tile0 >= n) return;
+    const int64_t wbase = wave_tile() * kPartRows;
+    if (wbase >= n) return;
     const float* __restrict__ C = coef + coef_unit(b, cv, id) * coef_words + j0 * F * 3;
     float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + j0;
     const bool packed = (G == GT);
+    WaveMoments<GT> mom;
 
-    {
-        const int64_t base = tile0;
+#pragma unroll 1
+    for (int it = 0; it < kPartLaneRows; ++it) {
+        const int64_t r0 = wbase + it * 64;
+        if (r0 >= n) break;
         // Lanes past the end recompute the last row and skip the store, so the
         // whole wave runs one straight-line body.
-        const int64_t r_out = base + threadIdx.x;
+        const int64_t r_out = r0 + (threadIdx.x & 63);
         const int64_t r = r_out < n ? r_out : n - 1;
         // Re-read the coefficients through the scalar cache on every pass: the
         // offset is zero but opaque to the compiler, so it cannot hoist hundreds
@@ -181,8 +199,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_f16_kernel(
             }
         }
         if (r_out < n) store_scores<GT>(rout + r_out * G, acc, packed);
-        if (part) emit_moments<GT>(acc, r_out < n, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
+        if (part) add_moments<GT>(mom, acc, r_out < n);
     }
+    if (part) emit_moments<GT>(mom, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
 }
 
 template <int HD, int GT>
@@ -197,8 +216,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     const int u = blockIdx.y;
     const UnitId id = unit_id(cv, u);
     const int64_t n = b.seq[id.seq].n;
-    const int64_t tile0 = (int64_t)blockIdx.x * kScoreThreads;
-    if (tile0 >= n) return;
+    const int64_t wbase = wave_tile() * kPartRows;
+    if (wbase >= n) return;
     const CoefGeom cg = coef_geom(TRIA_KV_Q8_0, HD, G);
     const int32_t* __restrict__ T = coef + coef_unit(b, cv, id) * coef_words;
     const int32_t* __restrict__ HI = T + cg.hi_off + j0 * W;
@@ -207,10 +226,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     const float* __restrict__ WT = reinterpret_cast<const float*>(T + cg.w_off) + j0 * F;
     float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + j0;
     const bool packed = (G == GT);
+    WaveMoments<GT> mom;
 
-    {
-        const int64_t base = tile0;
-        const int64_t r_out = base + threadIdx.x;
+#pragma unroll 1
+    for (int it = 0; it < kPartLaneRows; ++it) {
+        const int64_t r0 = wbase + it * 64;
+        if (r0 >= n) break;
+        const int64_t r_out = r0 + (threadIdx.x & 63);
         const int64_t r = r_out < n ? r_out : n - 1;
         // see score_f16_kernel: keep the tables in the scalar path
         const int z = opaque_zero_s();
@@ -294,8 +316,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
             for (int j = 0; j < GT; ++j) acc[j] = fmaf(WT[z + f * GT + j], mag, acc[j]);
         }
         if (r_out < n) store_scores<GT>(rout + r_out * G, acc, packed);
-        if (part) emit_moments<GT>(acc, r_out < n, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
+        if (part) add_moments<GT>(mom, acc, r_out < n);
     }
+    if (part) emit_moments<GT>(mom, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
 }
 
 template <int HD, int GT>
@@ -350,12 +373,12 @@ Runner pick_runner(int k_type, int hd, int gt) {
 
 hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_type, int G,
                         int hd, const int32_t* coef, float* raw, PartRec* part, hipStream_t s) {
-    static_assert(kPartRows == 64, "one moment partial per score wavefront");
     int64_t max_n = 0;
     for (int i = 0; i < b.n_seq; ++i) max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
     if (max_n <= 0 || n_units <= 0) return hipSuccess;
-    // one row per lane, 256 rows per workgroup
-    const int64_t tiles = (max_n + kScoreThreads - 1) / kScoreThreads;
+    // one moment tile per wavefront, kPartRows / 64 rows per lane
+    const int64_t rows_per_block = (int64_t)(kScoreThreads / 64) * kPartRows;
+    const int64_t tiles = (max_n + rows_per_block - 1) / rows_per_block;
     const dim3 grid((unsigned)tiles, (unsigned)n_units);
     const CoefGeom cg = coef_geom(k_type, hd, G);
     for (int j0 = 0; j0 < G;) {

@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
 }
 
 // Moment partials of caller-provided raw scores (the scorer writes them
-// itself during a whole pass): one wavefront per tile of 64 rows.
+// itself during a whole pass): one wavefront per tile of kPartRows rows.
 constexpr int kMomThreads = 256;
 __global__ __launch_bounds__(kMomThreads) void moments_kernel(Batch b, int units_per_seq, int G,
                                                               const float* __restrict__ raw,
@@ -522,20 +522,24 @@ __global__ __launch_bounds__(kMomThreads) void moments_kernel(Batch b, int units
     const int uu = u - seq * units_per_seq;
     const SeqDesc sd = b.seq[seq];
     const int64_t n = sd.n;
-    const int64_t tile = (int64_t)blockIdx.x * (kMomThreads / kPartRows) + (threadIdx.x >> 6);
+    const int64_t tile = (int64_t)blockIdx.x * (kMomThreads / 64) + (threadIdx.x >> 6);
     if (tile * kPartRows >= n) return;  // whole wavefront past the end
     const float* __restrict__ R = raw + sd.raw_off + (int64_t)uu * n * G;
     PartRec* out = part + (sd.part_off + (int64_t)uu * part_tiles(n) + tile) * G;
-    const int64_t r = tile * kPartRows + (threadIdx.x & 63);
     for (int h0 = 0; h0 < G; h0 += 4) {
-        float s[4];
-        bool v[4];
+        WaveMoments<4> mom;
+        for (int i = 0; i < kPartLaneRows; ++i) {
+            const int64_t r = tile * kPartRows + i * 64 + (threadIdx.x & 63);
+            float s[4];
+            bool v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s[q] = (r < n && h0 + q < G) ? R[r * G + h0 + q] : 0.0f;
-            v[q] = r < n && h0 + q < G && isfinite(s[q]);
+            for (int q = 0; q < 4; ++q) {
+                s[q] = (r < n && h0 + q < G) ? R[r * G + h0 + q] : 0.0f;
+                v[q] = r < n && h0 + q < G && isfinite(s[q]);
+            }
+            mom.add(s, v);
         }
-        wave_moments<4>(s, v, out + h0, G - h0 < 4 ? G - h0 : 4);
+        mom.emit(out + h0, G - h0 < 4 ? G - h0 : 4);
     }
 }
 
@@ -583,7 +587,8 @@ hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float*
     int64_t max_n = 0;
     for (int i = 0; i < b.n_seq; ++i) max_n = b.seq[i].n > max_n ? b.seq[i].n : max_n;
     if (max_n <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((max_n + kMomThreads - 1) / kMomThreads),
+    const int64_t rows_per_block = (int64_t)(kMomThreads / 64) * kPartRows;
+    const dim3 grid((unsigned)((max_n + rows_per_block - 1) / rows_per_block),
                     (unsigned)(units_per_seq * b.n_seq));
     hipLaunchKernelGGL(moments_kernel, grid, dim3(kMomThreads), 0, s, b, units_per_seq, G, raw,
                        part);
