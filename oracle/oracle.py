@@ -13,6 +13,10 @@ the passages of the source pages each step follows:
 * llama.cpp docs "TriAttention KV-Cache Eviction (--triattention)" --
   protect / sort / evict / compact (section 5, "Phase B") and per-head
   z-normalisation followed by a max over the GQA group (section 5, "Phase C").
+* Shared keep sets (one per KV head across layers, or one for the whole
+  cache): the worklog's per-head keep sets gathered in every layer and the
+  llama.cpp page's global z-normalisation shader; the cross-unit reduction is
+  read as the GQA group's max taken over the larger group.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force and hand-worked fixtures.  One reading is not pinned by
@@ -30,6 +34,11 @@ import numpy as np
 
 KV_F16 = 0
 KV_Q8_0 = 1
+
+# keep-set sharing (tria_oracle.c, orc_evict_mode)
+KEEP_UNIT = 0      # each (layer, KV head) unit selects on its own
+KEEP_KV_HEAD = 1   # one keep set per KV head, shared by all layers
+KEEP_GLOBAL = 2    # one keep set for the whole cache
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tria_oracle.c")
@@ -81,6 +90,8 @@ def _load():
             lib.orc_evict.restype = i64
             lib.orc_evict.argtypes = [i32, i32, i32, i32, i32, i32, dbl, vp, i32, vp, vp, vp,
                                       i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32]
+            lib.orc_evict_mode.restype = i64
+            lib.orc_evict_mode.argtypes = [i32] + lib.orc_evict.argtypes
             lib.orc_num_threads.restype = i32
             lib.orc_num_threads.argtypes = []
             _lib = lib
@@ -185,10 +196,13 @@ def compact_rows(rows: np.ndarray, keep_idx: np.ndarray) -> np.ndarray:
 
 def evict(k_type: int, v_type: int, L: int, Hkv: int, Hq: int, hd: int, theta: float, offsets,
           k: np.ndarray, v: np.ndarray, pos: np.ndarray, n: int, budget: int, sink: int,
-          window: int, q_re, q_im, w, want_raw=True, want_agg=True, compact=True):
+          window: int, q_re, q_im, w, want_raw=True, want_agg=True, compact=True,
+          keep_mode: int = KEEP_UNIT):
     """Whole pass over a contiguous host cache [L][Hkv][cap][row] (in place).
 
-    Returns dict(kept, keep_idx [L,Hkv,K], raw [L,Hkv,n,G] or None, agg or None).
+    keep_mode: KEEP_UNIT, KEEP_KV_HEAD or KEEP_GLOBAL (who shares a keep set).
+    Returns dict(kept, keep_idx [L,Hkv,K], raw [L,Hkv,n,G] or None, agg
+    [L,Hkv,n] -- the score each unit's keep set was selected on -- or None).
     """
     assert k.flags.c_contiguous and v.flags.c_contiguous and pos.flags.c_contiguous
     cap = pos.shape[-1]
@@ -201,9 +215,10 @@ def evict(k_type: int, v_type: int, L: int, Hkv: int, Hq: int, hd: int, theta: f
     agg = np.empty((L, Hkv, n), np.float64) if want_agg else None
     q_re, q_im, w = (_c(x, np.float32) for x in (q_re, q_im, w))
     offs = _c(offsets, np.int64)
-    rc = _load().orc_evict(k_type, v_type, L, Hkv, Hq, hd, float(theta), _p(offs), len(offs),
-                           _p(k), _p(v), _p(pos), cap, n, budget, sink, window, _p(q_re),
-                           _p(q_im), _p(w), _p(keep), _p(raw), _p(agg), 1 if compact else 0)
+    rc = _load().orc_evict_mode(int(keep_mode), k_type, v_type, L, Hkv, Hq, hd, float(theta),
+                                _p(offs), len(offs), _p(k), _p(v), _p(pos), cap, n, budget,
+                                sink, window, _p(q_re), _p(q_im), _p(w), _p(keep), _p(raw),
+                                _p(agg), 1 if compact else 0)
     if rc < 0:
         raise RuntimeError("oracle evict failed")
     return {"kept": int(rc), "keep_idx": keep[:, :, :K], "raw": raw, "agg": agg}

@@ -335,58 +335,142 @@ int orc_compact_rows(uint8_t *rows, int64_t row_bytes, const int32_t *keep_idx, 
 /* Whole pass over a contiguous cache [L][Hkv][cap][row].                     */
 /* ------------------------------------------------------------------------ */
 
-/* One eviction pass over every (layer, KV head) unit, each unit on its own.
+/* Keep-set sharing.  ORC_KEEP_UNIT: every (layer, KV head) unit selects on its
+ * own.  ORC_KEEP_KV_HEAD: one keep set per KV head, shared by all layers ([WL]
+ * "Later correction: selector and compaction are now cleared ...": keep sets
+ * compared per head, 8 of 8, and one per-head index list gathered in all 36
+ * layers; the worklog names a cross-layer aggregation step).  ORC_KEEP_GLOBAL:
+ * one keep set for the whole cache ([LC] section 5, "Phase C", the global
+ * z-normalisation shader; the cache's cells hold every layer and head).
+ * Neither page writes out the cross-unit reduction; it is read as the same
+ * rule as the GQA group's: every member query head is z-normalised over its
+ * own unit's rows, and the group score of a row is the max of those z-scores
+ * over all member heads (-inf if any member score is not finite). */
+#define ORC_KEEP_UNIT 0
+#define ORC_KEEP_KV_HEAD 1
+#define ORC_KEEP_GLOBAL 2
+
+/* Group of unit (l, g) and number of groups under a keep mode. */
+static int orc_n_groups(int mode, int L, int Hkv)
+{
+    return mode == ORC_KEEP_UNIT ? L * Hkv : (mode == ORC_KEEP_KV_HEAD ? Hkv : 1);
+}
+static int orc_group_of(int mode, int Hkv, int u)
+{
+    return mode == ORC_KEEP_UNIT ? u : (mode == ORC_KEEP_KV_HEAD ? u % Hkv : 0);
+}
+
+/* One eviction pass over every (layer, KV head) unit.
+ *   keep_mode : ORC_KEEP_UNIT, ORC_KEEP_KV_HEAD or ORC_KEEP_GLOBAL.
  *   k, v, pos : host copies, [L][Hkv][cap] rows; compacted in place.
  *   q_re, q_im, w : statistics [L][Hq][F]; query head h = g*G + j belongs to
  *                   KV head g (contiguous GQA grouping).
- *   keep_idx  : output [L][Hkv][K] (may be NULL)
+ *   keep_idx  : output [L][Hkv][K] (may be NULL); a shared keep set is written
+ *               for every member unit.
  *   raw       : output [L][Hkv][n][G] (may be NULL)
- *   agg       : output [L][Hkv][n]   (may be NULL)
+ *   agg       : output [L][Hkv][n] (may be NULL): the score the unit's keep set
+ *               was selected on (its group's score under a shared mode).
  * Returns the kept count K, or -1. */
+int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, int Hq, int hd,
+                       double theta, const int64_t *offsets, int n_off, uint8_t *k, uint8_t *v,
+                       int32_t *pos, int64_t cap, int64_t n, int64_t budget, int64_t sink,
+                       int64_t window, const float *q_re, const float *q_im, const float *w,
+                       int32_t *keep_idx, double *raw, double *agg, int do_compact)
+{
+    int G = Hq / Hkv;
+    int F = hd / 2;
+    int U = L * Hkv;
+    int64_t kb = orc_row_bytes(k_type, hd), vb = orc_row_bytes(v_type, hd);
+    int64_t K = orc_kept_count(n, budget, sink, window);
+    if (K < 0 || kb < 0 || vb < 0 || n > cap) return -1;
+    if (keep_mode < ORC_KEEP_UNIT || keep_mode > ORC_KEEP_GLOBAL) return -1;
+    int NG = orc_n_groups(keep_mode, L, Hkv);
+    int64_t nn = n > 0 ? n : 1;
+    double *rs = raw ? raw : (double *)malloc(sizeof(double) * (size_t)(U * nn * G));
+    double *ua = (double *)malloc(sizeof(double) * (size_t)(U * nn)); /* per-unit GQA max */
+    double *ga = (double *)malloc(sizeof(double) * (size_t)(NG * nn)); /* group score */
+    int32_t *gk = (int32_t *)malloc(sizeof(int32_t) * (size_t)(NG * nn));
+    int failed = !rs || !ua || !ga || !gk;
+    if (!failed && n > 0) {
+        /* 1. raw scores and the unit's z-normalised GQA max */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int u = 0; u < U; u++) {
+            int l = u / Hkv, g = u % Hkv;
+            uint8_t *ku = k + (int64_t)u * cap * kb;
+            int32_t *pu = pos + (int64_t)u * cap;
+            int64_t stat = ((int64_t)l * Hq + (int64_t)g * G) * F;
+            int64_t p = pu[n - 1];
+            int bad = orc_raw_scores_unit(k_type, ku, kb, n, hd, G, q_re + stat, q_im + stat,
+                                          w + stat, theta, p, offsets, n_off,
+                                          rs + (int64_t)u * n * G);
+            orc_aggregate_unit(rs + (int64_t)u * n * G, n, G, ua + (int64_t)u * n, NULL, NULL);
+            if (bad) {
+#pragma omp atomic write
+                failed = 1;
+            }
+        }
+        /* 2. group score: max over the member units' z-maxima (a unit's value is
+         *    -inf exactly when one of its head scores is not finite, and then the
+         *    group's is -inf too) */
+        for (int64_t i = 0; i < (int64_t)NG * n; i++) ga[i] = 0.0;
+        for (int gr = 0; gr < NG; gr++) {
+            double *gs = ga + (int64_t)gr * n;
+            int first = 1;
+            for (int u = 0; u < U; u++) {
+                if (orc_group_of(keep_mode, Hkv, u) != gr) continue;
+                const double *us = ua + (int64_t)u * n;
+                for (int64_t r = 0; r < n; r++) {
+                    if (us[r] == -INFINITY || (!first && gs[r] == -INFINITY)) gs[r] = -INFINITY;
+                    else if (first || us[r] > gs[r]) gs[r] = us[r];
+                }
+                first = 0;
+            }
+        }
+        /* 3. one selection per group */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int gr = 0; gr < NG; gr++) {
+            if (orc_select_unit(ga + (int64_t)gr * n, n, budget, sink, window,
+                                gk + (int64_t)gr * nn) != K) {
+#pragma omp atomic write
+                failed = 1;
+            }
+        }
+        /* 4. every unit gathers its rows with its group's keep set */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int u = 0; u < U; u++) {
+            int gr = orc_group_of(keep_mode, Hkv, u);
+            const int32_t *ki = gk + (int64_t)gr * nn;
+            int bad = 0;
+            if (keep_idx) memcpy(keep_idx + (int64_t)u * K, ki, sizeof(int32_t) * (size_t)K);
+            if (agg) memcpy(agg + (int64_t)u * n, ga + (int64_t)gr * n, sizeof(double) * (size_t)n);
+            if (do_compact && !failed) {
+                bad |= orc_compact_rows(k + (int64_t)u * cap * kb, kb, ki, K);
+                bad |= orc_compact_rows(v + (int64_t)u * cap * vb, vb, ki, K);
+                bad |= orc_compact_rows((uint8_t *)(pos + (int64_t)u * cap), 4, ki, K);
+            }
+            if (bad) {
+#pragma omp atomic write
+                failed = 1;
+            }
+        }
+    }
+    if (!raw) free(rs);
+    free(ua);
+    free(ga);
+    free(gk);
+    return failed ? -1 : K;
+}
+
+/* The per-unit pass (each unit selects on its own). */
 int64_t orc_evict(int k_type, int v_type, int L, int Hkv, int Hq, int hd, double theta,
                   const int64_t *offsets, int n_off, uint8_t *k, uint8_t *v, int32_t *pos,
                   int64_t cap, int64_t n, int64_t budget, int64_t sink, int64_t window,
                   const float *q_re, const float *q_im, const float *w, int32_t *keep_idx,
                   double *raw, double *agg, int do_compact)
 {
-    int G = Hq / Hkv;
-    int F = hd / 2;
-    int64_t kb = orc_row_bytes(k_type, hd), vb = orc_row_bytes(v_type, hd);
-    int64_t K = orc_kept_count(n, budget, sink, window);
-    if (K < 0 || kb < 0 || vb < 0 || n > cap) return -1;
-    int failed = 0;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int u = 0; u < L * Hkv; u++) {
-        int l = u / Hkv, g = u % Hkv;
-        double *rs = raw ? raw + (int64_t)u * n * G : (double *)malloc(sizeof(double) * (size_t)(n * G + 1));
-        double *ag = agg ? agg + (int64_t)u * n : (double *)malloc(sizeof(double) * (size_t)(n + 1));
-        int32_t *ki = keep_idx ? keep_idx + (int64_t)u * K : (int32_t *)malloc(sizeof(int32_t) * (size_t)(n + 1));
-        uint8_t *ku = k + (int64_t)u * cap * kb;
-        uint8_t *vu = v + (int64_t)u * cap * vb;
-        int32_t *pu = pos + (int64_t)u * cap;
-        int64_t stat = ((int64_t)l * Hq + (int64_t)g * G) * F;
-        int bad = 0;
-        if (n > 0) {
-            int64_t p = pu[n - 1];
-            bad |= orc_raw_scores_unit(k_type, ku, kb, n, hd, G, q_re + stat, q_im + stat,
-                                       w + stat, theta, p, offsets, n_off, rs);
-            orc_aggregate_unit(rs, n, G, ag, NULL, NULL);
-            if (orc_select_unit(ag, n, budget, sink, window, ki) != K) bad = 1;
-            if (do_compact && !bad) {
-                bad |= orc_compact_rows(ku, kb, ki, K);
-                bad |= orc_compact_rows(vu, vb, ki, K);
-                bad |= orc_compact_rows((uint8_t *)pu, 4, ki, K);
-            }
-        }
-        if (!raw) free(rs);
-        if (!agg) free(ag);
-        if (!keep_idx) free(ki);
-        if (bad) {
-#pragma omp atomic write
-            failed = 1;
-        }
-    }
-    return failed ? -1 : K;
+    return orc_evict_mode(ORC_KEEP_UNIT, k_type, v_type, L, Hkv, Hq, hd, theta, offsets, n_off,
+                          k, v, pos, cap, n, budget, sink, window, q_re, q_im, w, keep_idx, raw,
+                          agg, do_compact);
 }
 
 int orc_num_threads(void)

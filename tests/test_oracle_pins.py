@@ -439,3 +439,113 @@ def test_evict_end_to_end_small():
             assert np.array_equal(vb[l, g, :K], v0[l, g, keep])
             assert np.array_equal(pos[l, g, :K], p0[l, g, keep])
             assert np.all(np.diff(pos[l, g, :K]) > 0)
+
+
+# ---------------------------------------------------------------------------
+# Shared keep sets (one per KV head across layers; one for the whole cache)
+# ---------------------------------------------------------------------------
+
+def _shared_case(seed, L, Hkv, Hq, hd, n):
+    rng = np.random.default_rng(seed)
+    F = hd // 2
+    kd = rng.standard_normal((L, Hkv, n, hd)).astype(np.float16)
+    kb = np.ascontiguousarray(kd).view(np.uint8).reshape(L, Hkv, n, 2 * hd).copy()
+    vb = rng.integers(0, 256, size=(L, Hkv, n, 2 * hd), dtype=np.uint8)
+    pos = np.broadcast_to(np.arange(n, dtype=np.int32), (L, Hkv, n)).copy()
+    q_re = rng.standard_normal((L, Hq, F)).astype(np.float32)
+    q_im = rng.standard_normal((L, Hq, F)).astype(np.float32)
+    w = np.abs(rng.standard_normal((L, Hq, F))).astype(np.float32)
+    return kb, vb, pos, q_re, q_im, w
+
+
+def _shared_evict(case, L, Hkv, Hq, hd, n, budget, sink, window, mode, compact=True):
+    kb, vb, pos, q_re, q_im, w = (x.copy() for x in case)
+    out = oracle.evict(oracle.KV_F16, oracle.KV_F16, L, Hkv, Hq, hd, 1e6, [1, 4, 16], kb, vb, pos,
+                       n, budget, sink, window, q_re, q_im, w, compact=compact, keep_mode=mode)
+    return out, kb, vb, pos
+
+
+def test_shared_modes_reduce_to_per_unit():
+    """One layer: the per-KV-head mode is the per-unit mode.  One KV head: the global
+    mode is the per-KV-head mode.  One unit: all three agree."""
+    case = _shared_case(31, 1, 3, 6, 16, 60)
+    a, *ca = _shared_evict(case, 1, 3, 6, 16, 60, 20, 2, 6, oracle.KEEP_UNIT)
+    b, *cb = _shared_evict(case, 1, 3, 6, 16, 60, 20, 2, 6, oracle.KEEP_KV_HEAD)
+    assert np.array_equal(a["keep_idx"], b["keep_idx"]) and np.array_equal(a["agg"], b["agg"])
+    assert all(np.array_equal(x, y) for x, y in zip(ca, cb))
+    case = _shared_case(32, 3, 1, 2, 16, 60)
+    b, *cb = _shared_evict(case, 3, 1, 2, 16, 60, 20, 2, 6, oracle.KEEP_KV_HEAD)
+    c, *cc = _shared_evict(case, 3, 1, 2, 16, 60, 20, 2, 6, oracle.KEEP_GLOBAL)
+    assert np.array_equal(b["keep_idx"], c["keep_idx"]) and np.array_equal(b["agg"], c["agg"])
+    assert all(np.array_equal(x, y) for x, y in zip(cb, cc))
+    case = _shared_case(33, 1, 1, 4, 16, 60)
+    a, *_ = _shared_evict(case, 1, 1, 4, 16, 60, 20, 2, 6, oracle.KEEP_UNIT)
+    c, *_ = _shared_evict(case, 1, 1, 4, 16, 60, 20, 2, 6, oracle.KEEP_GLOBAL)
+    assert np.array_equal(a["keep_idx"], c["keep_idx"])
+
+
+def test_shared_group_score_is_the_max_over_members():
+    """A layer whose keys are all equal has sigma = 0, so its z-scores are 0: the group
+    score of the two-layer KV head is max(z_layer0, 0), not a mean or a sum (those would
+    keep layer 0's order below zero; the max ties every such row at 0, and ties go to
+    the lower row).  The budget reaches below zero, where the two readings part."""
+    L, Hkv, Hq, hd, n = 2, 1, 2, 16, 80
+    case = list(_shared_case(34, L, Hkv, Hq, hd, n))
+    case[0][1] = case[0][1][:, :1]  # layer 1: every key row the same
+    out, *_ = _shared_evict(case, L, Hkv, Hq, hd, n, 60, 3, 8, oracle.KEEP_KV_HEAD,
+                            compact=False)
+    unit, *_ = _shared_evict(case, L, Hkv, Hq, hd, n, 60, 3, 8, oracle.KEEP_UNIT, compact=False)
+    z0 = unit["agg"][0, 0]
+    assert np.all(unit["agg"][1, 0] == 0.0)
+    want = np.maximum(z0, 0.0)
+    assert np.allclose(out["agg"][0, 0], want, rtol=0, atol=0)
+    keep = brute_keep(want, 60, 3, 8)
+    assert out["keep_idx"][0, 0].tolist() == keep and out["keep_idx"][1, 0].tolist() == keep
+    # a mean over the layers would give another keep set on this input
+    assert brute_keep(z0 / 2, 60, 3, 8) != keep
+
+
+def test_shared_nonfinite_score_evicts_the_row_in_every_layer():
+    L, Hkv, Hq, hd, n = 3, 2, 4, 16, 50
+    case = list(_shared_case(35, L, Hkv, Hq, hd, n))
+    k16 = case[0].view(np.float16).reshape(L, Hkv, n, hd)
+    k16[2, 1, 20, 3] = np.float16(np.inf)  # one key element of layer 2, KV head 1, row 20
+    for mode, groups in ((oracle.KEEP_KV_HEAD, [(g,) for g in range(Hkv)]),
+                         (oracle.KEEP_GLOBAL, [tuple(range(Hkv))])):
+        out, *_ = _shared_evict(case, L, Hkv, Hq, hd, n, 40, 2, 4, mode, compact=False)
+        for grp in groups:
+            hit = 1 in grp
+            for l in range(L):
+                for g in grp:
+                    assert (out["agg"][l, g, 20] == -np.inf) == hit
+                    assert (20 in out["keep_idx"][l, g]) == (not hit)
+
+
+def test_shared_members_share_keep_sets_and_gather_exactly():
+    L, Hkv, Hq, hd, n = 3, 2, 4, 16, 70
+    case = _shared_case(36, L, Hkv, Hq, hd, n)
+    kb0, vb0, p0 = case[0], case[1], case[2]
+    for mode in (oracle.KEEP_KV_HEAD, oracle.KEEP_GLOBAL):
+        out, kb, vb, pos = _shared_evict(case, L, Hkv, Hq, hd, n, 25, 2, 5, mode)
+        K = out["kept"]
+        for l in range(L):
+            for g in range(Hkv):
+                ref = out["keep_idx"][0, g if mode == oracle.KEEP_KV_HEAD else 0]
+                keep = out["keep_idx"][l, g]
+                assert np.array_equal(keep, ref)
+                assert np.array_equal(kb[l, g, :K], kb0[l, g, keep])
+                assert np.array_equal(vb[l, g, :K], vb0[l, g, keep])
+                assert np.array_equal(pos[l, g, :K], p0[l, g, keep])
+                assert keep.tolist() == brute_keep(out["agg"][l, g], 25, 2, 5)
+
+
+def test_shared_layer_order_does_not_matter():
+    L, Hkv, Hq, hd, n = 4, 2, 4, 16, 64
+    case = _shared_case(37, L, Hkv, Hq, hd, n)
+    perm = [2, 0, 3, 1]
+    pcase = [x[perm].copy() for x in case]
+    for mode in (oracle.KEEP_KV_HEAD, oracle.KEEP_GLOBAL):
+        a, *_ = _shared_evict(case, L, Hkv, Hq, hd, n, 20, 1, 4, mode, compact=False)
+        b, *_ = _shared_evict(pcase, L, Hkv, Hq, hd, n, 20, 1, 4, mode, compact=False)
+        assert np.array_equal(a["keep_idx"][perm], b["keep_idx"])
+        assert np.array_equal(a["agg"][perm], b["agg"])
