@@ -51,7 +51,13 @@ def parse():
                          "the timed steps, as the byte reference for profiler counters")
     ap.add_argument("--layers-per-group", type=int, default=0,
                     help="tria_set_pipeline: 0 = one group; > 0 = overlapped layer groups")
+    ap.add_argument("--keep-mode", choices=sorted(KEEP_MODES), default="per_unit",
+                    help="tria_set_keep_mode: who shares a keep set")
     return ap.parse_args()
+
+
+# --keep-mode -> (library mode, oracle mode)
+KEEP_MODES = {"per_unit": (0, 0), "per_kv_head": (1, 1), "global": (2, 2)}
 
 
 def measured_traffic(stage, workload):
@@ -127,6 +133,7 @@ def bench_contiguous(args, wl):
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
     tria.tria_set_pipeline(ctx, args.layers_per_group)
+    tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
     K = tria.tria_kept_count(n, B, S, W)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -208,7 +215,7 @@ def bench_contiguous(args, wl):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, stats, k0.cpu().numpy(), v0.cpu().numpy(), p0.cpu().numpy(),
-                           args.cpu_seconds)
+                           args.cpu_seconds, KEEP_MODES[args.keep_mode][1])
 
     out = {
         "metric": METRIC,
@@ -229,7 +236,7 @@ def bench_contiguous(args, wl):
                    "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
                    "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
                    "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU",
-                   "layers_per_group": args.layers_per_group},
+                   "layers_per_group": args.layers_per_group, "keep_mode": args.keep_mode},
         "pass_ms_p10_p90": [float(np.percentile(t_pass, 10)), float(np.percentile(t_pass, 90))],
         "tokens_per_s": n / (ms * 1e-3),
         "pass_alg_bytes": pass_bytes,
@@ -270,6 +277,7 @@ def bench_paged(args, wl):
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
     tria.tria_set_pipeline(ctx, args.layers_per_group)
+    tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
     pools = [pg[x] for x in ("k_pool", "v_pool", "pos_pool", "block_table")]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -351,7 +359,7 @@ def bench_paged(args, wl):
         "config": {"workload": wl.name, "sequences": wl.n_seq, "lengths": lens,
                    "budgets": budgets, "append": m, "sink": wl.sink, "window": wl.window,
                    "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq, "head_dim": wl.hd,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "keep_mode": args.keep_mode},
         "round_ms_p10_p90": [float(np.percentile(t_round, 10)), float(np.percentile(t_round, 90))],
         "initial_pass_ms": first_ms,
         "initial_pass_rows_per_s": sum(wl.L * wl.Hkv * x for x in lens) / (first_ms * 1e-3),
@@ -369,7 +377,7 @@ def bench_paged(args, wl):
     return out
 
 
-def cpu_baseline(wl, stats, k0, v0, p0, seconds):
+def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0):
     """The CPU oracle, as it stands, on whole passes over the same input (host copies of
     the device-generated cache), repeated until about `seconds` of CPU work."""
     import numpy as np
@@ -383,7 +391,7 @@ def cpu_baseline(wl, stats, k0, v0, p0, seconds):
         t = time.perf_counter()
         oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
                      list(wl.offsets), k, v, pos, wl.n, wl.budget, wl.sink, wl.window, *stats,
-                     want_raw=False, want_agg=False)
+                     want_raw=False, want_agg=False, keep_mode=keep_mode)
         dt = time.perf_counter() - t
         times.append(dt)
         spent += dt

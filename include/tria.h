@@ -201,6 +201,33 @@ int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t
  * identical either way.  Returns TRIA_OK or TRIA_E_INVAL. */
 int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
 
+/* Who shares a keep set in tria_select / tria_evict / tria_evict_paged_batch.
+ *   TRIA_KEEP_PER_UNIT (default): every (layer, KV head) unit selects on its
+ *     own scores (tria_select's rule).
+ *   TRIA_KEEP_PER_KV_HEAD: one keep set per KV head g, used by every layer:
+ *     the worklog ("TriAttention Native C++ Worklog", section "Later
+ *     correction: selector and compaction are now cleared on the aggressive
+ *     sample7 path") checks one keep-index list per KV head and gathers it in
+ *     all layers, after a cross-layer aggregation step.
+ *   TRIA_KEEP_GLOBAL: one keep set for the whole cache: the llama.cpp page
+ *     ("TriAttention KV-Cache Eviction (--triattention)", section 5, "Phase
+ *     C") ships a global z-normalisation shader for its cells, which hold
+ *     every layer and head.
+ * Neither page spells out the cross-unit reduction; it is taken as the GQA
+ * group's rule over the larger group: each member query head is z-normalised
+ * over its own unit's rows, the group score of a row is the max of those
+ * z-scores over every member head (-inf if any member score is not finite),
+ * and the group keeps the protected rows plus its highest-scoring candidates.
+ * The raw scores, kept counts and compaction are those of the per-unit pass;
+ * keep_idx (and agg_out) are written for every unit, equal within a group.
+ * A shared mode runs tria_evict without layer groups (tria_set_pipeline has
+ * no effect), since a group spans all layers.  Returns TRIA_OK, or
+ * TRIA_E_INVAL for another mode. */
+#define TRIA_KEEP_PER_UNIT 0
+#define TRIA_KEEP_PER_KV_HEAD 1
+#define TRIA_KEEP_GLOBAL 2
+int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
+
 /* Waits for the whole device, then reports and clears the context's device
  * error word: TRIA_OK, or TRIA_E_DEVICE if a compaction launched through this
  * context gave up one of its bounded waits since the last call (its output

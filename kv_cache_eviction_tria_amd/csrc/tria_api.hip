@@ -7,7 +7,7 @@
 
 #include <new>
 
-#include "tria_internal.h"
+#include "tria_group.h"
 
 namespace tria {
 int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G);
@@ -56,6 +56,16 @@ struct tria_ctx {
     hipEvent_t ev_join = nullptr;
     hipEvent_t ev_group[8] = {};
     int layers_per_group = 0;  // 0: one group (tria_set_pipeline)
+    // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
+    int keep_mode = TRIA_KEEP_PER_UNIT;
+    HeadNorm* norms = nullptr;
+    size_t norms_bytes = 0;
+    float* gagg = nullptr;
+    size_t gagg_bytes = 0;
+    int32_t* gkeep = nullptr;
+    size_t gkeep_bytes = 0;
+    int32_t* gpb = nullptr;
+    size_t gpb_bytes = 0;
     // per-kernel timing (tria_timing_*)
     bool timing = false;
     hipEvent_t tev[TRIA_TIMED_MAX][2] = {};
@@ -265,19 +275,51 @@ int reserve_select(tria_ctx* ctx, const Batch& b, int units_per_seq, hipStream_t
     return rc;
 }
 
+// Scratch of a shared-keep-set selection over a whole batch (all layers).
+int reserve_shared(tria_ctx* ctx, const Batch& b, hipStream_t s) {
+    const int ng = keep_groups(ctx->keep_mode, ctx->L, ctx->Hkv);
+    const GroupOff tot = group_offsets(b, b.n_seq, ng);
+    const size_t units = (size_t)b.n_seq * ctx->L * ctx->Hkv;
+    int rc = grow(ctx, reinterpret_cast<void**>(&ctx->norms), &ctx->norms_bytes,
+                  units * ctx->G * sizeof(HeadNorm), s);
+    if (!rc)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->gagg), &ctx->gagg_bytes,
+                  (size_t)tot.agg * sizeof(float), s);
+    if (!rc)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->gkeep), &ctx->gkeep_bytes,
+                  (size_t)tot.keep * sizeof(int32_t), s);
+    if (!rc)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->gpb), &ctx->gpb_bytes,
+                  (size_t)tot.pb * sizeof(int32_t), s);
+    const int64_t krows = select_key_scratch_rows(group_batch(b, ng), ng, 1);
+    if (!rc && krows > 0)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->keys), &ctx->keys_bytes, (size_t)krows * 4, s);
+    return rc;
+}
+
 // Select over `layers` layers per sequence (all by default).  have_part: the
 // scorer already wrote the moment partials of these scores into ctx->part.
+// A shared keep mode needs all layers (layers < 0).
 int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
                bool have_part, hipStream_t s, int layers = -1, int group = 0) {
     const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
+    const bool shared = ctx->keep_mode != TRIA_KEEP_PER_UNIT;
+    if (shared && layers >= 0 && layers != ctx->L) return TRIA_E_INVAL;
     int rc = reserve_select(ctx, b, ups, s);
+    if (!rc && shared) rc = reserve_shared(ctx, b, s);
     if (rc) return rc;
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_SELECT, s, &slot);
     if (e == hipSuccess && !have_part) e = launch_moments(b, ups, ctx->G, raw, ctx->part, s);
-    if (e == hipSuccess)
-        e = launch_select_impl(b, ups, ctx->G, raw, ctx->part, keep, agg, ctx->keys, ctx->pb,
-                               ctx->cst.ticket + group, s);
+    if (e == hipSuccess) {
+        if (shared)
+            e = launch_shared_select(b, ctx->L, ctx->Hkv, ctx->G, ctx->keep_mode, raw, ctx->part,
+                                     ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb, ctx->keys, keep,
+                                     ctx->pb, agg, ctx->cst.ticket + group, s);
+        else
+            e = launch_select_impl(b, ups, ctx->G, raw, ctx->part, keep, agg, ctx->keys, ctx->pb,
+                                   ctx->cst.ticket + group, s);
+    }
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
     return TRIA_OK;
@@ -319,7 +361,10 @@ Batch sub_batch(const Batch& b, int l0, int L, int Hkv, int G) {
 // the last compaction, so the pass stays ordered with respect to `s`.
 int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) {
     const int L = ctx->L, n_seq = b.n_seq;
-    const int lpg = ctx->layers_per_group > 0 ? ctx->layers_per_group : L;
+    // a shared keep set spans all layers: no layer groups
+    const int lpg = ctx->layers_per_group > 0 && ctx->keep_mode == TRIA_KEEP_PER_UNIT
+                        ? ctx->layers_per_group
+                        : L;
     int ng = (L + lpg - 1) / lpg;
     ng = ng > kMaxGroups ? kMaxGroups : ng;
     const int all_units = n_seq * L * ctx->Hkv;
@@ -393,7 +438,8 @@ void tria_free(tria_ctx* ctx) {
     if (!ctx) return;
     void* bufs[] = {ctx->q_re, ctx->q_im, ctx->w,    ctx->omega, ctx->m_re,      ctx->m_im,
                     ctx->coef, ctx->raw,  ctx->keep, ctx->keys,  ctx->part,      ctx->pb,
-                    ctx->cst.flags,       ctx->cst.err,          ctx->cst.ticket};
+                    ctx->cst.flags,       ctx->cst.err,          ctx->cst.ticket,
+                    ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
@@ -618,6 +664,14 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
 int tria_set_pipeline(tria_ctx* ctx, int32_t layers_per_group) {
     if (!ctx || layers_per_group < 0) return TRIA_E_INVAL;
     ctx->layers_per_group = layers_per_group;
+    return TRIA_OK;
+}
+
+int tria_set_keep_mode(tria_ctx* ctx, int32_t mode) {
+    if (!ctx) return TRIA_E_INVAL;
+    if (mode != TRIA_KEEP_PER_UNIT && mode != TRIA_KEEP_PER_KV_HEAD && mode != TRIA_KEEP_GLOBAL)
+        return TRIA_E_INVAL;
+    ctx->keep_mode = mode;
     return TRIA_OK;
 }
 

@@ -29,7 +29,7 @@
 //      written in ascending order: ranks in row order come from wave ballots
 //      plus a prefix over the (j, wave) counts.
 // Keys live in registers for n <= 32K rows, else in a global scratch array.
-#include "tria_internal.h"
+#include "tria_group.h"
 
 namespace tria {
 
@@ -139,13 +139,6 @@ __device__ __forceinline__ float f4_get(const float4& v, int q) {
     return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
 }
 
-// Per-head z-normalisation constants: mu as an unevaluated sum of two floats
-// (hi + lo) and 1/sigma.  z = ((s - hi) - lo) * isg in fp32: the subtraction
-// removes the head's common offset first, so z keeps ~1e-6 relative accuracy.
-struct HeadNorm {
-    float hi, lo, isg;
-};
-
 __device__ __forceinline__ float uniform_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -172,8 +165,7 @@ __device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, in
         for (int h = 0; h < G; ++h) {
             const float s = R[r * G + h];
             if (!isfinite(s)) bad = true;
-            const HeadNorm c = sh[h];
-            const float z = ((s - c.hi) - c.lo) * c.isg;
+            const float z = znorm(s, sh[h]);
             best = (h == 0 || z > best) ? z : best;
         }
     } else {
@@ -181,7 +173,7 @@ __device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, in
         for (int h = 0; h < GV; ++h) {
             const float s = f4_get(x.v[h >> 2], h & 3);
             if (!isfinite(s)) bad = true;
-            const float z = ((s - nm.h[h].hi) - nm.h[h].lo) * nm.h[h].isg;
+            const float z = znorm(s, nm.h[h]);
             best = (h == 0 || z > best) ? z : best;
         }
     }
@@ -213,7 +205,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     float* AG = agg_out ? agg_out + sd.raw_off / G + (int64_t)uu * n : nullptr;
     uint32_t* KS = kRegKeys ? nullptr : key_scratch + sd.raw_off / G + (int64_t)uu * n;
     const int64_t tiles = part_tiles(n);
-    const PartRec* __restrict__ P = part + (sd.part_off + (int64_t)uu * tiles) * G;
+    const PartRec* __restrict__ P = part ? part + (sd.part_off + (int64_t)uu * tiles) * G : nullptr;
 
     __shared__ HeadNorm norm_sh[64];
     __shared__ uint32_t hist[kBins];
@@ -228,33 +220,11 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     auto row_of = [&](int j) -> int { return j * kSelThreads + t; };
 
     // 1. head statistics from the tile partials: wavefront w merges heads
-    //    w, w + 16, ... (lanes stride over the tiles; fixed summation order)
+    //    w, w + 16, ...  Without partials the scores are used as they are
+    //    (identity norms: a shared keep set's group scores).
     for (int h = wid; h < G; h += kWaves) {
-        double c = 0.0, a = 0.0;
-        for (int64_t i = lane; i < tiles; i += 64) {
-            const PartRec pr = P[i * G + h];
-            double mean, m2;
-            part_stats(pr, &mean, &m2);
-            c += pr.cnt;
-            a += pr.cnt * mean;
-        }
-        c = wave_sum_f64(c);
-        a = wave_sum_f64(a);
-        const double mu = c > 0.0 ? a / c : 0.0;
-        double m2 = 0.0;
-        for (int64_t i = lane; i < tiles; i += 64) {
-            const PartRec pr = P[i * G + h];
-            double mean, mt;
-            part_stats(pr, &mean, &mt);
-            const double d = mean - mu;
-            m2 += mt + pr.cnt * d * d;
-        }
-        m2 = wave_sum_f64(m2);
-        if (lane == 0) {
-            const double var = c > 0.0 ? m2 / c : 0.0;
-            const float hi = (float)mu;
-            norm_sh[h] = HeadNorm{hi, (float)(mu - (double)hi), var > 0.0 ? (float)(1.0 / sqrt(var)) : 0.0f};
-        }
+        const HeadNorm hn = part ? merge_head_norm(P, tiles, G, h) : HeadNorm{0.0f, 0.0f, 1.0f};
+        if (lane == 0) norm_sh[h] = hn;
     }
     for (int i = t; i < kBins; i += kSelThreads) hist[i] = 0;
     __syncthreads();

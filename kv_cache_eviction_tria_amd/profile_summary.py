@@ -24,7 +24,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 STAGE_SOURCES = {
     "score": ["tria_score.hip", "tria_prep.hip", "tria_internal.h"],
-    "select": ["tria_select.hip", "tria_internal.h"],
+    "select": ["tria_select.hip", "tria_group.h", "tria_internal.h"],
     "compact": ["tria_compact.hip", "tria_internal.h"],
 }
 STAGE_KERNELS = {"score": "score_", "select": "select_kernel", "compact": "compact_flow_kernel"}

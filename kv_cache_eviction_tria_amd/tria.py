@@ -92,6 +92,8 @@ def lib():
                                                  i64, vp, vp]
             L.tria_set_pipeline.restype = ctypes.c_int
             L.tria_set_pipeline.argtypes = [vp, i32]
+            L.tria_set_keep_mode.restype = ctypes.c_int
+            L.tria_set_keep_mode.argtypes = [vp, i32]
             L.tria_device_status.restype = ctypes.c_int
             L.tria_device_status.argtypes = [vp]
             L.tria_timing_enable.restype = ctypes.c_int
@@ -242,6 +244,17 @@ def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, 
 def tria_set_pipeline(ctx: TriaCtx, layers_per_group: int) -> None:
     """0: one group (default); > 0: layer groups overlapped on two streams."""
     _check(lib().tria_set_pipeline(ctx.handle, int(layers_per_group)), "tria_set_pipeline")
+
+
+TRIA_KEEP_PER_UNIT = 0
+TRIA_KEEP_PER_KV_HEAD = 1
+TRIA_KEEP_GLOBAL = 2
+
+
+def tria_set_keep_mode(ctx: TriaCtx, mode: int) -> None:
+    """Who shares a keep set: TRIA_KEEP_PER_UNIT (default), TRIA_KEEP_PER_KV_HEAD
+    (one per KV head across layers) or TRIA_KEEP_GLOBAL (one for the cache)."""
+    _check(lib().tria_set_keep_mode(ctx.handle, int(mode)), "tria_set_keep_mode")
 
 
 def tria_device_status(ctx: TriaCtx) -> None:

@@ -332,3 +332,109 @@ def test_paged_batch(k_type):
                 pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
                 pu.check_gather(v0[l, h], va[l, h], keep, K, where + " V")
     ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# Shared keep sets (one per KV head across layers; one for the whole cache)
+# ---------------------------------------------------------------------------
+
+MODES = {oracle.KEEP_KV_HEAD: tria.TRIA_KEEP_PER_KV_HEAD, oracle.KEEP_GLOBAL: tria.TRIA_KEEP_GLOBAL}
+
+
+@pytest.mark.parametrize("mode", sorted(MODES), ids=["per_kv_head", "global"])
+@pytest.mark.parametrize("k_type,G", [(Q8, 4), (F16, 4), (Q8, 3)], ids=["q8_g4", "f16_g4", "q8_g3"])
+def test_shared_keep_modes(mode, k_type, G):
+    """Staged score -> select -> compact with a shared keep mode against the oracle's
+    same mode: raw scores, group scores, kept sets (cutoff band), exact gathers; every
+    member of a group holds the same kept rows; tria_evict leaves the same cache."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="shared", L=5, Hkv=3, Hq=3 * G,
+                 k_type=k_type)
+    n, B, S, W = 3000, 700, 4, 256
+    pu.say("case shared mode %d k%d G%d" % (mode, k_type, G))
+    case = synth.make_case(wl, device="cpu", n=n, cap=n + 3)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    k0, v0, p0 = case["k"].numpy().copy(), case["v"].numpy().copy(), case["pos"].numpy().copy()
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_keep_mode(ctx, MODES[mode])
+    a = [case[x].to(DEV) for x in ("k", "v", "pos")]
+    b = [t.clone() for t in a]
+    g = pu.gpu_pass(ctx, *a, n, B, S, W, wl.G)
+    assert tria.tria_evict(ctx, *b, n, B, S, W) == g["K"]
+    tria.tria_device_status(ctx)
+    o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                     list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, B, S, W, *stats,
+                     compact=False, keep_mode=mode)
+    nd = pu.compare_pass(g, o, n, B, S, W, "shared mode %d" % mode)
+    K = g["K"]
+    ka, va, pa = pu.host(a[0]), pu.host(a[1]), pu.host(a[2])
+    for l in range(wl.L):
+        for h in range(wl.Hkv):
+            ref = g["keep"][0, h if mode == oracle.KEEP_KV_HEAD else 0]
+            assert np.array_equal(g["keep"][l, h], ref), "group members differ"
+            assert np.array_equal(g["agg"][l, h], g["agg"][0, h if mode == oracle.KEEP_KV_HEAD else 0])
+            pu.check_gather(k0[l, h], ka[l, h], ref, K, "K")
+            pu.check_gather(v0[l, h], va[l, h], ref, K, "V")
+            pu.check_gather(p0[l, h], pa[l, h], ref, K, "pos")
+    for x, y in zip(a, b):
+        assert torch.equal(x[:, :, :K], y[:, :, :K]), "tria_evict differs from the stages"
+    ctx.close()
+    pu.say("  ok: kept %d, %d rows in the cutoff band differ" % (K, nd))
+
+
+def test_shared_mode_one_layer_is_the_per_unit_pass():
+    """With one layer the per-KV-head mode must leave exactly the per-unit result."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="shared1", L=1, Hkv=8, Hq=32, k_type=Q8)
+    n, B, S, W = 20000, 5000, 4, 512
+    case = synth.make_case(wl, device="cpu", n=n)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    a = [case[x].to(DEV) for x in ("k", "v", "pos")]
+    b = [t.clone() for t in a]
+    ctx = pu.make_ctx(wl, stats)
+    assert tria.tria_evict(ctx, *a, n, B, S, W) == B
+    tria.tria_set_keep_mode(ctx, tria.TRIA_KEEP_PER_KV_HEAD)
+    assert tria.tria_evict(ctx, *b, n, B, S, W) == B
+    tria.tria_device_status(ctx)
+    for x, y in zip(a, b):
+        assert torch.equal(x[:, :, :B], y[:, :, :B])
+    ctx.close()
+
+
+def test_shared_mode_paged_batch():
+    """Per-KV-head keep sets over a paged batch of sequences of different lengths."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged_shared", L=4, Hkv=2, Hq=8, hd=128)
+    lens = [2500, 700, 64, 1800]
+    budgets = [800, 200, 100, 500]
+    S, W = 0, 128
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 78)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 6)
+    before = [(synth.paged_rows(pg["k_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["v_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["pos_pool"], pg["block_table"][s], n).numpy().copy())
+              for s, n in enumerate(lens)]
+    pu.say("case paged shared lens %s" % lens)
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_keep_mode(ctx, tria.TRIA_KEEP_PER_KV_HEAD)
+    dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+    kept = tria.tria_evict_paged_batch(ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"],
+                                       dev["block_table"], lens, budgets, S, W)
+    tria.tria_device_status(ctx)
+    bt = dev["block_table"].cpu()
+    for s, n in enumerate(lens):
+        K = oracle.kept_count(n, budgets[s], S, W)
+        assert kept[s] == K
+        k0, v0, p0 = before[s]
+        o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                         list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, budgets[s], S, W,
+                         *stats, compact=False, keep_mode=oracle.KEEP_KV_HEAD)
+        ka = synth.paged_rows(dev["k_pool"].cpu(), bt[s], n).numpy()
+        pa = synth.paged_rows(dev["pos_pool"].cpu(), bt[s], n).numpy()
+        for h in range(wl.Hkv):
+            ref = pa[0, h, :K]
+            for l in range(wl.L):
+                keep = pa[l, h, :K]
+                where = "paged shared seq %d unit (%d,%d)" % (s, l, h)
+                assert np.array_equal(keep, ref), where + ": layers differ"
+                pu.check_kept(keep, o["keep_idx"][l, h], o["agg"][l, h], n, budgets[s], S, W,
+                              where)
+                pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
+    ctx.close()
