@@ -11,10 +11,10 @@
 // Kernels (all HBM-light next to the score and the compaction):
 //   norm_kernel       per-head mean / 1/sigma of every unit from the scorer's
 //                     tile partials (one wavefront per head);
-//   group_agg_kernel  one thread per (row, group): reads the member units'
-//                     raw scores (consecutive rows per wavefront, so every
-//                     member's G scores come in coalesced 16-byte loads) and
-//                     writes the group score;
+//   group_agg_kernel  64 rows of one group per block, the members split over
+//                     its four wavefronts (lane = row, so every member's G
+//                     scores come in coalesced 16-byte loads), maxima combined
+//                     in LDS; writes the group score;
 //   the selector      over the group scores with identity norms;
 //   broadcast_kernel  copies each group's kept rows and chunk prefix counts to
 //                     its member units, whose compaction then runs unchanged.
@@ -53,23 +53,34 @@ __device__ __forceinline__ int member_unit(int mode, int Hkv, int grp, int m) {
     return mode == TRIA_KEEP_PER_KV_HEAD ? m * Hkv + grp : m;
 }
 
-// grid (row blocks, groups, sequences).  GV: scores per row read as float4
-// (G when G % 4 == 0), 0 for scalar loads.
+// grid (row blocks of kAggRows, groups, sequences).  Wavefront w of a block
+// takes members w, w + kAggSlices, ... of the group for the block's 64 rows
+// (lane = row, so each member's scores come in one coalesced sweep); the
+// slices' maxima are combined through LDS.  GV: scores per row read as
+// float4 (G when G % 4 == 0), 0 for scalar loads.
+constexpr int kAggRows = 64;
+constexpr int kAggSlices = kGroupThreads / kAggRows;
+
 template <int GV>
 __global__ __launch_bounds__(kGroupThreads) void group_agg_kernel(
     Batch b, int L, int Hkv, int G, int mode, const float* __restrict__ raw,
     const HeadNorm* __restrict__ norms, float* __restrict__ gagg) {
+    __shared__ float best_sh[kAggSlices][kAggRows];
+    __shared__ int bad_sh[kAggSlices][kAggRows];
     const int seq = blockIdx.z, grp = blockIdx.y;
     const SeqDesc sd = b.seq[seq];
     const int64_t n = sd.n;
-    const int64_t r = (int64_t)blockIdx.x * kGroupThreads + threadIdx.x;
-    if (r >= n) return;
+    const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * kAggRows + lane;
+    if ((int64_t)blockIdx.x * kAggRows >= n) return;  // whole block past the end
+    const bool in = r < n;
     const int ups = L * Hkv;
     const int ng = keep_groups(mode, L, Hkv);
     const int members = mode == TRIA_KEEP_PER_KV_HEAD ? L : ups;
+    // z-scores are finite or +-inf, so -inf is the identity of the max
     float best = -INFINITY;
-    bool bad = false, first = true;
-    for (int m = 0; m < members; ++m) {
+    bool bad = false;
+    for (int m = slice; in && m < members; m += kAggSlices) {
         const int uu = member_unit(mode, Hkv, grp, m);
         const float* R = raw + sd.raw_off + ((int64_t)uu * n + r) * G;
         const HeadNorm* NU = norms + ((int64_t)seq * ups + uu) * G;
@@ -80,11 +91,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_agg_kernel(
                 const float sv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float s = sv[i];
-                    if (!isfinite(s)) bad = true;
-                    const float z = znorm(s, NU[4 * q + i]);
-                    best = (first || z > best) ? z : best;
-                    first = false;
+                    if (!isfinite(sv[i])) bad = true;
+                    const float z = znorm(sv[i], NU[4 * q + i]);
+                    best = z > best ? z : best;
                 }
             }
         } else {
@@ -92,13 +101,23 @@ __global__ __launch_bounds__(kGroupThreads) void group_agg_kernel(
                 const float s = R[h];
                 if (!isfinite(s)) bad = true;
                 const float z = znorm(s, NU[h]);
-                best = (first || z > best) ? z : best;
-                first = false;
+                best = z > best ? z : best;
             }
         }
     }
-    const GroupOff go = group_offsets(b, seq, ng);
-    gagg[go.agg + (int64_t)grp * n + r] = bad ? -INFINITY : best + 0.0f;
+    best_sh[slice][lane] = best;
+    bad_sh[slice][lane] = bad ? 1 : 0;
+    __syncthreads();
+    if (slice == 0 && in) {
+#pragma unroll
+        for (int q = 1; q < kAggSlices; ++q) {
+            const float o = best_sh[q][lane];
+            best = o > best ? o : best;
+            bad = bad || bad_sh[q][lane];
+        }
+        const GroupOff go = group_offsets(b, seq, ng);
+        gagg[go.agg + (int64_t)grp * n + r] = bad ? -INFINITY : best + 0.0f;
+    }
 }
 
 // Block u: unit u of the batch; copies its group's kept rows, chunk prefix
@@ -159,7 +178,7 @@ hipError_t launch_shared_select(const Batch& b, int L, int Hkv, int G, int mode,
     hipLaunchKernelGGL(norm_kernel, dim3(units), dim3(kGroupThreads), 0, s, b, ups, G, part, norms);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((max_n + kGroupThreads - 1) / kGroupThreads), (unsigned)ng,
+    const dim3 grid((unsigned)((max_n + kAggRows - 1) / kAggRows), (unsigned)ng,
                     (unsigned)b.n_seq);
     if (G % 4 == 0 && G <= 8) {
         if (G == 4)
