@@ -17,6 +17,10 @@ the passages of the source pages each step follows:
   cache): the worklog's per-head keep sets gathered in every layer and the
   llama.cpp page's global z-normalisation shader; the cross-unit reduction is
   read as the GQA group's max taken over the larger group.
+* Hole-filling compaction (a variant of the order-preserving gather): the
+  page asks for the kept rows packed in place without gaps; the variant keeps
+  the sinks first and the newest rows last, in order, and fills the holes
+  below them from above.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force and hand-worked fixtures.  One reading is not pinned by
@@ -34,6 +38,10 @@ import numpy as np
 
 KV_F16 = 0
 KV_Q8_0 = 1
+
+# compaction rule (tria_oracle.c, orc_evict_ex)
+COMPACT_ORDERED = 0   # order-preserving gather (the pages' rule)
+COMPACT_HOLEFILL = 1  # holes below the trailing run filled from above it
 
 # keep-set sharing (tria_oracle.c, orc_evict_mode)
 KEEP_UNIT = 0      # each (layer, KV head) unit selects on its own
@@ -92,6 +100,10 @@ def _load():
                                       i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32]
             lib.orc_evict_mode.restype = i64
             lib.orc_evict_mode.argtypes = [i32] + lib.orc_evict.argtypes
+            lib.orc_evict_ex.restype = i64
+            lib.orc_evict_ex.argtypes = [i32, i32] + lib.orc_evict.argtypes
+            lib.orc_compact_holefill.restype = i64
+            lib.orc_compact_holefill.argtypes = [vp, i64, vp, i64, i64]
             lib.orc_num_threads.restype = i32
             lib.orc_num_threads.argtypes = []
             _lib = lib
@@ -194,13 +206,25 @@ def compact_rows(rows: np.ndarray, keep_idx: np.ndarray) -> np.ndarray:
     return out
 
 
+def compact_holefill(rows: np.ndarray, keep_idx: np.ndarray, n: int):
+    """Hole-filling compaction of a copy of rows [n, ...]; returns (rows, moves)."""
+    out = np.array(rows, copy=True, order="C")
+    rb = out.reshape(out.shape[0], -1).view(np.uint8).shape[1]
+    ki = _c(keep_idx, np.int32)
+    moves = _load().orc_compact_holefill(_p(out), rb, _p(ki), len(ki), int(n))
+    if moves < 0:
+        raise MemoryError("oracle hole-fill compaction failed")
+    return out, int(moves)
+
+
 def evict(k_type: int, v_type: int, L: int, Hkv: int, Hq: int, hd: int, theta: float, offsets,
           k: np.ndarray, v: np.ndarray, pos: np.ndarray, n: int, budget: int, sink: int,
           window: int, q_re, q_im, w, want_raw=True, want_agg=True, compact=True,
-          keep_mode: int = KEEP_UNIT):
+          keep_mode: int = KEEP_UNIT, compact_mode: int = COMPACT_ORDERED):
     """Whole pass over a contiguous host cache [L][Hkv][cap][row] (in place).
 
     keep_mode: KEEP_UNIT, KEEP_KV_HEAD or KEEP_GLOBAL (who shares a keep set).
+    compact_mode: COMPACT_ORDERED or COMPACT_HOLEFILL.
     Returns dict(kept, keep_idx [L,Hkv,K], raw [L,Hkv,n,G] or None, agg
     [L,Hkv,n] -- the score each unit's keep set was selected on -- or None).
     """
@@ -215,10 +239,10 @@ def evict(k_type: int, v_type: int, L: int, Hkv: int, Hq: int, hd: int, theta: f
     agg = np.empty((L, Hkv, n), np.float64) if want_agg else None
     q_re, q_im, w = (_c(x, np.float32) for x in (q_re, q_im, w))
     offs = _c(offsets, np.int64)
-    rc = _load().orc_evict_mode(int(keep_mode), k_type, v_type, L, Hkv, Hq, hd, float(theta),
-                                _p(offs), len(offs), _p(k), _p(v), _p(pos), cap, n, budget,
-                                sink, window, _p(q_re), _p(q_im), _p(w), _p(keep), _p(raw),
-                                _p(agg), 1 if compact else 0)
+    rc = _load().orc_evict_ex(int(keep_mode), int(compact_mode), k_type, v_type, L, Hkv, Hq, hd,
+                              float(theta), _p(offs), len(offs), _p(k), _p(v), _p(pos), cap, n,
+                              budget, sink, window, _p(q_re), _p(q_im), _p(w), _p(keep), _p(raw),
+                              _p(agg), 1 if compact else 0)
     if rc < 0:
         raise RuntimeError("oracle evict failed")
     return {"kept": int(rc), "keep_idx": keep[:, :, :K], "raw": raw, "agg": agg}

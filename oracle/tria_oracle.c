@@ -331,6 +331,55 @@ int orc_compact_rows(uint8_t *rows, int64_t row_bytes, const int32_t *keep_idx, 
     return 0;
 }
 
+/* Hole-filling compaction (a variant; the order-preserving gather above is
+ * the pages' rule).  [LC] section 5, "Phase B" step 4 asks only that the kept
+ * rows end up packed in place with no gaps; the cache's cells carry their
+ * positions.  The variant keeps the layout the selection relies on -- the
+ * sink rows stay first, the newest rows stay last and in order -- and moves
+ * as few rows as that allows:
+ *   R = the trailing run: the kept rows n-|R| .. n-1 (the longest run of
+ *       kept rows that ends at row n-1; it holds the protected window);
+ *   holes = the rows below K-|R| that are not kept, ascending;
+ *   tails = the kept rows at or above K-|R| that are not in R, ascending
+ *           (as many as there are holes);
+ *   hole i <- tail i, then the run moves to rows K-|R| .. K-1, in order.
+ * Rows kept below K-|R| (the sinks among them) do not move.  Positions move
+ * with their rows, so rows [0, K) hold exactly the kept rows.
+ * keep_idx: ascending kept rows (K of them) of a unit of n rows.
+ * Returns the number of rows written (moves), or -1. */
+int64_t orc_compact_holefill(uint8_t *rows, int64_t row_bytes, const int32_t *keep_idx,
+                             int64_t K, int64_t n)
+{
+    if (K >= n || K <= 0) return 0;
+    int64_t run = 0;
+    while (run < K && keep_idx[K - 1 - run] == n - 1 - run) run++;
+    int64_t lim = K - run; /* rows [0, lim) hold the kept rows outside the run */
+    unsigned char *kept = (unsigned char *)calloc((size_t)n, 1);
+    if (!kept) return -1;
+    for (int64_t e = 0; e < K; e++) kept[keep_idx[e]] = 1;
+    int64_t moves = 0;
+    int64_t h = 0;                                     /* next hole candidate */
+    for (int64_t e = 0; e < K - run; e++) {            /* kept rows outside the run */
+        int64_t src = keep_idx[e];
+        if (src < lim) continue;                       /* already in place */
+        while (kept[h]) h++;                           /* next hole below lim */
+        memcpy(rows + h * row_bytes, rows + src * row_bytes, (size_t)row_bytes);
+        h++;
+        moves++;
+    }
+    /* the run moves down by n - K rows, in ascending order (an overlapping
+     * move towards lower rows is safe in this order) */
+    for (int64_t j = 0; j < run; j++) {
+        int64_t src = n - run + j, dst = lim + j;
+        if (src != dst) {
+            memmove(rows + dst * row_bytes, rows + src * row_bytes, (size_t)row_bytes);
+            moves++;
+        }
+    }
+    free(kept);
+    return moves;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Whole pass over a contiguous cache [L][Hkv][cap][row].                     */
 /* ------------------------------------------------------------------------ */
@@ -346,6 +395,8 @@ int orc_compact_rows(uint8_t *rows, int64_t row_bytes, const int32_t *keep_idx, 
  * rule as the GQA group's: every member query head is z-normalised over its
  * own unit's rows, and the group score of a row is the max of those z-scores
  * over all member heads (-inf if any member score is not finite). */
+#define ORC_COMPACT_ORDERED 0
+#define ORC_COMPACT_HOLEFILL 1
 #define ORC_KEEP_UNIT 0
 #define ORC_KEEP_KV_HEAD 1
 #define ORC_KEEP_GLOBAL 2
@@ -362,6 +413,7 @@ static int orc_group_of(int mode, int Hkv, int u)
 
 /* One eviction pass over every (layer, KV head) unit.
  *   keep_mode : ORC_KEEP_UNIT, ORC_KEEP_KV_HEAD or ORC_KEEP_GLOBAL.
+ *   compact_mode : ORC_COMPACT_ORDERED (the gather) or ORC_COMPACT_HOLEFILL.
  *   k, v, pos : host copies, [L][Hkv][cap] rows; compacted in place.
  *   q_re, q_im, w : statistics [L][Hq][F]; query head h = g*G + j belongs to
  *                   KV head g (contiguous GQA grouping).
@@ -371,11 +423,11 @@ static int orc_group_of(int mode, int Hkv, int u)
  *   agg       : output [L][Hkv][n] (may be NULL): the score the unit's keep set
  *               was selected on (its group's score under a shared mode).
  * Returns the kept count K, or -1. */
-int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, int Hq, int hd,
-                       double theta, const int64_t *offsets, int n_off, uint8_t *k, uint8_t *v,
-                       int32_t *pos, int64_t cap, int64_t n, int64_t budget, int64_t sink,
-                       int64_t window, const float *q_re, const float *q_im, const float *w,
-                       int32_t *keep_idx, double *raw, double *agg, int do_compact)
+int64_t orc_evict_ex(int keep_mode, int compact_mode, int k_type, int v_type, int L, int Hkv,
+                     int Hq, int hd, double theta, const int64_t *offsets, int n_off, uint8_t *k,
+                     uint8_t *v, int32_t *pos, int64_t cap, int64_t n, int64_t budget,
+                     int64_t sink, int64_t window, const float *q_re, const float *q_im,
+                     const float *w, int32_t *keep_idx, double *raw, double *agg, int do_compact)
 {
     int G = Hq / Hkv;
     int F = hd / 2;
@@ -384,6 +436,7 @@ int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, in
     int64_t K = orc_kept_count(n, budget, sink, window);
     if (K < 0 || kb < 0 || vb < 0 || n > cap) return -1;
     if (keep_mode < ORC_KEEP_UNIT || keep_mode > ORC_KEEP_GLOBAL) return -1;
+    if (compact_mode != ORC_COMPACT_ORDERED && compact_mode != ORC_COMPACT_HOLEFILL) return -1;
     int NG = orc_n_groups(keep_mode, L, Hkv);
     int64_t nn = n > 0 ? n : 1;
     double *rs = raw ? raw : (double *)malloc(sizeof(double) * (size_t)(U * nn * G));
@@ -443,7 +496,11 @@ int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, in
             int bad = 0;
             if (keep_idx) memcpy(keep_idx + (int64_t)u * K, ki, sizeof(int32_t) * (size_t)K);
             if (agg) memcpy(agg + (int64_t)u * n, ga + (int64_t)gr * n, sizeof(double) * (size_t)n);
-            if (do_compact && !failed) {
+            if (do_compact && !failed && compact_mode == ORC_COMPACT_HOLEFILL) {
+                bad |= orc_compact_holefill(k + (int64_t)u * cap * kb, kb, ki, K, n) < 0;
+                bad |= orc_compact_holefill(v + (int64_t)u * cap * vb, vb, ki, K, n) < 0;
+                bad |= orc_compact_holefill((uint8_t *)(pos + (int64_t)u * cap), 4, ki, K, n) < 0;
+            } else if (do_compact && !failed) {
                 bad |= orc_compact_rows(k + (int64_t)u * cap * kb, kb, ki, K);
                 bad |= orc_compact_rows(v + (int64_t)u * cap * vb, vb, ki, K);
                 bad |= orc_compact_rows((uint8_t *)(pos + (int64_t)u * cap), 4, ki, K);
@@ -459,6 +516,18 @@ int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, in
     free(ga);
     free(gk);
     return failed ? -1 : K;
+}
+
+/* Order-preserving compaction (the pages' rule). */
+int64_t orc_evict_mode(int keep_mode, int k_type, int v_type, int L, int Hkv, int Hq, int hd,
+                       double theta, const int64_t *offsets, int n_off, uint8_t *k, uint8_t *v,
+                       int32_t *pos, int64_t cap, int64_t n, int64_t budget, int64_t sink,
+                       int64_t window, const float *q_re, const float *q_im, const float *w,
+                       int32_t *keep_idx, double *raw, double *agg, int do_compact)
+{
+    return orc_evict_ex(keep_mode, ORC_COMPACT_ORDERED, k_type, v_type, L, Hkv, Hq, hd, theta,
+                        offsets, n_off, k, v, pos, cap, n, budget, sink, window, q_re, q_im, w,
+                        keep_idx, raw, agg, do_compact);
 }
 
 /* The per-unit pass (each unit selects on its own). */

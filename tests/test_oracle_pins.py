@@ -549,3 +549,96 @@ def test_shared_layer_order_does_not_matter():
         b, *_ = _shared_evict(pcase, L, Hkv, Hq, hd, n, 20, 1, 4, mode, compact=False)
         assert np.array_equal(a["keep_idx"][perm], b["keep_idx"])
         assert np.array_equal(a["agg"][perm], b["agg"])
+
+
+# ---------------------------------------------------------------------------
+# Hole-filling compaction (variant)
+# ---------------------------------------------------------------------------
+
+def test_holefill_layout_rules():
+    """Rows [0, K) hold exactly the kept rows; kept rows below the trailing run do not
+    move; the trailing run of kept rows ends at row K-1 in its order; every moved row
+    is a hole below the run or a row of the run."""
+    rng = np.random.default_rng(40)
+    for trial in range(300):
+        n = int(rng.integers(2, 90))
+        K = int(rng.integers(1, n + 1))
+        keep = np.sort(rng.choice(n, K, replace=False)).astype(np.int32)
+        if trial % 3 == 0:  # a protected-window-like run at the end
+            run = int(rng.integers(1, K + 1))
+            rest = np.sort(rng.choice(n - run, K - run, replace=False))
+            keep = np.concatenate([rest, np.arange(n - run, n)]).astype(np.int32)
+        rows = np.arange(n, dtype=np.int64) * 7 + 3
+        out, moves = oracle.compact_holefill(rows, keep, n)
+        if K == n:
+            assert moves == 0 and np.array_equal(out, rows)
+            continue
+        assert sorted(out[:K].tolist()) == sorted(rows[keep].tolist())
+        run = 0
+        while run < K and keep[K - 1 - run] == n - 1 - run:
+            run += 1
+        lim = K - run
+        assert np.array_equal(out[lim:K], rows[n - run:n])
+        kept_low = keep[keep < lim]
+        assert np.array_equal(out[kept_low], rows[kept_low])
+        holes = sorted(set(range(lim)) - set(kept_low.tolist()))
+        tails = [r for r in keep[:K - run] if r >= lim]
+        assert len(holes) == len(tails)
+        assert [out[h] for h in holes] == [rows[t] for t in tails]
+        assert moves == len(tails) + (run if n > K else 0)
+
+
+def _rounds(mode, rounds, seed, L=2, Hkv=2, Hq=4, hd=32, n0=300, budget=120, sink=4,
+            window=40, append=24):
+    """Rounds of 'append `append` fresh rows, evict to the budget' on a contiguous cache;
+    returns the kept positions (as sets per unit) and the moved rows of every round."""
+    rng = np.random.default_rng(seed)
+    F = hd // 2
+    cap = n0 + rounds * append
+    q_re = rng.standard_normal((L, Hq, F)).astype(np.float32)
+    q_im = rng.standard_normal((L, Hq, F)).astype(np.float32)
+    w = np.abs(rng.standard_normal((L, Hq, F))).astype(np.float32)
+    fresh = rng.standard_normal((L, Hkv, cap, hd)).astype(np.float16)
+    k = np.zeros((L, Hkv, cap, 2 * hd), np.uint8)
+    v = np.zeros((L, Hkv, cap, 2 * hd), np.uint8)
+    pos = np.zeros((L, Hkv, cap), np.int32)
+    k[:, :, :n0] = fresh[:, :, :n0].view(np.uint8).reshape(L, Hkv, n0, 2 * hd)
+    v[:, :, :n0] = k[:, :, :n0] ^ 0x5A
+    pos[:, :, :n0] = np.arange(n0)
+    n, nxt, out = n0, n0, []
+    for r in range(rounds):
+        if r > 0:  # append fresh rows at the next positions
+            sl = slice(n, n + append)
+            k[:, :, sl] = fresh[:, :, nxt:nxt + append].view(np.uint8).reshape(L, Hkv, append, 2 * hd)
+            v[:, :, sl] = k[:, :, sl] ^ 0x5A
+            pos[:, :, sl] = np.arange(nxt, nxt + append)
+            n += append
+            nxt += append
+        before = pos.copy()
+        o = oracle.evict(oracle.KV_F16, oracle.KV_F16, L, Hkv, Hq, hd, 1e6, [1, 8, 64], k, v, pos,
+                         n, budget, sink, window, q_re, q_im, w, compact_mode=mode)
+        K = o["kept"]
+        # every kept row carries its own K and V bytes
+        for l in range(L):
+            for g in range(Hkv):
+                p = pos[l, g, :K]
+                assert np.array_equal(k[l, g, :K], fresh[l, g, p].view(np.uint8).reshape(K, 2 * hd))
+                assert np.array_equal(v[l, g, :K], k[l, g, :K] ^ 0x5A)
+        moved = int((pos[:, :, :K] != before[:, :, :K]).sum())
+        out.append(([set(pos[l, g, :K].tolist()) for l in range(L) for g in range(Hkv)], moved))
+        n = K
+    return out
+
+
+def test_holefill_rounds_keep_the_same_tokens_as_the_ordered_gather():
+    """Sinks stay first and the newest rows stay last, so every round protects the same
+    tokens and scores them the same: with continuous scores (no ties at the cutoff) the
+    kept positions equal the order-preserving pass's, round after round, while the
+    variant moves far fewer rows once the cache is in steady state."""
+    a = _rounds(oracle.COMPACT_ORDERED, 8, 41)
+    b = _rounds(oracle.COMPACT_HOLEFILL, 8, 41)
+    for (sa, ma), (sb, mb) in zip(a, b):
+        assert sa == sb
+    steady_a = sum(m for _, m in a[2:])
+    steady_b = sum(m for _, m in b[2:])
+    assert steady_b * 2 < steady_a, (steady_a, steady_b)
