@@ -228,6 +228,30 @@ int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
 #define TRIA_KEEP_GLOBAL 2
 int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
 
+/* How tria_compact / tria_evict / tria_evict_paged_batch pack the kept rows.
+ *   TRIA_COMPACT_ORDERED (default): the order-preserving gather documented at
+ *     tria_compact.
+ *   TRIA_COMPACT_HOLE_FILL: a variant that moves far fewer rows once a cache
+ *     is in steady state.  The llama.cpp page ("TriAttention KV-Cache Eviction
+ *     (--triattention)", section 5, "Phase B" step 4) asks only that the kept
+ *     rows end up packed in place with no gaps (cells carry their positions).
+ *     With K kept rows of n: let the run be the kept rows n-r .. n-1 (the
+ *     longest run of kept rows ending at row n-1; it holds the window).  The
+ *     rows below K-r that are not kept (holes) receive, in ascending order,
+ *     the kept rows at or above K-r outside the run (tails, ascending); then
+ *     the run moves to rows K-r .. K-1 in order.  Kept rows below K-r (the
+ *     sinks among them) do not move.  Rows [0, K) then hold exactly the kept
+ *     rows, the sinks first and the newest rows last, so later passes protect
+ *     the same tokens and keep the same ones as with the ordered gather,
+ *     except where candidates tie exactly at the cutoff (a tie goes to the
+ *     lower row, and rows are no longer in position order).  Positions move
+ *     with their rows.  keep_idx must be ascending as for tria_compact; an
+ *     entry that would move a row outside [0, n) is skipped.
+ * Returns TRIA_OK, or TRIA_E_INVAL for another mode. */
+#define TRIA_COMPACT_ORDERED 0
+#define TRIA_COMPACT_HOLE_FILL 1
+int tria_set_compaction(tria_ctx *ctx, int32_t mode);
+
 /* Waits for the whole device, then reports and clears the context's device
  * error word: TRIA_OK, or TRIA_E_DEVICE if a compaction launched through this
  * context gave up one of its bounded waits since the last call (its output

@@ -13,6 +13,8 @@ namespace tria {
 int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G);
 hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float* raw,
                           PartRec* part, hipStream_t s);
+hipError_t launch_holefill(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
+                           hipStream_t s);
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
                               const PartRec* part, int32_t* keep, float* agg,
                               uint32_t* key_scratch, int32_t* chunk_pb, uint32_t* ticket,
@@ -58,6 +60,7 @@ struct tria_ctx {
     int layers_per_group = 0;  // 0: one group (tria_set_pipeline)
     // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
     int keep_mode = TRIA_KEEP_PER_UNIT;
+    int compact_mode = TRIA_COMPACT_ORDERED;  // tria_set_compaction
     HeadNorm* norms = nullptr;
     size_t norms_bytes = 0;
     float* gagg = nullptr;
@@ -147,7 +150,9 @@ int compact_timed(tria_ctx* ctx, const CacheView& cv, const Batch& b, int units,
                   const int32_t* keep, const int32_t* pb, hipStream_t s, int group = 0) {
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_COMPACT, s, &slot);
-    if (e == hipSuccess)
+    if (e == hipSuccess && ctx->compact_mode == TRIA_COMPACT_HOLE_FILL)
+        e = launch_holefill(cv, b, units, keep, s);
+    else if (e == hipSuccess)
         e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, ctx->cst.ticket + group, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
@@ -664,6 +669,13 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
 int tria_set_pipeline(tria_ctx* ctx, int32_t layers_per_group) {
     if (!ctx || layers_per_group < 0) return TRIA_E_INVAL;
     ctx->layers_per_group = layers_per_group;
+    return TRIA_OK;
+}
+
+int tria_set_compaction(tria_ctx* ctx, int32_t mode) {
+    if (!ctx) return TRIA_E_INVAL;
+    if (mode != TRIA_COMPACT_ORDERED && mode != TRIA_COMPACT_HOLE_FILL) return TRIA_E_INVAL;
+    ctx->compact_mode = mode;
     return TRIA_OK;
 }
 

@@ -26,6 +26,7 @@ STAGE_SOURCES = {
     "score": ["tria_score.hip", "tria_prep.hip", "tria_internal.h"],
     "select": ["tria_select.hip", "tria_group.h", "tria_internal.h"],
     "compact": ["tria_compact.hip", "tria_internal.h"],
+    "holefill": ["tria_holefill.hip", "tria_internal.h"],
 }
 STAGE_KERNELS = {"score": "score_", "select": "select_kernel", "compact": "compact_flow_kernel"}
 CAL_KERNEL = "BitwiseXorFunctor"

@@ -94,6 +94,8 @@ def lib():
             L.tria_set_pipeline.argtypes = [vp, i32]
             L.tria_set_keep_mode.restype = ctypes.c_int
             L.tria_set_keep_mode.argtypes = [vp, i32]
+            L.tria_set_compaction.restype = ctypes.c_int
+            L.tria_set_compaction.argtypes = [vp, i32]
             L.tria_device_status.restype = ctypes.c_int
             L.tria_device_status.argtypes = [vp]
             L.tria_timing_enable.restype = ctypes.c_int
@@ -255,6 +257,15 @@ def tria_set_keep_mode(ctx: TriaCtx, mode: int) -> None:
     """Who shares a keep set: TRIA_KEEP_PER_UNIT (default), TRIA_KEEP_PER_KV_HEAD
     (one per KV head across layers) or TRIA_KEEP_GLOBAL (one for the cache)."""
     _check(lib().tria_set_keep_mode(ctx.handle, int(mode)), "tria_set_keep_mode")
+
+
+TRIA_COMPACT_ORDERED = 0
+TRIA_COMPACT_HOLE_FILL = 1
+
+
+def tria_set_compaction(ctx: TriaCtx, mode: int) -> None:
+    """TRIA_COMPACT_ORDERED (default gather) or TRIA_COMPACT_HOLE_FILL (variant)."""
+    _check(lib().tria_set_compaction(ctx.handle, int(mode)), "tria_set_compaction")
 
 
 def tria_device_status(ctx: TriaCtx) -> None:

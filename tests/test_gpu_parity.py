@@ -438,3 +438,147 @@ def test_shared_mode_paged_batch():
                               where)
                 pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
     ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# Hole-filling compaction (variant)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pattern", ["random", "window_run", "all_tail", "one_hole", "invalid"])
+def test_holefill_compaction_patterns(pattern):
+    """tria_compact with TRIA_COMPACT_HOLE_FILL against the oracle's hole fill on the
+    same kept indices, every unit, K, V and positions, bit-exact (rows >= kept are
+    not compared)."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="hole", L=3, Hkv=2, Hq=8, k_type=Q8)
+    n = 5000
+    K = 1300
+    rng = np.random.default_rng(hash(pattern) % 1000)
+    keep = np.zeros((wl.L, wl.Hkv, K), np.int32)
+    for l in range(wl.L):
+        for h in range(wl.Hkv):
+            if pattern == "random":
+                kk = np.sort(rng.choice(n, K, replace=False))
+            elif pattern == "window_run":
+                kk = np.concatenate([np.sort(rng.choice(n - 500, K - 500, replace=False)),
+                                     np.arange(n - 500, n)])
+            elif pattern == "all_tail":
+                kk = np.arange(n - K, n)
+            elif pattern == "one_hole":
+                kk = np.concatenate([np.arange(0, 700), np.arange(701, K + 1)])
+            else:  # ascending but with entries outside [0, n) at both ends
+                kk = np.sort(rng.choice(n, K, replace=False))
+                kk[0] = -7
+                kk[-1] = n + 40
+            keep[l, h] = kk
+    pu.say("case holefill pattern %s" % pattern)
+    case = synth.make_case(wl, device="cpu", n=n)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    k0, v0, p0 = case["k"].numpy().copy(), case["v"].numpy().copy(), case["pos"].numpy().copy()
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    tria.tria_compact(ctx, k, v, pos, n, torch.from_numpy(keep).to(DEV), K)
+    tria.tria_device_status(ctx)
+    ka, va, pa = pu.host(k), pu.host(v), pu.host(pos)
+    for l in range(wl.L):
+        for h in range(wl.Hkv):
+            kk = keep[l, h]
+            if pattern == "invalid":
+                # unspecified layout, but nothing from outside the unit: every row
+                # below the kept count is one of the unit's own rows, intact
+                for d in range(K):
+                    p = int(pa[l, h, d])
+                    assert 0 <= p < n
+                    assert np.array_equal(ka[l, h, d], k0[l, h, p])
+                    assert np.array_equal(va[l, h, d], v0[l, h, p])
+                continue
+            for arr0, arr, name in ((k0, ka, "K"), (v0, va, "V"), (p0, pa, "pos")):
+                want, _ = oracle.compact_holefill(arr0[l, h, :n], kk, n)
+                assert np.array_equal(arr[l, h, :K], want[:K]), "%s unit (%d,%d)" % (name, l, h)
+    ctx.close()
+
+
+def test_holefill_paged_rounds():
+    """Rounds of 'append 64 rows to every sequence, evict' on a paged batch with
+    hole-filling compaction: every round the GPU's kept rows match the oracle's (cutoff
+    band), and the compacted logical rows are exactly the oracle's hole fill of the
+    GPU's own kept rows; the rows that moved are few once in steady state."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged_hole", L=3, Hkv=2, Hq=8, hd=128)
+    lens = [2000, 900, 64, 1500]
+    pct = 30
+    S, W, m_app = 0, 128, 64
+    budgets = [max(1, n * pct // 100) for n in lens]
+    rounds = 4
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 79,
+                         extra_blocks=(rounds * m_app) // 16 + 1)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 7)
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+    n_now = list(lens)
+    next_pos = list(lens)
+    bt = dev["block_table"].cpu()
+    moved_last = None
+    for r in range(rounds):
+        if r > 0:
+            for s in range(len(lens)):
+                synth.append_paged(dev, s, n_now[s], m_app, next_pos[s], wl.L, wl.Hkv, wl.hd,
+                                   wl.k_type, wl.v_type, 900 + 10 * r + s)
+                n_now[s] += m_app
+                next_pos[s] += m_app
+        pu.say("case paged holefill round %d n %s" % (r, n_now))
+        before = []
+        for s, n in enumerate(n_now):
+            before.append(tuple(synth.paged_rows(dev[x].cpu(), bt[s], n).numpy().copy()
+                                for x in ("k_pool", "v_pool", "pos_pool")))
+        kept = tria.tria_evict_paged_batch(ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"],
+                                           dev["block_table"], n_now, budgets, S, W)
+        tria.tria_device_status(ctx)
+        moved = 0
+        for s, n in enumerate(n_now):
+            K = oracle.kept_count(n, budgets[s], S, W)
+            assert kept[s] == K
+            k0, v0, p0 = before[s]
+            o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                             list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, budgets[s],
+                             S, W, *stats, compact=False)
+            ka = synth.paged_rows(dev["k_pool"].cpu(), bt[s], n).numpy()
+            va = synth.paged_rows(dev["v_pool"].cpu(), bt[s], n).numpy()
+            pa = synth.paged_rows(dev["pos_pool"].cpu(), bt[s], n).numpy()
+            for l in range(wl.L):
+                for h in range(wl.Hkv):
+                    where = "round %d seq %d unit (%d,%d)" % (r, s, l, h)
+                    row_of = {int(p): i for i, p in enumerate(p0[l, h])}
+                    gkeep = np.array(sorted(row_of[int(p)] for p in pa[l, h, :K]), np.int32)
+                    pu.check_kept(gkeep, o["keep_idx"][l, h], o["agg"][l, h], n, budgets[s], S,
+                                  W, where)
+                    if K < n:
+                        for arr0, arr, name in ((k0, ka, "K"), (v0, va, "V"), (p0, pa, "pos")):
+                            want, mv = oracle.compact_holefill(arr0[l, h], gkeep, n)
+                            assert np.array_equal(arr[l, h, :K], want[:K]), where + " " + name
+                        moved += mv
+            n_now[s] = K
+        pu.say("  moved rows %d" % moved)
+        moved_last = moved
+    # steady state: each unit moves its appended rows (in the run) plus at most as many
+    # tails as holes -- far below the kept rows
+    units = wl.L * wl.Hkv * sum(1 for b_, n in zip(budgets, lens) if b_ < n)
+    assert moved_last <= units * (W + 4 * m_app)
+    ctx.close()
+
+
+def test_holefill_evict_equals_the_stages():
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="hole_stages", L=4, Hkv=4, Hq=16, k_type=Q8)
+    n, B, S, W = 9000, 2000, 4, 512
+    case = synth.make_case(wl, device="cpu", n=n, cap=n + 5)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    a = [case[x].to(DEV) for x in ("k", "v", "pos")]
+    b = [t.clone() for t in a]
+    assert tria.tria_evict(ctx, *a, n, B, S, W) == B
+    pu.gpu_pass(ctx, *b, n, B, S, W, wl.G)
+    tria.tria_device_status(ctx)
+    for x, y in zip(a, b):
+        assert torch.equal(x[:, :, :B], y[:, :, :B])
+    ctx.close()
