@@ -53,11 +53,15 @@ def parse():
                     help="tria_set_pipeline: 0 = one group; > 0 = overlapped layer groups")
     ap.add_argument("--keep-mode", choices=sorted(KEEP_MODES), default="per_unit",
                     help="tria_set_keep_mode: who shares a keep set")
+    ap.add_argument("--compaction", choices=sorted(COMPACTIONS), default="ordered",
+                    help="tria_set_compaction: order-preserving gather or hole filling")
     return ap.parse_args()
 
 
 # --keep-mode -> (library mode, oracle mode)
 KEEP_MODES = {"per_unit": (0, 0), "per_kv_head": (1, 1), "global": (2, 2)}
+# --compaction -> (library mode, oracle mode, profile key of its kernels)
+COMPACTIONS = {"ordered": (0, 0, "compact"), "hole_fill": (1, 1, "holefill")}
 
 
 def measured_traffic(stage, workload):
@@ -74,14 +78,21 @@ def measured_traffic(stage, workload):
     return float(t["bytes_per_launch"])
 
 
-def roofline(stage, ms_total, launches, alg_bytes_total, workload):
-    """Roofline entry for one stage from its summed launch durations."""
+def traffic_key_fn(args):
+    """Profile key of each stage's kernels under the chosen compaction."""
+    return lambda stage: COMPACTIONS[args.compaction][2] if stage == "compact" else stage
+
+
+def roofline(stage, ms_total, launches, alg_bytes_total, workload, traffic_key=None):
+    """Roofline entry for one stage from its summed launch durations (traffic_key: the
+    profile the stage's counters are stored under, the stage's own name by default)."""
     avg_ms = ms_total / max(launches, 1)
     per_launch = alg_bytes_total / max(launches, 1) if alg_bytes_total else None
     achieved = per_launch / (avg_ms * 1e-3) / 1e9 if per_launch else None
     return {"kernel": stage, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-            "traffic": measured_traffic(stage, workload), "alg_bytes_per_launch": per_launch,
+            "traffic": measured_traffic(traffic_key or stage, workload),
+            "alg_bytes_per_launch": per_launch,
             "launches_per_step": launches, "avg_launch_ms": avg_ms}
 
 
@@ -117,6 +128,7 @@ def log(msg):
 
 
 def bench_contiguous(args, wl):
+    tkey = traffic_key_fn(args)
     import numpy as np
     import torch
 
@@ -134,6 +146,7 @@ def bench_contiguous(args, wl):
                                list(wl.offsets), *stats)
     tria.tria_set_pipeline(ctx, args.layers_per_group)
     tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
+    tria.tria_set_compaction(ctx, COMPACTIONS[args.compaction][0])
     K = tria.tria_kept_count(n, B, S, W)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -215,7 +228,8 @@ def bench_contiguous(args, wl):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, stats, k0.cpu().numpy(), v0.cpu().numpy(), p0.cpu().numpy(),
-                           args.cpu_seconds, KEEP_MODES[args.keep_mode][1])
+                           args.cpu_seconds, KEEP_MODES[args.keep_mode][1],
+                           COMPACTIONS[args.compaction][1])
 
     out = {
         "metric": METRIC,
@@ -236,7 +250,8 @@ def bench_contiguous(args, wl):
                    "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
                    "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
                    "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU",
-                   "layers_per_group": args.layers_per_group, "keep_mode": args.keep_mode},
+                   "layers_per_group": args.layers_per_group, "keep_mode": args.keep_mode,
+                   "compaction": args.compaction},
         "pass_ms_p10_p90": [float(np.percentile(t_pass, 10)), float(np.percentile(t_pass, 90))],
         "tokens_per_s": n / (ms * 1e-3),
         "pass_alg_bytes": pass_bytes,
@@ -249,8 +264,9 @@ def bench_contiguous(args, wl):
         "sequential_stage_ms": seq_ms,
         "sequential_pass_ms": float(sum(seq_ms.values())) if seq_ms else None,
         "wall_s_timed_loop_incl_restore": t_wall,
-        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name),
-        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name)
+        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name,
+                             tkey(dom)),
+        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name, tkey(s))
                          for s in tria.STAGES},
         "cpu_baseline": cpu,
     }
@@ -259,6 +275,7 @@ def bench_contiguous(args, wl):
 
 
 def bench_paged(args, wl):
+    tkey = traffic_key_fn(args)
     import numpy as np
     import torch
 
@@ -278,15 +295,16 @@ def bench_paged(args, wl):
                                list(wl.offsets), *stats)
     tria.tria_set_pipeline(ctx, args.layers_per_group)
     tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
+    tria.tria_set_compaction(ctx, COMPACTIONS[args.compaction][0])
     pools = [pg[x] for x in ("k_pool", "v_pool", "pos_pool", "block_table")]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     log("initial pass")
-    e0.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     kept = tria.tria_evict_paged_batch(ctx, *pools, lens, budgets, wl.sink, wl.window, stream)
-    e1.record(stream)
-    e1.synchronize()
-    first_ms = e0.elapsed_time(e1)
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
     assert kept == budgets, (kept, budgets)
     n_now = list(budgets)
 
@@ -301,6 +319,7 @@ def bench_paged(args, wl):
     st_ms = {s: 0.0 for s in tria.STAGES}
     st_n = {s: 0 for s in tria.STAGES}
     t_round = []
+    t_event = []
     total = args.warmup + args.steps
     log("rounds: %d warmup + %d timed" % (args.warmup, args.steps))
     def kept_positions():
@@ -316,13 +335,21 @@ def bench_paged(args, wl):
         before = kept_positions() if r >= args.warmup else None
         if r == args.warmup:
             tria.tria_timing_enable(ctx, True)
+        # A round is timed on the host, idle device to idle device (it includes
+        # the enqueue, ~0.2 ms): events recorded around this call on an idle
+        # stream were found to read up to 2x the host-observed time of the same
+        # round, so they are only reported alongside.
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         e0.record(stream)
         kept = tria.tria_evict_paged_batch(ctx, *pools, n_now, budgets, wl.sink, wl.window,
                                            stream)
         e1.record(stream)
-        e1.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
         if r >= args.warmup:
-            t_round.append(e0.elapsed_time(e1))
+            t_round.append((t1 - t0) * 1e3)
+            t_event.append(e0.elapsed_time(e1))
             ms_i, n_i, _ = tria.tria_timing_read(ctx)
             for s in tria.STAGES:
                 st_ms[s] += ms_i[s]
@@ -359,8 +386,11 @@ def bench_paged(args, wl):
         "config": {"workload": wl.name, "sequences": wl.n_seq, "lengths": lens,
                    "budgets": budgets, "append": m, "sink": wl.sink, "window": wl.window,
                    "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq, "head_dim": wl.hd,
-                   "parallelism": "single GPU", "keep_mode": args.keep_mode},
+                   "parallelism": "single GPU", "keep_mode": args.keep_mode,
+                   "compaction": args.compaction},
         "round_ms_p10_p90": [float(np.percentile(t_round, 10)), float(np.percentile(t_round, 90))],
+        "round_timing": "host clock, synchronised device on both sides, enqueue included",
+        "round_ms_events_median": float(np.median(t_event)),
         "initial_pass_ms": first_ms,
         "initial_pass_rows_per_s": sum(wl.L * wl.Hkv * x for x in lens) / (first_ms * 1e-3),
         "kernel_ms_per_step": per_step_ms,
@@ -368,8 +398,9 @@ def bench_paged(args, wl):
         "moved_rows_per_round": moved,
         "round_alg_bytes": alg["score"] + alg["compact"],
         "round_frac_hbm": (alg["score"] + alg["compact"]) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name),
-        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name)
+        "roofline": roofline(dom, per_step_ms[dom], per_step_n[dom], alg[dom], wl.name,
+                             tkey(dom)),
+        "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name, tkey(s))
                          for s in tria.STAGES},
         "cpu_baseline": None,
     }
@@ -377,7 +408,7 @@ def bench_paged(args, wl):
     return out
 
 
-def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0):
+def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0, compact_mode=0):
     """The CPU oracle, as it stands, on whole passes over the same input (host copies of
     the device-generated cache), repeated until about `seconds` of CPU work."""
     import numpy as np
@@ -391,7 +422,8 @@ def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0):
         t = time.perf_counter()
         oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
                      list(wl.offsets), k, v, pos, wl.n, wl.budget, wl.sink, wl.window, *stats,
-                     want_raw=False, want_agg=False, keep_mode=keep_mode)
+                     want_raw=False, want_agg=False, keep_mode=keep_mode,
+                     compact_mode=compact_mode)
         dt = time.perf_counter() - t
         times.append(dt)
         spent += dt
