@@ -17,6 +17,9 @@ the passages of the source pages each step follows:
   cache): the worklog's per-head keep sets gathered in every layer and the
   llama.cpp page's global z-normalisation shader; the cross-unit reduction is
   read as the GQA group's max taken over the larger group.
+* Calibration statistics: per query head and frequency pair, the mean
+  pre-RoPE query pair, the mean pair magnitude and the norm weight
+  q_abs - |q_mean| (llama.cpp page section 2, the generator's accumulation).
 * Hole-filling compaction (a variant of the order-preserving gather): the
   page asks for the kept rows packed in place without gaps; the variant keeps
   the sinks first and the newest rows last, in order, and fills the holes
@@ -104,6 +107,8 @@ def _load():
             lib.orc_evict_ex.argtypes = [i32, i32] + lib.orc_evict.argtypes
             lib.orc_compact_holefill.restype = i64
             lib.orc_compact_holefill.argtypes = [vp, i64, vp, i64, i64]
+            lib.orc_calib_stats.restype = None
+            lib.orc_calib_stats.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
             lib.orc_num_threads.restype = i32
             lib.orc_num_threads.argtypes = []
             _lib = lib
@@ -215,6 +220,17 @@ def compact_holefill(rows: np.ndarray, keep_idx: np.ndarray, n: int):
     if moves < 0:
         raise MemoryError("oracle hole-fill compaction failed")
     return out, int(moves)
+
+
+def calib_stats(q: np.ndarray):
+    """q: [T, H, hd] query values (any float dtype; fp16/fp32 widen exactly, a
+    bfloat16 stream is passed as its float32 widening).  Returns fp64 arrays
+    (q_re, q_im, q_abs, w), each [H, hd/2]."""
+    q = _c(q, np.float64)
+    T, H, hd = q.shape
+    out = [np.empty((H, hd // 2), np.float64) for _ in range(4)]
+    _load().orc_calib_stats(_p(q), T, H, hd, *[_p(x) for x in out])
+    return tuple(out)
 
 
 def evict(k_type: int, v_type: int, L: int, Hkv: int, Hq: int, hd: int, theta: float, offsets,

@@ -542,6 +542,48 @@ int64_t orc_evict(int k_type, int v_type, int L, int Hkv, int Hq, int hd, double
                           agg, do_compact);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Calibration statistics.                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* [LC] section 2, "Generating a .tria file": the generator hooks each layer's
+ * pre-RoPE query tensor during forward passes and accumulates, per query head
+ * and frequency pair, the mean query direction and a per-frequency weight
+ * ([LC] section 5, "Phase C": per-head q_mean / q_abs arrays).  With the
+ * query pair q_f = q[f] + i q[f + hd/2] (NEOX halves) of every token t:
+ *   q_mean_f = (1/T) sum_t q_f(t)        (complex)
+ *   q_abs_f  = (1/T) sum_t |q_f(t)|
+ *   w_f      = q_abs_f - |q_mean_f|      (the norm-term weight: zero when
+ *              every token's pair points the same way, q_abs when the
+ *              directions cancel; [WL] "Phase 9" keeps this additive term
+ *              on |K_rot|)
+ * q: T tokens x H heads x hd values (row-major, fp64); outputs [H][hd/2]. */
+void orc_calib_stats(const double *q, int64_t T, int H, int hd, double *q_re, double *q_im,
+                     double *q_abs, double *w)
+{
+    int F = hd / 2;
+    for (int h = 0; h < H; h++) {
+        for (int f = 0; f < F; f++) {
+            double sr = 0.0, si = 0.0, sa = 0.0;
+            for (int64_t t = 0; t < T; t++) {
+                const double *row = q + (t * H + h) * (int64_t)hd;
+                double re = row[f], im = row[f + F];
+                sr += re;
+                si += im;
+                sa += sqrt(re * re + im * im);
+            }
+            int64_t o = (int64_t)h * F + f;
+            double mr = T > 0 ? sr / (double)T : 0.0;
+            double mi = T > 0 ? si / (double)T : 0.0;
+            double ma = T > 0 ? sa / (double)T : 0.0;
+            q_re[o] = mr;
+            q_im[o] = mi;
+            q_abs[o] = ma;
+            w[o] = ma - sqrt(mr * mr + mi * mi);
+        }
+    }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

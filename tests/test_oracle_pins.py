@@ -642,3 +642,50 @@ def test_holefill_rounds_keep_the_same_tokens_as_the_ordered_gather():
     steady_a = sum(m for _, m in a[2:])
     steady_b = sum(m for _, m in b[2:])
     assert steady_b * 2 < steady_a, (steady_a, steady_b)
+
+
+# ---------------------------------------------------------------------------
+# Calibration statistics
+# ---------------------------------------------------------------------------
+
+def test_calib_constant_stream():
+    """Every token the same: the mean is that query, q_abs its magnitude, w = 0."""
+    rng = np.random.default_rng(50)
+    q1 = rng.standard_normal((3, 16))
+    q = np.broadcast_to(q1, (37, 3, 16)).copy()
+    re, im, ab, w = oracle.calib_stats(q)
+    assert np.allclose(re, q1[:, :8], atol=1e-15) and np.allclose(im, q1[:, 8:], atol=1e-15)
+    assert np.allclose(ab, np.hypot(q1[:, :8], q1[:, 8:]), rtol=1e-15)
+    assert np.allclose(w, 0.0, atol=1e-14)
+
+
+def test_calib_rotating_pair_cancels():
+    """A pair of fixed length A whose phase turns by 2 pi / T per token: the mean is
+    0, q_abs = A and w = A (the directions cancel exactly)."""
+    T, A = 64, 2.5
+    t = np.arange(T)
+    q = np.zeros((T, 1, 4))
+    q[:, 0, 0] = A * np.cos(2 * np.pi * t / T)
+    q[:, 0, 2] = A * np.sin(2 * np.pi * t / T)
+    q[:, 0, 1] = 1.0  # second pair: constant (1, 0)
+    re, im, ab, w = oracle.calib_stats(q)
+    assert abs(re[0, 0]) < 1e-13 and abs(im[0, 0]) < 1e-13
+    assert abs(ab[0, 0] - A) < 1e-13 and abs(w[0, 0] - A) < 1e-12
+    assert re[0, 1] == 1.0 and im[0, 1] == 0.0 and w[0, 1] == 0.0
+
+
+def test_calib_opposite_halves_and_scaling():
+    """Half the tokens c, half -c: mean 0, w = |c|.  Scaling the stream by s scales
+    the mean by s and q_abs and w by |s|; w is never negative (triangle inequality)."""
+    c = np.array([[0.3, -1.2, 0.7, 2.0]])
+    q = np.concatenate([np.broadcast_to(c, (10, 1, 4)), np.broadcast_to(-c, (10, 1, 4))])
+    re, im, ab, w = oracle.calib_stats(q)
+    mag = np.hypot(c[0, :2], c[0, 2:])
+    assert np.allclose(re, 0, atol=1e-15) and np.allclose(w[0], mag, rtol=1e-14)
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((200, 5, 32)) + 0.4
+    a = oracle.calib_stats(q)
+    b = oracle.calib_stats(-3.0 * q)
+    assert np.allclose(b[0], -3.0 * a[0], rtol=1e-12) and np.allclose(b[1], -3.0 * a[1], rtol=1e-12)
+    assert np.allclose(b[2], 3.0 * a[2], rtol=1e-12) and np.allclose(b[3], 3.0 * a[3], rtol=1e-11)
+    assert np.all(a[3] >= -1e-15)
