@@ -252,6 +252,49 @@ int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
 #define TRIA_COMPACT_HOLE_FILL 1
 int tria_set_compaction(tria_ctx *ctx, int32_t mode);
 
+/* ------------------------------------------------------------------------
+ * Calibration statistics (the stats tria_load_stats takes), accumulated on
+ * the GPU from pre-RoPE query vectors: the llama.cpp page ("TriAttention
+ * KV-Cache Eviction (--triattention)", section 2, "Generating a .tria file")
+ * hooks each layer's pre-RoPE query tensor during forward passes over a
+ * corpus and accumulates per-head statistics; section 5, "Phase C", names the
+ * per-head q_mean / q_abs arrays.  Per layer l, query head h and pair f, with
+ * q_f = q[f] + i q[f + head_dim/2] over the T tokens added for that layer:
+ *   q_re + i q_im = (1/T) sum q_f,   q_abs = (1/T) sum |q_f|,
+ *   norm_w = q_abs - |q_re + i q_im|   (zero when every token's pair points the
+ *   same way; q_abs when the directions cancel).
+ * Sums are fp64 and their order is fixed by the calls, so a sequence of calls
+ * gives the same result every time.
+ * ------------------------------------------------------------------------ */
+#define TRIA_Q_F32 0
+#define TRIA_Q_F16 1
+#define TRIA_Q_BF16 2
+typedef struct tria_calib tria_calib;
+
+/* Zeroed accumulators for n_layers x n_q_heads x head_dim/2 pairs (device
+ * memory owned by the object).  head_dim even, <= 1024.  Synchronous. */
+int tria_calib_create(tria_calib **out, int32_t n_layers, int32_t n_q_heads, int32_t head_dim);
+
+/* Adds n_tokens query rows of one layer: q (device) holds row t at element
+ * t * row_stride, head h's head_dim values at + h * head_dim (row_stride >=
+ * n_q_heads * head_dim, e.g. the query slice of a fused projection), type
+ * TRIA_Q_*.  Stream-ordered; q must stay valid until the work has run.  At
+ * most 65535 * 64 tokens per call (TRIA_E_UNSUPPORTED beyond: add in batches).
+ * Calls on one object must use one stream (or be ordered by the caller). */
+int tria_calib_add(tria_calib *c, int32_t layer, const void *q, int32_t q_type, int64_t n_tokens,
+                   int64_t row_stride, hipStream_t stream);
+
+/* Tokens added so far to a layer (host count), or an error code. */
+int64_t tria_calib_tokens(const tria_calib *c, int32_t layer);
+
+/* Writes the statistics of every layer to device arrays [n_layers][n_q_heads]
+ * [head_dim/2] fp32 (q_abs may be NULL); a layer with no tokens gives zeros.
+ * Stream-ordered; the accumulators keep their sums (more adds may follow). */
+int tria_calib_finish(tria_calib *c, float *q_re, float *q_im, float *q_abs, float *norm_w,
+                      hipStream_t stream);
+
+void tria_calib_free(tria_calib *c);
+
 /* Waits for the whole device, then reports and clears the context's device
  * error word: TRIA_OK, or TRIA_E_DEVICE if a compaction launched through this
  * context gave up one of its bounded waits since the last call (its output

@@ -1,0 +1,202 @@
+// Calibration statistics on the GPU (llama.cpp page "TriAttention KV-Cache
+// Eviction (--triattention)", section 2, "Generating a .tria file": the
+// generator hooks each layer's pre-RoPE query tensor during forward passes and
+// accumulates per-head statistics; section 5, "Phase C", names the per-head
+// q_mean / q_abs arrays the scorer uploads).  Per layer, query head h and
+// frequency pair f, with q_f = q[f] + i q[f + hd/2] (NEOX halves):
+//   sums over tokens of Re q_f, Im q_f and |q_f|  (fp64)
+// and, at the end,
+//   q_mean = sums / T,  q_abs = sum|q_f| / T,  w = q_abs - |q_mean|
+// (w: the norm-term weight; zero when every token's pair points the same way).
+//
+// Streaming: tria_calib_add takes one layer's query rows of one batch; every
+// workgroup covers 64 tokens of 256 (head, pair) slots -- consecutive slots
+// read consecutive values of a row, so each token is a coalesced sweep -- and
+// writes its fp64 partial sums; a second kernel adds the partials into the
+// layer's accumulators in a fixed order, so the result does not depend on
+// scheduling.  The pair magnitude is formed in fp32 (the inputs are at most
+// fp32), the sums in fp64.
+#include <new>
+
+#include "tria_internal.h"
+
+namespace {
+
+constexpr int kCalThreads = 256;
+constexpr int kCalTok = 64;  // tokens per partial
+
+template <typename QT>
+__device__ __forceinline__ float q_load(const QT* p);
+template <>
+__device__ __forceinline__ float q_load<float>(const float* p) {
+    return *p;
+}
+template <>
+__device__ __forceinline__ float q_load<_Float16>(const _Float16* p) {
+    return (float)*p;
+}
+template <>
+__device__ __forceinline__ float q_load<uint16_t>(const uint16_t* p) {
+    return __uint_as_float((uint32_t)*p << 16);  // bfloat16: the top half of a float
+}
+
+// grid (slot blocks, token chunks); partial[(chunk * HF + slot) * 3 + {re, im, abs}]
+template <typename QT>
+__global__ __launch_bounds__(kCalThreads) void calib_partial_kernel(
+    const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
+    double* __restrict__ partial) {
+    const int i = blockIdx.x * kCalThreads + threadIdx.x;
+    if (i >= HF) return;
+    const int h = i / F, f = i - h * F;
+    const int64_t t0 = (int64_t)blockIdx.y * kCalTok;
+    const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
+    const QT* base = q + (int64_t)h * hd + f;
+    double sr = 0.0, si = 0.0, sa = 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float re = q_load<QT>(base + t * stride);
+        const float im = q_load<QT>(base + t * stride + F);
+        sr += (double)re;
+        si += (double)im;
+        sa += (double)__builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
+    }
+    double* out = partial + ((int64_t)blockIdx.y * HF + i) * 3;
+    out[0] = sr;
+    out[1] = si;
+    out[2] = sa;
+}
+
+// acc[j] += sum over chunks c (in order) of partial[c * 3HF + j], j < 3HF
+__global__ __launch_bounds__(kCalThreads) void calib_reduce_kernel(const double* __restrict__ partial,
+                                                                   int chunks, int n3,
+                                                                   double* __restrict__ acc) {
+    const int j = blockIdx.x * kCalThreads + threadIdx.x;
+    if (j >= n3) return;
+    double s = 0.0;
+    for (int c = 0; c < chunks; ++c) s += partial[(int64_t)c * n3 + j];
+    acc[j] += s;
+}
+
+// One layer's outputs from its sums over `count` tokens (zeros if none).
+__global__ __launch_bounds__(kCalThreads) void calib_finish_kernel(const double* __restrict__ acc,
+                                                                   int HF, int64_t count,
+                                                                   float* q_re, float* q_im,
+                                                                   float* q_abs, float* w) {
+    const int i = blockIdx.x * kCalThreads + threadIdx.x;
+    if (i >= HF) return;
+    const double inv = count > 0 ? 1.0 / (double)count : 0.0;
+    const double mr = acc[3 * i] * inv, mi = acc[3 * i + 1] * inv, ma = acc[3 * i + 2] * inv;
+    q_re[i] = (float)mr;
+    q_im[i] = (float)mi;
+    if (q_abs) q_abs[i] = (float)ma;
+    w[i] = (float)(ma - sqrt(mr * mr + mi * mi));
+}
+
+}  // namespace
+
+struct tria_calib {
+    int L, Hq, hd, F, HF;
+    double* acc = nullptr;      // [L][HF][3]
+    double* partial = nullptr;  // [chunks][HF][3], grown on demand
+    size_t partial_bytes = 0;
+    int64_t* count = nullptr;   // host [L]
+};
+
+extern "C" {
+
+int tria_calib_create(tria_calib** out, int32_t n_layers, int32_t n_q_heads, int32_t head_dim) {
+    if (!out) return TRIA_E_INVAL;
+    *out = nullptr;
+    if (n_layers < 1 || n_q_heads < 1) return TRIA_E_INVAL;
+    if (head_dim < 2 || head_dim % 2 != 0 || head_dim > 1024) return TRIA_E_UNSUPPORTED;
+    tria_calib* c = new (std::nothrow) tria_calib();
+    if (!c) return TRIA_E_NOMEM;
+    c->L = n_layers;
+    c->Hq = n_q_heads;
+    c->hd = head_dim;
+    c->F = head_dim / 2;
+    c->HF = n_q_heads * c->F;
+    c->count = static_cast<int64_t*>(calloc((size_t)n_layers, sizeof(int64_t)));
+    const size_t bytes = (size_t)n_layers * c->HF * 3 * sizeof(double);
+    hipError_t e = c->count ? hipMalloc(reinterpret_cast<void**>(&c->acc), bytes) : hipErrorOutOfMemory;
+    if (e == hipSuccess) e = hipMemset(c->acc, 0, bytes);
+    if (e != hipSuccess) {
+        tria_calib_free(c);
+        return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
+    }
+    *out = c;
+    return TRIA_OK;
+}
+
+void tria_calib_free(tria_calib* c) {
+    if (!c) return;
+    if (c->acc) (void)hipFree(c->acc);
+    if (c->partial) (void)hipFree(c->partial);
+    free(c->count);
+    delete c;
+}
+
+int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, int64_t n_tokens,
+                   int64_t row_stride, hipStream_t stream) {
+    if (!c || !q || layer < 0 || layer >= c->L || n_tokens < 0) return TRIA_E_INVAL;
+    if (row_stride < (int64_t)c->Hq * c->hd) return TRIA_E_INVAL;
+    if (q_type != TRIA_Q_F32 && q_type != TRIA_Q_F16 && q_type != TRIA_Q_BF16)
+        return TRIA_E_UNSUPPORTED;
+    if (n_tokens == 0) return TRIA_OK;
+    const int64_t chunks = (n_tokens + kCalTok - 1) / kCalTok;
+    if (chunks > 65535) return TRIA_E_UNSUPPORTED;  // grid.y; add in batches
+    const size_t need = (size_t)chunks * c->HF * 3 * sizeof(double);
+    if (need > c->partial_bytes) {
+        // earlier adds on this stream may still read the old buffer
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e == hipSuccess && c->partial) e = hipFree(c->partial);
+        c->partial = nullptr;
+        c->partial_bytes = 0;
+        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->partial), need);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
+        c->partial_bytes = need;
+    }
+    const dim3 grid((unsigned)((c->HF + kCalThreads - 1) / kCalThreads), (unsigned)chunks);
+    if (q_type == TRIA_Q_F32)
+        hipLaunchKernelGGL(calib_partial_kernel<float>, grid, dim3(kCalThreads), 0, stream,
+                           static_cast<const float*>(q), n_tokens, row_stride, c->F, c->hd, c->HF,
+                           c->partial);
+    else if (q_type == TRIA_Q_F16)
+        hipLaunchKernelGGL(calib_partial_kernel<_Float16>, grid, dim3(kCalThreads), 0, stream,
+                           static_cast<const _Float16*>(q), n_tokens, row_stride, c->F, c->hd,
+                           c->HF, c->partial);
+    else
+        hipLaunchKernelGGL(calib_partial_kernel<uint16_t>, grid, dim3(kCalThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), n_tokens, row_stride, c->F, c->hd,
+                           c->HF, c->partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return TRIA_E_HIP;
+    const int n3 = 3 * c->HF;
+    hipLaunchKernelGGL(calib_reduce_kernel, dim3((unsigned)((n3 + kCalThreads - 1) / kCalThreads)),
+                       dim3(kCalThreads), 0, stream, c->partial, (int)chunks, n3,
+                       c->acc + (int64_t)layer * n3);
+    e = hipGetLastError();
+    if (e != hipSuccess) return TRIA_E_HIP;
+    c->count[layer] += n_tokens;
+    return TRIA_OK;
+}
+
+int64_t tria_calib_tokens(const tria_calib* c, int32_t layer) {
+    if (!c || layer < 0 || layer >= c->L) return TRIA_E_INVAL;
+    return c->count[layer];
+}
+
+int tria_calib_finish(tria_calib* c, float* q_re, float* q_im, float* q_abs, float* norm_w,
+                      hipStream_t stream) {
+    if (!c || !q_re || !q_im || !norm_w) return TRIA_E_INVAL;
+    const unsigned blocks = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
+    for (int l = 0; l < c->L; ++l) {
+        const int64_t o = (int64_t)l * c->HF;
+        hipLaunchKernelGGL(calib_finish_kernel, dim3(blocks), dim3(kCalThreads), 0, stream,
+                           c->acc + o * 3, c->HF, c->count[l], q_re + o, q_im + o,
+                           q_abs ? q_abs + o : nullptr, norm_w + o);
+        if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;
+    }
+    return TRIA_OK;
+}
+
+}  // extern "C"

@@ -96,6 +96,16 @@ def lib():
             L.tria_set_keep_mode.argtypes = [vp, i32]
             L.tria_set_compaction.restype = ctypes.c_int
             L.tria_set_compaction.argtypes = [vp, i32]
+            L.tria_calib_create.restype = ctypes.c_int
+            L.tria_calib_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
+            L.tria_calib_add.restype = ctypes.c_int
+            L.tria_calib_add.argtypes = [vp, i32, vp, i32, i64, i64, vp]
+            L.tria_calib_tokens.restype = i64
+            L.tria_calib_tokens.argtypes = [vp, i32]
+            L.tria_calib_finish.restype = ctypes.c_int
+            L.tria_calib_finish.argtypes = [vp, vp, vp, vp, vp, vp]
+            L.tria_calib_free.restype = None
+            L.tria_calib_free.argtypes = [vp]
             L.tria_device_status.restype = ctypes.c_int
             L.tria_device_status.argtypes = [vp]
             L.tria_timing_enable.restype = ctypes.c_int
@@ -261,6 +271,55 @@ def tria_set_keep_mode(ctx: TriaCtx, mode: int) -> None:
 
 TRIA_COMPACT_ORDERED = 0
 TRIA_COMPACT_HOLE_FILL = 1
+
+TRIA_Q_F32 = 0
+TRIA_Q_F16 = 1
+TRIA_Q_BF16 = 2
+_Q_TYPES = {torch.float32: TRIA_Q_F32, torch.float16: TRIA_Q_F16, torch.bfloat16: TRIA_Q_BF16}
+
+
+class TriaCalib:
+    """Owns a tria_calib handle: GPU accumulators of calibration statistics."""
+
+    def __init__(self, n_layers: int, n_q_heads: int, head_dim: int):
+        h = ctypes.c_void_p()
+        _check(lib().tria_calib_create(ctypes.byref(h), int(n_layers), int(n_q_heads),
+                                       int(head_dim)), "tria_calib_create")
+        self.handle = h
+        self.n_layers, self.n_q_heads, self.head_dim = n_layers, n_q_heads, head_dim
+
+    def add(self, layer: int, q, stream=None) -> None:
+        """q: device [n_tokens, n_q_heads * head_dim (or more)], fp32/fp16/bf16, rows
+        contiguous in their first n_q_heads * head_dim values."""
+        if not isinstance(q, torch.Tensor) or not q.is_cuda or q.dim() != 2:
+            raise TypeError("q must be a 2-D CUDA tensor")
+        if q.dtype not in _Q_TYPES or q.stride(1) != 1:
+            raise TypeError("q must be fp32/fp16/bf16 with unit stride along a row")
+        _check(lib().tria_calib_add(self.handle, int(layer), ctypes.c_void_p(q.data_ptr()),
+                                    _Q_TYPES[q.dtype], q.shape[0], q.stride(0), _stream(stream)),
+               "tria_calib_add")
+
+    def tokens(self, layer: int) -> int:
+        return int(_check(lib().tria_calib_tokens(self.handle, int(layer)), "tria_calib_tokens"))
+
+    def finish(self, stream=None):
+        """Returns device fp32 tensors (q_re, q_im, q_abs, norm_w), each [L, Hq, hd/2]."""
+        shape = (self.n_layers, self.n_q_heads, self.head_dim // 2)
+        out = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(4)]
+        _check(lib().tria_calib_finish(self.handle, *[ctypes.c_void_p(t.data_ptr()) for t in out],
+                                       _stream(stream)), "tria_calib_finish")
+        return tuple(out)
+
+    def close(self):
+        if self.handle:
+            lib().tria_calib_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def tria_set_compaction(ctx: TriaCtx, mode: int) -> None:

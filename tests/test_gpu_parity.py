@@ -582,3 +582,67 @@ def test_holefill_evict_equals_the_stages():
     for x, y in zip(a, b):
         assert torch.equal(x[:, :, :B], y[:, :, :B])
     ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# Calibration statistics
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=["f32", "f16", "bf16"])
+def test_calib_stats_match_the_oracle(dtype):
+    """Three layers, the tokens of each added in uneven batches from a fused buffer
+    (row stride larger than the query slice); every statistic against the oracle on
+    the same values.  Bar: |g - o| <= 1e-6 * max(q_abs, 1e-3) per pair (the pair
+    magnitude is formed in fp32, sums in fp64, outputs rounded to fp32)."""
+    L, Hq, hd = 3, 6, 64
+    T = [300, 1, 517]
+    rng = np.random.default_rng(60)
+    pu.say("case calib %s" % dtype)
+    cal = tria.TriaCalib(L, Hq, hd)
+    for l in range(L):
+        mean = rng.standard_normal((Hq, hd)) * 0.7
+        x = (mean + rng.standard_normal((T[l], Hq, hd))).astype(np.float32)
+        fused = torch.zeros(T[l], Hq * hd + 96, dtype=dtype)
+        fused[:, :Hq * hd] = torch.from_numpy(x.reshape(T[l], -1)).to(dtype)
+        qv = fused[:, :Hq * hd].float().numpy().reshape(T[l], Hq, hd)  # the values added
+        dev = fused.to(DEV)
+        cut = [0, T[l] // 3, T[l] // 3 + 1, T[l]]
+        for a, b in zip(cut[:-1], cut[1:]):
+            if b > a:
+                cal.add(l, dev[a:b])
+        assert cal.tokens(l) == T[l]
+        re, im, ab, w = (pu.host(t)[l] for t in cal.finish())
+        o = oracle.calib_stats(qv)
+        scale = np.maximum(o[2], 1e-3)
+        for g, oo, name in zip((re, im, ab, w), o, ("q_re", "q_im", "q_abs", "w")):
+            err = np.abs(g.astype(np.float64) - oo)
+            assert np.all(err <= 1e-6 * scale), "%s layer %d: max err %g" % (name, l, err.max())
+    cal.close()
+
+
+def test_calib_feeds_the_eviction_pass():
+    """Statistics accumulated on the GPU load into a context and drive a pass that
+    matches the oracle run with the same statistics."""
+    wl = variant(WL["tiny_1x1_4k_f16"], name="calib_pass", L=2, Hkv=2, Hq=8, hd=128)
+    rng = np.random.default_rng(61)
+    cal = tria.TriaCalib(wl.L, wl.Hq, wl.hd)
+    for l in range(wl.L):
+        q = torch.from_numpy((rng.standard_normal((256, wl.Hq * wl.hd)) +
+                              np.repeat(rng.standard_normal((1, wl.Hq * wl.hd)), 256, 0))
+                             .astype(np.float32)).to(DEV)
+        cal.add(l, q)
+    re, im, _, w = cal.finish()
+    stats = tuple(pu.host(t).astype(np.float32) for t in (re, im, w))
+    n, B, S, W = 3000, 1000, 4, 256
+    case = synth.make_case(wl, device="cpu", n=n)
+    k0, v0, p0 = case["k"].numpy().copy(), case["v"].numpy().copy(), case["pos"].numpy().copy()
+    ctx = pu.make_ctx(wl, stats)
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    g = pu.gpu_pass(ctx, k, v, pos, n, B, S, W, wl.G)
+    o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                     list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, B, S, W, *stats,
+                     compact=False)
+    pu.compare_pass(g, o, n, B, S, W, "calibrated stats")
+    ctx.close()
+    cal.close()
