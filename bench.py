@@ -104,10 +104,13 @@ def main():
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     from kv_cache_eviction_tria_amd import synth
-    wl = synth.WORKLOADS[args.workload]
     if args.calibrate_bytes > 0:
         calibrate(args.calibrate_bytes)
-    out = bench_paged(args, wl) if wl.n_seq else bench_contiguous(args, wl)
+    if args.workload in synth.CALIB_WORKLOADS:
+        out = bench_calib(args, args.workload)
+    else:
+        wl = synth.WORKLOADS[args.workload]
+        out = bench_paged(args, wl) if wl.n_seq else bench_contiguous(args, wl)
     print(json.dumps(out), flush=True)
 
 
@@ -406,6 +409,80 @@ def bench_paged(args, wl):
     }
     ctx.close()
     return out
+
+
+def bench_calib(args, name):
+    """Calibration statistics: one step = every layer's query rows of one sample added
+    (one tria_calib_add per layer) and the statistics finished."""
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_tria_amd import synth, tria
+
+    L, Hq, hd, T, dtype = synth.CALIB_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log("calibration stream %s: generating on the device" % name)
+    qs = synth.gen_query_stream(L, Hq, hd, T, dtype, 7, dev)
+    cal = tria.TriaCalib(L, Hq, hd)
+
+    def step():
+        for l in range(L):
+            cal.add(l, qs[l], stream)
+        return cal.finish(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(args.steps):
+        torch.cuda._sleep(1_000_000)  # the start event follows real work (see bench_paged)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    alg = T * L * Hq * hd * torch.tensor([], dtype=dtype).element_size()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: oracle statistics of a few layers")
+        t0 = time.perf_counter()
+        nl = 0
+        while nl < L and (nl == 0 or time.perf_counter() - t0 < min(args.cpu_seconds, 10.0)):
+            q = qs[nl].float().cpu().numpy().reshape(T, Hq, hd)
+            oracle.calib_stats(q)
+            nl += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": nl * T / dt, "unit": "query tokens/s per layer", "cores": 1,
+               "kind": "oracle", "sample": "%d of %d layers, %d tokens each, %.1f s" % (
+                   nl, L, T, dt)}
+    cal.close()
+    achieved = alg / (ms * 1e-3) / 1e9
+    return {
+        "metric": "calibration query rows accumulated/sec (layer x token)",
+        "value": L * T / (ms * 1e-3),
+        "unit": "layer-token query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": str(dtype).replace("torch.", "") + " in, f64 sums",
+        "data": "synthetic (per-(head, pair) lognormal/uniform-phase mean plus N(0,1) noise)",
+        "config": {"workload": name, "layers": L, "q_heads": Hq, "head_dim": hd, "tokens": T,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "calib", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "alg_bytes_per_launch": alg / L, "launches_per_step": L,
+                     "avg_launch_ms": ms / L},
+        "cpu_baseline": cpu,
+    }
 
 
 def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0, compact_mode=0):

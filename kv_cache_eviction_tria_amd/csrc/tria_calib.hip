@@ -10,9 +10,11 @@
 // (w: the norm-term weight; zero when every token's pair points the same way).
 //
 // Streaming: tria_calib_add takes one layer's query rows of one batch; every
-// workgroup covers 64 tokens of 256 (head, pair) slots -- consecutive slots
-// read consecutive values of a row, so each token is a coalesced sweep -- and
-// writes its fp64 partial sums; a second kernel adds the partials into the
+// workgroup covers 32 tokens of 256 (head, pair) slots: four consecutive pairs
+// per lane (one 16-byte load of the real halves and one of the imaginary
+// halves per token; consecutive lanes read consecutive bytes), the tokens
+// dealt over its four wavefronts and their sums combined in LDS; it writes
+// fp64 partial sums; a second kernel adds the partials into the
 // layer's accumulators in a fixed order, so the result does not depend on
 // scheduling.  The pair magnitude is formed in fp32 (the inputs are at most
 // fp32), the sums in fp64.
@@ -23,7 +25,8 @@
 namespace {
 
 constexpr int kCalThreads = 256;
-constexpr int kCalTok = 64;  // tokens per partial
+constexpr int kCalTok = 32;  // tokens per partial
+constexpr int kCalMaxLayers = 128;  // layers finished per launch
 
 template <typename QT>
 __device__ __forceinline__ float q_load(const QT* p);
@@ -40,7 +43,80 @@ __device__ __forceinline__ float q_load<uint16_t>(const uint16_t* p) {
     return __uint_as_float((uint32_t)*p << 16);  // bfloat16: the top half of a float
 }
 
-// grid (slot blocks, token chunks); partial[(chunk * HF + slot) * 3 + {re, im, abs}]
+// Four consecutive values of a row as floats (one 16-byte load for fp32,
+// 8 bytes for the 16-bit types).
+template <typename QT>
+__device__ __forceinline__ float4 q_load4(const QT* p);
+template <>
+__device__ __forceinline__ float4 q_load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 q_load4<_Float16>(const _Float16* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xffffu)),
+                       (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16)),
+                       (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xffffu)),
+                       (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16)));
+}
+template <>
+__device__ __forceinline__ float4 q_load4<uint16_t>(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// grid (pair blocks of 256, token chunks).  Lane j of every wavefront takes
+// pairs 4j .. 4j+3 of the block's 256 (F % 4 == 0: never across a head) and
+// wavefront w the tokens t0 + w, t0 + w + 4, ... of the chunk; the four
+// wavefronts' sums are added in LDS in a fixed order and written as
+// partial[(chunk * HF + pair) * 3 + {re, im, abs}].
+constexpr int kCalWaves = kCalThreads / 64;
+
+template <typename QT>
+__global__ __launch_bounds__(kCalThreads) void calib_partial4_kernel(
+    const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
+    double* __restrict__ partial) {
+    __shared__ double sums[kCalWaves][12][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p0 = blockIdx.x * 256 + 4 * lane;
+    const bool in = p0 < HF;
+    const int h = p0 / F, f = p0 - h * F;
+    const int64_t t0 = (int64_t)blockIdx.y * kCalTok;
+    const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
+    const QT* base = q + (int64_t)h * hd + f;
+    double sr[4] = {0.0, 0.0, 0.0, 0.0}, si[4] = {0.0, 0.0, 0.0, 0.0}, sa[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t t = t0 + wave; in && t < t1; t += kCalWaves) {
+        const float4 re = q_load4<QT>(base + t * stride);
+        const float4 im = q_load4<QT>(base + t * stride + F);
+        const float r[4] = {re.x, re.y, re.z, re.w}, m[4] = {im.x, im.y, im.z, im.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sr[k] += (double)r[k];
+            si[k] += (double)m[k];
+            sa[k] += (double)__builtin_amdgcn_sqrtf(fmaf(r[k], r[k], m[k] * m[k]));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        sums[wave][3 * k][lane] = sr[k];
+        sums[wave][3 * k + 1][lane] = si[k];
+        sums[wave][3 * k + 2][lane] = sa[k];
+    }
+    __syncthreads();
+    if (wave == 0 && in) {
+        double* out = partial + ((int64_t)blockIdx.y * HF + p0) * 3;
+#pragma unroll
+        for (int j = 0; j < 12; ++j) {
+            double s = sums[0][j][lane];
+#pragma unroll
+            for (int w = 1; w < kCalWaves; ++w) s += sums[w][j][lane];
+            out[j] = s;
+        }
+    }
+}
+
+// Any F: one pair per thread.
 template <typename QT>
 __global__ __launch_bounds__(kCalThreads) void calib_partial_kernel(
     const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
@@ -76,19 +152,28 @@ __global__ __launch_bounds__(kCalThreads) void calib_reduce_kernel(const double*
     acc[j] += s;
 }
 
-// One layer's outputs from its sums over `count` tokens (zeros if none).
+// Token counts of up to kCalMaxLayers layers, passed by value.
+struct CalCounts {
+    int64_t n[kCalMaxLayers];
+};
+
+// Outputs of layers l0 .. l0 + gridDim.y - 1 from their sums (zeros for a
+// layer with no tokens).
 __global__ __launch_bounds__(kCalThreads) void calib_finish_kernel(const double* __restrict__ acc,
-                                                                   int HF, int64_t count,
+                                                                   int HF, int l0, CalCounts cnt,
                                                                    float* q_re, float* q_im,
                                                                    float* q_abs, float* w) {
     const int i = blockIdx.x * kCalThreads + threadIdx.x;
     if (i >= HF) return;
+    const int l = l0 + (int)blockIdx.y;
+    const int64_t count = cnt.n[blockIdx.y];
+    const int64_t o = (int64_t)l * HF + i;
     const double inv = count > 0 ? 1.0 / (double)count : 0.0;
-    const double mr = acc[3 * i] * inv, mi = acc[3 * i + 1] * inv, ma = acc[3 * i + 2] * inv;
-    q_re[i] = (float)mr;
-    q_im[i] = (float)mi;
-    if (q_abs) q_abs[i] = (float)ma;
-    w[i] = (float)(ma - sqrt(mr * mr + mi * mi));
+    const double mr = acc[3 * o] * inv, mi = acc[3 * o + 1] * inv, ma = acc[3 * o + 2] * inv;
+    q_re[o] = (float)mr;
+    q_im[o] = (float)mi;
+    if (q_abs) q_abs[o] = (float)ma;
+    w[o] = (float)(ma - sqrt(mr * mr + mi * mi));
 }
 
 }  // namespace
@@ -155,19 +240,28 @@ int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, 
         if (e != hipSuccess) return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
         c->partial_bytes = need;
     }
-    const dim3 grid((unsigned)((c->HF + kCalThreads - 1) / kCalThreads), (unsigned)chunks);
-    if (q_type == TRIA_Q_F32)
-        hipLaunchKernelGGL(calib_partial_kernel<float>, grid, dim3(kCalThreads), 0, stream,
-                           static_cast<const float*>(q), n_tokens, row_stride, c->F, c->hd, c->HF,
-                           c->partial);
-    else if (q_type == TRIA_Q_F16)
-        hipLaunchKernelGGL(calib_partial_kernel<_Float16>, grid, dim3(kCalThreads), 0, stream,
-                           static_cast<const _Float16*>(q), n_tokens, row_stride, c->F, c->hd,
-                           c->HF, c->partial);
-    else
-        hipLaunchKernelGGL(calib_partial_kernel<uint16_t>, grid, dim3(kCalThreads), 0, stream,
-                           static_cast<const uint16_t*>(q), n_tokens, row_stride, c->F, c->hd,
-                           c->HF, c->partial);
+    const bool vec = c->F % 4 == 0;
+    // vector path: 256 pairs per block; scalar path: one pair per thread
+    dim3 grid((unsigned)((c->HF + 255) / 256), (unsigned)chunks);
+    // 16-byte (8-byte) loads need the rows aligned: the base and the stride
+    const size_t esz = q_type == TRIA_Q_F32 ? 4 : 2;
+    const bool aligned = (reinterpret_cast<uintptr_t>(q) % (4 * esz)) == 0 && row_stride % 4 == 0;
+    if (q_type == TRIA_Q_F32) {
+        auto k = vec && aligned ? calib_partial4_kernel<float> : calib_partial_kernel<float>;
+        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
+        hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const float*>(q),
+                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+    } else if (q_type == TRIA_Q_F16) {
+        auto k = vec && aligned ? calib_partial4_kernel<_Float16> : calib_partial_kernel<_Float16>;
+        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
+        hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const _Float16*>(q),
+                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+    } else {
+        auto k = vec && aligned ? calib_partial4_kernel<uint16_t> : calib_partial_kernel<uint16_t>;
+        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
+        hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const uint16_t*>(q),
+                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return TRIA_E_HIP;
     const int n3 = 3 * c->HF;
@@ -189,11 +283,12 @@ int tria_calib_finish(tria_calib* c, float* q_re, float* q_im, float* q_abs, flo
                       hipStream_t stream) {
     if (!c || !q_re || !q_im || !norm_w) return TRIA_E_INVAL;
     const unsigned blocks = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
-    for (int l = 0; l < c->L; ++l) {
-        const int64_t o = (int64_t)l * c->HF;
-        hipLaunchKernelGGL(calib_finish_kernel, dim3(blocks), dim3(kCalThreads), 0, stream,
-                           c->acc + o * 3, c->HF, c->count[l], q_re + o, q_im + o,
-                           q_abs ? q_abs + o : nullptr, norm_w + o);
+    for (int l0 = 0; l0 < c->L; l0 += kCalMaxLayers) {
+        const int nl = c->L - l0 < kCalMaxLayers ? c->L - l0 : kCalMaxLayers;
+        CalCounts cnt;
+        for (int j = 0; j < kCalMaxLayers; ++j) cnt.n[j] = j < nl ? c->count[l0 + j] : 0;
+        hipLaunchKernelGGL(calib_finish_kernel, dim3(blocks, (unsigned)nl), dim3(kCalThreads), 0,
+                           stream, c->acc, c->HF, l0, cnt, q_re, q_im, q_abs, norm_w);
         if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;
     }
     return TRIA_OK;

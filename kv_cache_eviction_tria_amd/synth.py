@@ -269,3 +269,31 @@ def append_paged(pg: dict, s: int, n: int, m: int, first_pos: int, L: int, Hkv: 
     pools[0][:, blk, :, within] = k.permute(2, 0, 1, 3)
     pools[1][:, blk, :, within] = v.permute(2, 0, 1, 3)
     pools[2][:, blk, :, within] = pos.view(m, 1, 1).expand(m, L, Hkv)
+
+
+# --------------------------------------------------------------------------
+# Calibration query streams
+# --------------------------------------------------------------------------
+
+# name -> (layers, query heads, head_dim, tokens, dtype): a Qwen3-8B-shaped
+# stream of pre-RoPE query rows, the size of one calibration sample (the
+# llama.cpp page suggests 512-2K tokens per sample).
+CALIB_WORKLOADS = {
+    "calib_qwen3_8b_2k_f32": (36, 32, 128, 2048, torch.float32),
+}
+
+
+def gen_query_stream(L: int, Hq: int, hd: int, T: int, dtype, seed: int, device):
+    """Per layer a device tensor [T, Hq*hd]: a fixed per-(head, dim) mean direction
+    (lognormal size, uniform phase per pair) plus N(0,1) noise per token."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    F = hd // 2
+    out = []
+    for _ in range(L):
+        mag = torch.exp(torch.randn(Hq, F, generator=g))
+        ph = torch.rand(Hq, F, generator=g) * (2 * np.pi)
+        mean = torch.cat([mag * torch.cos(ph), mag * torch.sin(ph)], dim=1)  # [Hq, hd]
+        noise = torch.randn(T, Hq, hd, generator=g)
+        out.append((noise + mean).reshape(T, Hq * hd).to(dtype).to(device))
+    return out
+
