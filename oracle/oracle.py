@@ -17,6 +17,9 @@ the passages of the source pages each step follows:
   cache): the worklog's per-head keep sets gathered in every layer and the
   llama.cpp page's global z-normalisation shader; the cross-unit reduction is
   read as the GQA group's max taken over the larger group.
+* Decode attention over a (compacted) cache: softmax of scaled q.k over the
+  unit's rows, weights times V, per query head of the GQA group -- the step
+  the eviction pass exists to make cheaper.
 * Calibration statistics: per query head and frequency pair, the mean
   pre-RoPE query pair, the mean pair magnitude and the norm weight
   q_abs - |q_mean| (llama.cpp page section 2, the generator's accumulation).
@@ -107,6 +110,9 @@ def _load():
             lib.orc_evict_ex.argtypes = [i32, i32] + lib.orc_evict.argtypes
             lib.orc_compact_holefill.restype = i64
             lib.orc_compact_holefill.argtypes = [vp, i64, vp, i64, i64]
+            lib.orc_decode_attention_unit.restype = i32
+            lib.orc_decode_attention_unit.argtypes = [i32, i32, vp, vp, i64, i32, i32, vp, dbl,
+                                                      vp]
             lib.orc_calib_stats.restype = None
             lib.orc_calib_stats.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
             lib.orc_num_threads.restype = i32
@@ -220,6 +226,21 @@ def compact_holefill(rows: np.ndarray, keep_idx: np.ndarray, n: int):
     if moves < 0:
         raise MemoryError("oracle hole-fill compaction failed")
     return out, int(moves)
+
+
+def decode_attention_unit(k_type: int, v_type: int, k_rows: np.ndarray, v_rows: np.ndarray,
+                          hd: int, q: np.ndarray, scale: float) -> np.ndarray:
+    """k_rows, v_rows: uint8 [n, row_bytes]; q: [G, hd].  Returns out [G, hd] fp64."""
+    k_rows = _c(k_rows, np.uint8).reshape(-1, row_bytes(k_type, hd))
+    v_rows = _c(v_rows, np.uint8).reshape(-1, row_bytes(v_type, hd))
+    q = _c(q, np.float64).reshape(-1, hd)
+    out = np.empty_like(q)
+    rc = _load().orc_decode_attention_unit(k_type, v_type, _p(k_rows), _p(v_rows),
+                                           k_rows.shape[0], hd, q.shape[0], _p(q), float(scale),
+                                           _p(out))
+    if rc != 0:
+        raise ValueError("oracle decode attention failed")
+    return out
 
 
 def calib_stats(q: np.ndarray):

@@ -543,6 +543,55 @@ int64_t orc_evict(int k_type, int v_type, int L, int Hkv, int Hq, int hd, double
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode attention over the cache.                                          */
+/* ------------------------------------------------------------------------ */
+
+/* One decode step's attention for one (layer, KV head) unit: the G query
+ * heads of the KV head ([LC] section 4's GQA grouping, query head g*G + j)
+ * attend to the unit's n cached rows -- the rows an eviction pass leaves,
+ * whatever their order ([WL] "What was implemented": decode continues on the
+ * compacted cache; attention weights do not depend on the row order):
+ *   s_j(r) = scale * q_j . k_r,   p_j(r) = exp(s_j(r)) / sum_r' exp(s_j(r')),
+ *   out_j  = sum_r p_j(r) v_r.
+ * q: [G][hd]; k_rows / v_rows: n stored rows (decoded exactly); out: [G][hd].
+ * Returns 0, or -1 on a bad row type. */
+int orc_decode_attention_unit(int k_type, int v_type, const uint8_t *k_rows,
+                              const uint8_t *v_rows, int64_t n, int hd, int G, const double *q,
+                              double scale, double *out)
+{
+    int64_t kb = orc_row_bytes(k_type, hd), vb = orc_row_bytes(v_type, hd);
+    if (kb < 0 || vb < 0) return -1;
+    double *kd = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *vd = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)G);
+    if (!kd || !vd || !s) { free(kd); free(vd); free(s); return -1; }
+    for (int64_t r = 0; r < n; r++) {
+        orc_decode_row(k_type, k_rows + r * kb, hd, kd);
+        for (int j = 0; j < G; j++) {
+            double d = 0.0;
+            for (int e = 0; e < hd; e++) d += q[j * hd + e] * kd[e];
+            s[r * G + j] = scale * d;
+        }
+    }
+    for (int j = 0; j < G; j++) {
+        double mx = -INFINITY;
+        for (int64_t r = 0; r < n; r++) mx = s[r * G + j] > mx ? s[r * G + j] : mx;
+        double den = 0.0;
+        for (int64_t r = 0; r < n; r++) den += exp(s[r * G + j] - mx);
+        for (int e = 0; e < hd; e++) out[j * hd + e] = 0.0;
+        for (int64_t r = 0; r < n; r++) {
+            double pr = exp(s[r * G + j] - mx) / den;
+            orc_decode_row(v_type, v_rows + r * vb, hd, vd);
+            for (int e = 0; e < hd; e++) out[j * hd + e] += pr * vd[e];
+        }
+    }
+    free(kd);
+    free(vd);
+    free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Calibration statistics.                                                    */
 /* ------------------------------------------------------------------------ */
 

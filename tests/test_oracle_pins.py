@@ -689,3 +689,66 @@ def test_calib_opposite_halves_and_scaling():
     assert np.allclose(b[0], -3.0 * a[0], rtol=1e-12) and np.allclose(b[1], -3.0 * a[1], rtol=1e-12)
     assert np.allclose(b[2], 3.0 * a[2], rtol=1e-12) and np.allclose(b[3], 3.0 * a[3], rtol=1e-11)
     assert np.all(a[3] >= -1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Decode attention
+# ---------------------------------------------------------------------------
+
+def _rows_f16(x):
+    return np.ascontiguousarray(x.astype(np.float16)).view(np.uint8).reshape(x.shape[0], -1)
+
+
+def test_attention_equal_keys_average_the_values():
+    """Every key the same: uniform weights, the output is the mean of V (any scale)."""
+    rng = np.random.default_rng(70)
+    hd, n = 32, 37
+    k = np.broadcast_to(rng.standard_normal(hd), (n, hd))
+    v = rng.standard_normal((n, hd)).astype(np.float16)
+    q = rng.standard_normal((3, hd))
+    out = oracle.decode_attention_unit(oracle.KV_F16, oracle.KV_F16, _rows_f16(k), _rows_f16(v),
+                                       hd, q, 0.7)
+    want = v.astype(np.float64).mean(axis=0)
+    assert np.allclose(out, np.broadcast_to(want, out.shape), atol=1e-12)
+
+
+def test_attention_two_rows_closed_form_and_order():
+    """Two rows: weights are a logistic function of the score gap; permuting the rows
+    (a compaction's order) changes nothing; a dominant key returns its own V."""
+    hd = 16
+    k = np.zeros((2, hd)); k[0, 0] = 1.0; k[1, 1] = 1.0
+    v = np.zeros((2, hd)); v[0, :] = 2.0; v[1, :] = -1.0
+    q = np.zeros((1, hd)); q[0, 0] = 3.0; q[0, 1] = 1.0
+    sc = 0.5
+    out = oracle.decode_attention_unit(oracle.KV_F16, oracle.KV_F16, _rows_f16(k), _rows_f16(v),
+                                       hd, q, sc)
+    p0 = 1.0 / (1.0 + np.exp(-sc * (3.0 - 1.0)))
+    assert np.allclose(out[0], p0 * 2.0 + (1 - p0) * -1.0, atol=1e-14)
+    outp = oracle.decode_attention_unit(oracle.KV_F16, oracle.KV_F16, _rows_f16(k[::-1]),
+                                        _rows_f16(v[::-1]), hd, q, sc)
+    assert np.allclose(out, outp, atol=1e-15)
+    big = oracle.decode_attention_unit(oracle.KV_F16, oracle.KV_F16, _rows_f16(k), _rows_f16(v),
+                                       hd, q * 200.0, sc)
+    assert np.allclose(big[0], 2.0, atol=1e-12)
+
+
+def test_attention_q8_rows_equal_the_decoded_fp16_rows():
+    """q8_0 keys holding values that fp16 also represents exactly give the same output
+    as the fp16 rows."""
+    rng = np.random.default_rng(71)
+    hd, n = 64, 20
+    d = np.float16(0.125)
+    qv = rng.integers(-100, 101, size=(n, hd)).astype(np.int8)
+    blocks = []
+    for r in range(n):
+        row = b""
+        for b_ in range(hd // 32):
+            row += np.array([d]).view(np.uint8).tobytes() + qv[r, 32 * b_:32 * b_ + 32].tobytes()
+        blocks.append(np.frombuffer(row, np.uint8))
+    k8 = np.stack(blocks)
+    k16 = _rows_f16(qv.astype(np.float64) * 0.125)
+    v = _rows_f16(rng.standard_normal((n, hd)))
+    q = rng.standard_normal((2, hd))
+    a = oracle.decode_attention_unit(oracle.KV_Q8_0, oracle.KV_F16, k8, v, hd, q, 0.1)
+    b = oracle.decode_attention_unit(oracle.KV_F16, oracle.KV_F16, k16, v, hd, q, 0.1)
+    assert np.allclose(a, b, atol=1e-13)
