@@ -252,6 +252,24 @@ int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
 #define TRIA_COMPACT_HOLE_FILL 1
 int tria_set_compaction(tria_ctx *ctx, int32_t mode);
 
+/* One decode step's attention over the cache -- the cost an eviction pass
+ * cuts ("TriAttention Native C++ Worklog", "What was implemented": decode
+ * continues on the compacted cache).  For every layer and query head h =
+ * g*G + j (KV head g):
+ *   out_h = sum_r softmax_r(scale * q_h . k_r) v_r   over the unit's n rows.
+ * Row order does not matter (ordered or hole-filled caches alike).
+ *   q, out : device fp32 [L][Hq][head_dim] (q already rotated for its
+ *            position; the keys are stored rotated); n_tokens = 0 gives zeros.
+ * fp32 arithmetic; every K and V row is read once.  Scratch (per-range
+ * partial results) is owned by the context. */
+int tria_decode_attention(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
+                          const float *q, float scale, float *out, hipStream_t stream);
+
+/* The same over n_seq sequences of a paged cache: q, out [n_seq][L][Hq][hd]. */
+int tria_decode_attention_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache,
+                                      int32_t n_seq, const int64_t *n_tokens, const float *q,
+                                      float scale, float *out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Calibration statistics (the stats tria_load_stats takes), accumulated on
  * the GPU from pre-RoPE query vectors: the llama.cpp page ("TriAttention

@@ -15,6 +15,12 @@ hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float*
                           PartRec* part, hipStream_t s);
 hipError_t launch_holefill(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,
                            hipStream_t s);
+void attention_splits(const Batch& b, int n_units, int* n_split, int* rows_per_split);
+hipError_t launch_attention(const CacheView& cv, const Batch& b, int n_units, int G, int hd,
+                            int k_type, int v_type, const float* q, float scale, int n_split,
+                            int rows_per_split, void* parts, float* pacc, float* out,
+                            hipStream_t s);
+size_t attention_part_bytes();
 hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const float* raw,
                               const PartRec* part, int32_t* keep, float* agg,
                               uint32_t* key_scratch, int32_t* chunk_pb, uint32_t* ticket,
@@ -61,6 +67,11 @@ struct tria_ctx {
     // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
     int keep_mode = TRIA_KEEP_PER_UNIT;
     int compact_mode = TRIA_COMPACT_ORDERED;  // tria_set_compaction
+    // decode attention (tria_decode_attention*): per-split partial results
+    void* att_parts = nullptr;
+    size_t att_parts_bytes = 0;
+    float* att_acc = nullptr;
+    size_t att_acc_bytes = 0;
     HeadNorm* norms = nullptr;
     size_t norms_bytes = 0;
     float* gagg = nullptr;
@@ -409,9 +420,72 @@ int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) 
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
 
+// One decode step's attention over every unit of the batch (q, out: [seq][L]
+// [Hq][hd] fp32).
+int run_attention(tria_ctx* ctx, const CacheView& cv, const Batch& b, const float* q, float scale,
+                  float* out, hipStream_t s) {
+    const int units = b.n_seq * ctx->L * ctx->Hkv;
+    int n_split = 1, rps = 64;
+    attention_splits(b, units, &n_split, &rps);
+    const size_t recs = (size_t)units * n_split * ctx->G;
+    int rc = grow(ctx, &ctx->att_parts, &ctx->att_parts_bytes, recs * attention_part_bytes(), s);
+    if (!rc)
+        rc = grow(ctx, reinterpret_cast<void**>(&ctx->att_acc), &ctx->att_acc_bytes,
+                  recs * ctx->hd * sizeof(float), s);
+    if (rc) return rc;
+    const hipError_t e = launch_attention(cv, b, units, ctx->G, ctx->hd, ctx->k_type, ctx->v_type,
+                                          q, scale, n_split, rps, ctx->att_parts, ctx->att_acc,
+                                          out, s);
+    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+}
+
 }  // namespace
 
 extern "C" {
+
+int tria_decode_attention(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, const float* q,
+                          float scale, float* out, hipStream_t stream) {
+    if (!ctx || !q || !out) return TRIA_E_INVAL;
+    int rc = check_cache(cache, n_tokens);
+    if (rc) return rc;
+    Protect p;
+    p.kept = n_tokens;
+    p.s_end = p.w_start = n_tokens;
+    const Batch b = one_seq(n_tokens, p);
+    return run_attention(ctx, view_of(ctx, cache), b, q, scale, out, stream);
+}
+
+int tria_decode_attention_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t n_seq,
+                                      const int64_t* n_tokens, const float* q, float scale,
+                                      float* out, hipStream_t stream) {
+    if (!ctx || !cache || !n_tokens || !q || !out) return TRIA_E_INVAL;
+    if (!cache->k_pool || !cache->v_pool || !cache->pos_pool || !cache->block_table)
+        return TRIA_E_INVAL;
+    if (n_seq < 1 || n_seq > TRIA_MAX_SEQ || cache->n_blocks < 1 || cache->max_blocks < 1)
+        return TRIA_E_INVAL;
+    Batch b;
+    memset(&b, 0, sizeof(b));
+    b.n_seq = n_seq;
+    for (int i = 0; i < n_seq; ++i) {
+        if (n_tokens[i] < 0 || n_tokens[i] > (int64_t)cache->max_blocks * TRIA_BLOCK)
+            return TRIA_E_INVAL;
+        b.seq[i].n = n_tokens[i];
+        b.seq[i].kept = n_tokens[i];
+    }
+    CacheView cv;
+    cv.k = static_cast<uint8_t*>(cache->k_pool);
+    cv.v = static_cast<uint8_t*>(cache->v_pool);
+    cv.pos = cache->pos_pool;
+    cv.cap = 0;
+    cv.n_blocks = cache->n_blocks;
+    cv.bt = cache->block_table;
+    cv.max_blocks = cache->max_blocks;
+    cv.L = ctx->L;
+    cv.Hkv = ctx->Hkv;
+    cv.kb = ctx->kb;
+    cv.vb = ctx->vb;
+    return run_attention(ctx, cv, b, q, scale, out, stream);
+}
 
 const char* tria_strerror(int code) {
     switch (code) {
@@ -444,7 +518,7 @@ void tria_free(tria_ctx* ctx) {
     void* bufs[] = {ctx->q_re, ctx->q_im, ctx->w,    ctx->omega, ctx->m_re,      ctx->m_im,
                     ctx->coef, ctx->raw,  ctx->keep, ctx->keys,  ctx->part,      ctx->pb,
                     ctx->cst.flags,       ctx->cst.err,          ctx->cst.ticket,
-                    ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb};
+                    ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb, ctx->att_parts, ctx->att_acc};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     if (ctx->aux) (void)hipStreamDestroy(ctx->aux);

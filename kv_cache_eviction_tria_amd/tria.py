@@ -96,6 +96,12 @@ def lib():
             L.tria_set_keep_mode.argtypes = [vp, i32]
             L.tria_set_compaction.restype = ctypes.c_int
             L.tria_set_compaction.argtypes = [vp, i32]
+            L.tria_decode_attention.restype = ctypes.c_int
+            L.tria_decode_attention.argtypes = [vp, ctypes.POINTER(Cache), i64, vp,
+                                                ctypes.c_float, vp, vp]
+            L.tria_decode_attention_paged_batch.restype = ctypes.c_int
+            L.tria_decode_attention_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32,
+                                                            vp, vp, ctypes.c_float, vp, vp]
             L.tria_calib_create.restype = ctypes.c_int
             L.tria_calib_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
             L.tria_calib_add.restype = ctypes.c_int
@@ -251,6 +257,42 @@ def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, 
     _check(lib().tria_evict_paged_batch(ctx.handle, ctypes.byref(pc), n_seq, nt, bd, sink,
                                         window, kept, _stream(stream)), "tria_evict_paged_batch")
     return [int(x) for x in kept]
+
+
+def tria_decode_attention(ctx: TriaCtx, k, v, pos, n_tokens: int, q, scale=None, out=None,
+                          stream=None):
+    """q: device fp32 [L, Hq, hd]; returns out (device fp32 [L, Hq, hd]).  scale
+    defaults to 1/sqrt(hd)."""
+    if scale is None:
+        scale = 1.0 / float(ctx.head_dim) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    cache = _cache(k, v, pos)
+    _check(lib().tria_decode_attention(ctx.handle, ctypes.byref(cache), int(n_tokens),
+                                       _ptr(q, "q", torch.float32), float(scale),
+                                       _ptr(out, "out", torch.float32), _stream(stream)),
+           "tria_decode_attention")
+    return out
+
+
+def tria_decode_attention_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table,
+                                      n_tokens, q, scale=None, out=None, stream=None):
+    """q: device fp32 [n_seq, L, Hq, hd]; returns out of the same shape."""
+    if scale is None:
+        scale = 1.0 / float(ctx.head_dim) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    n_seq = len(n_tokens)
+    nt = (ctypes.c_int64 * n_seq)(*[int(x) for x in n_tokens])
+    pc = PagedCache(_ptr(k_pool, "k_pool", torch.uint8), _ptr(v_pool, "v_pool", torch.uint8),
+                    _ptr(pos_pool, "pos_pool", torch.int32), pos_pool.shape[1],
+                    _ptr(block_table, "block_table", torch.int32), block_table.shape[1])
+    _check(lib().tria_decode_attention_paged_batch(ctx.handle, ctypes.byref(pc), n_seq, nt,
+                                                   _ptr(q, "q", torch.float32), float(scale),
+                                                   _ptr(out, "out", torch.float32),
+                                                   _stream(stream)),
+           "tria_decode_attention_paged_batch")
+    return out
 
 
 def tria_set_pipeline(ctx: TriaCtx, layers_per_group: int) -> None:

@@ -646,3 +646,94 @@ def test_calib_feeds_the_eviction_pass():
     pu.compare_pass(g, o, n, B, S, W, "calibrated stats")
     ctx.close()
     cal.close()
+
+
+# ---------------------------------------------------------------------------
+# Decode attention over the (compacted) cache
+# ---------------------------------------------------------------------------
+
+def _att_check(g, o, where):
+    """Bar: |g - o| <= 1e-4 * max(max|o|, 1e-2) per head (fp32 scores, softmax and
+    sums over up to 10^5 rows against fp64)."""
+    tol = 1e-4 * max(float(np.abs(o).max()), 1e-2)
+    err = float(np.abs(g.astype(np.float64) - o).max())
+    assert err <= tol, "%s: max err %g > %g" % (where, err, tol)
+
+
+@pytest.mark.parametrize("k_type,hd,G,n", [(Q8, 128, 4, 3000), (F16, 128, 4, 2500),
+                                           (F16, 256, 4, 700), (Q8, 64, 1, 129),
+                                           (F16, 96, 12, 65), (Q8, 128, 4, 1), (F16, 128, 4, 0)],
+                         ids=lambda x: str(x))
+def test_decode_attention_matches_the_oracle(k_type, hd, G, n):
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="att", L=2, Hkv=2, Hq=2 * G, hd=hd,
+                 k_type=k_type)
+    pu.say("case attention k%d hd%d G%d n%d" % (k_type, hd, G, n))
+    case = synth.make_case(wl, device="cpu", n=max(n, 1))
+    stats = (case["q_re"], case["q_im"], case["w"])
+    rng = np.random.default_rng(80 + hd + G)
+    q = rng.standard_normal((wl.L, wl.Hq, hd)).astype(np.float32)
+    ctx = pu.make_ctx(wl, stats)
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    scale = 1.0 / np.sqrt(hd)
+    out = pu.host(tria.tria_decode_attention(ctx, k, v, pos, n, torch.from_numpy(q).to(DEV)))
+    kk, vv = case["k"].numpy(), case["v"].numpy()
+    for l in range(wl.L):
+        for g in range(wl.Hkv):
+            hs = slice(g * G, g * G + G)
+            if n == 0:
+                assert np.all(out[l, hs] == 0.0)
+                continue
+            o = oracle.decode_attention_unit(k_type, wl.v_type, kk[l, g, :n], vv[l, g, :n], hd,
+                                             q[l, hs], scale)
+            _att_check(out[l, hs], o, "unit (%d,%d)" % (l, g))
+    ctx.close()
+
+
+@pytest.mark.parametrize("compaction", ["ordered", "hole_fill"])
+def test_decode_attention_after_eviction(compaction):
+    """Attention over the rows an eviction pass keeps equals the oracle's attention over
+    exactly those rows (any order)."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="att_evict", L=3, Hkv=2, Hq=8, k_type=Q8)
+    n, B, S, W = 6000, 1500, 4, 256
+    case = synth.make_case(wl, device="cpu", n=n)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    ctx = pu.make_ctx(wl, stats)
+    if compaction == "hole_fill":
+        tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    K = tria.tria_evict(ctx, k, v, pos, n, B, S, W)
+    q = np.random.default_rng(81).standard_normal((wl.L, wl.Hq, wl.hd)).astype(np.float32)
+    out = pu.host(tria.tria_decode_attention(ctx, k, v, pos, K, torch.from_numpy(q).to(DEV)))
+    kept = pu.host(pos)[:, :, :K]
+    kk, vv = case["k"].numpy(), case["v"].numpy()
+    for l in range(wl.L):
+        for g in range(wl.Hkv):
+            rows = kept[l, g]  # positions were 0..n-1: the kept original rows
+            o = oracle.decode_attention_unit(wl.k_type, wl.v_type, kk[l, g, rows], vv[l, g, rows],
+                                             wl.hd, q[l, g * wl.G:(g + 1) * wl.G],
+                                             1.0 / np.sqrt(wl.hd))
+            _att_check(out[l, g * wl.G:(g + 1) * wl.G], o, "%s unit (%d,%d)" % (compaction, l, g))
+    ctx.close()
+
+
+def test_decode_attention_paged_batch():
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="att_paged", L=2, Hkv=2, Hq=8, hd=128)
+    lens = [1000, 17, 2100]
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 82)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 8)
+    ctx = pu.make_ctx(wl, stats)
+    dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+    q = np.random.default_rng(83).standard_normal((len(lens), wl.L, wl.Hq, wl.hd)).astype(np.float32)
+    out = pu.host(tria.tria_decode_attention_paged_batch(
+        ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"], dev["block_table"], lens,
+        torch.from_numpy(q).to(DEV)))
+    for s, n in enumerate(lens):
+        kk = synth.paged_rows(pg["k_pool"], pg["block_table"][s], n).numpy()
+        vv = synth.paged_rows(pg["v_pool"], pg["block_table"][s], n).numpy()
+        for l in range(wl.L):
+            for g in range(wl.Hkv):
+                o = oracle.decode_attention_unit(wl.k_type, wl.v_type, kk[l, g], vv[l, g], wl.hd,
+                                                 q[s, l, g * wl.G:(g + 1) * wl.G],
+                                                 1.0 / np.sqrt(wl.hd))
+                _att_check(out[s, l, g * wl.G:(g + 1) * wl.G], o, "seq %d unit (%d,%d)" % (s, l, g))
+    ctx.close()
