@@ -252,6 +252,61 @@ int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
 #define TRIA_COMPACT_HOLE_FILL 1
 int tria_set_compaction(tria_ctx *ctx, int32_t mode);
 
+/* ------------------------------------------------------------------------
+ * Decode-loop policy: when a pass runs, and with which arguments.
+ *   TRIA_TRIGGER_THRESHOLD ("TriAttention Native C++ Worklog", sections
+ *     "4. Separate physical cache limit from logical TriAttention budget" and
+ *     the compaction-trigger notes): a pass runs once the counted rows reach
+ *     budget + divide_length and keeps `budget` counted rows (the logged
+ *     schedule: 3200 rows -> 3072 every 128 decode steps at budget 3072,
+ *     divide length 128).  With protect_prefill the prompt rows are neither
+ *     counted nor evicted (decode-only accounting; prompt state is never
+ *     compacted while it is being built).
+ *   TRIA_TRIGGER_INTERVAL (llama.cpp page, section 1 --tri-interval; section 5
+ *     "Phase B": the evictor fires in decode only): a pass runs every
+ *     `interval` decode steps once the counted rows exceed the budget.
+ * Passes never run during prefill: the caller sets n_prompt after prefill and
+ * calls tria_decode_step once per decode step.
+ * ------------------------------------------------------------------------ */
+#define TRIA_TRIGGER_THRESHOLD 0
+#define TRIA_TRIGGER_INTERVAL 1
+
+typedef struct {
+    int32_t trigger;         /* TRIA_TRIGGER_* */
+    int32_t protect_prefill; /* 1: the prompt rows are kept and not counted */
+    int64_t budget;          /* counted rows a pass keeps (>= 1) */
+    int64_t divide_length;   /* THRESHOLD: slack before a pass runs (>= 1) */
+    int64_t interval;        /* INTERVAL: decode steps between passes (>= 1) */
+    int64_t sink, window;    /* as for tria_evict (>= 0) */
+} tria_policy;
+
+typedef struct {
+    int64_t n_rows;   /* rows in the cache, the newest last */
+    int64_t n_prompt; /* prompt rows at the front (0 if none) */
+    int64_t steps;    /* decode steps since the last pass (or since the prompt) */
+    int64_t passes;   /* passes run so far */
+} tria_decode_state;
+
+/* Host-only decision for the current state: returns 1 and the arguments of
+ * the pass (for tria_evict) if one is due, 0 if not, TRIA_E_INVAL on a bad
+ * policy or state.  With protect_prefill the pass keeps budget + n_prompt
+ * rows with sink max(sink, n_prompt). */
+int tria_policy_due(const tria_policy *p, const tria_decode_state *st, int64_t *budget_rows,
+                    int64_t *sink_rows, int64_t *window_rows);
+
+/* Physical rows a cache must hold so that appending one row per decode step
+ * never overflows before the policy's pass runs (the worklog's fix for
+ * prompt-time overflow: physical capacity above the logical budget).  Returns
+ * the row count or TRIA_E_INVAL. */
+int64_t tria_policy_peak_rows(const tria_policy *p, int64_t n_prompt);
+
+/* One decode step, after the caller appended this step's row (st->n_rows
+ * counts it): counts the step, runs tria_evict if the policy says so (on
+ * `stream`), and updates the state.  Returns the rows now in the cache, or an
+ * error code (TRIA_E_INVAL also when n_rows exceeds the cache's capacity). */
+int64_t tria_decode_step(tria_ctx *ctx, const tria_cache *cache, const tria_policy *p,
+                         tria_decode_state *st, hipStream_t stream);
+
 /* One decode step's attention over the cache -- the cost an eviction pass
  * cuts ("TriAttention Native C++ Worklog", "What was implemented": decode
  * continues on the compacted cache).  For every layer and query head h =

@@ -15,7 +15,8 @@ LIB = os.path.join(LIBDIR, "libtria.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["tria_prep.hip", "tria_score.hip", "tria_select.hip", "tria_group.hip", "tria_compact.hip",
-           "tria_holefill.hip", "tria_calib.hip", "tria_attention.hip", "tria_api.hip"]
+           "tria_holefill.hip", "tria_calib.hip", "tria_attention.hip", "tria_runtime.hip",
+           "tria_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -56,6 +56,20 @@ class PagedCache(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32)]
 
 
+class Policy(ctypes.Structure):
+    """tria_policy: when the decode loop runs an eviction pass."""
+    _fields_ = [("trigger", ctypes.c_int32), ("protect_prefill", ctypes.c_int32),
+                ("budget", ctypes.c_int64), ("divide_length", ctypes.c_int64),
+                ("interval", ctypes.c_int64), ("sink", ctypes.c_int64),
+                ("window", ctypes.c_int64)]
+
+
+class DecodeState(ctypes.Structure):
+    """tria_decode_state: rows in the cache, prompt rows, steps since the last pass."""
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_prompt", ctypes.c_int64),
+                ("steps", ctypes.c_int64), ("passes", ctypes.c_int64)]
+
+
 def lib():
     """Load libtria.so (raises if it has not been built)."""
     global _lib
@@ -102,6 +116,15 @@ def lib():
             L.tria_decode_attention_paged_batch.restype = ctypes.c_int
             L.tria_decode_attention_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32,
                                                             vp, vp, ctypes.c_float, vp, vp]
+            L.tria_policy_due.restype = ctypes.c_int
+            L.tria_policy_due.argtypes = [ctypes.POINTER(Policy), ctypes.POINTER(DecodeState),
+                                          ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                          ctypes.POINTER(i64)]
+            L.tria_policy_peak_rows.restype = i64
+            L.tria_policy_peak_rows.argtypes = [ctypes.POINTER(Policy), i64]
+            L.tria_decode_step.restype = i64
+            L.tria_decode_step.argtypes = [vp, ctypes.POINTER(Cache), ctypes.POINTER(Policy),
+                                           ctypes.POINTER(DecodeState), vp]
             L.tria_calib_create.restype = ctypes.c_int
             L.tria_calib_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
             L.tria_calib_add.restype = ctypes.c_int
@@ -313,6 +336,32 @@ def tria_set_keep_mode(ctx: TriaCtx, mode: int) -> None:
 
 TRIA_COMPACT_ORDERED = 0
 TRIA_COMPACT_HOLE_FILL = 1
+
+TRIA_TRIGGER_THRESHOLD = 0
+TRIA_TRIGGER_INTERVAL = 1
+
+
+def tria_policy_due(policy: Policy, state: DecodeState):
+    """(budget, sink, window) of the pass due now, or None."""
+    b, s_, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = _check(lib().tria_policy_due(ctypes.byref(policy), ctypes.byref(state), ctypes.byref(b),
+                                      ctypes.byref(s_), ctypes.byref(w)), "tria_policy_due")
+    return (b.value, s_.value, w.value) if rc == 1 else None
+
+
+def tria_policy_peak_rows(policy: Policy, n_prompt: int) -> int:
+    return int(_check(lib().tria_policy_peak_rows(ctypes.byref(policy), int(n_prompt)),
+                      "tria_policy_peak_rows"))
+
+
+def tria_decode_step(ctx: TriaCtx, k, v, pos, policy: Policy, state: DecodeState,
+                     stream=None) -> int:
+    """One decode step after the caller appended its row; returns the rows now held."""
+    cache = _cache(k, v, pos)
+    return int(_check(lib().tria_decode_step(ctx.handle, ctypes.byref(cache),
+                                             ctypes.byref(policy), ctypes.byref(state),
+                                             _stream(stream)), "tria_decode_step"))
+
 
 TRIA_Q_F32 = 0
 TRIA_Q_F16 = 1

@@ -737,3 +737,73 @@ def test_decode_attention_paged_batch():
                                                  1.0 / np.sqrt(wl.hd))
                 _att_check(out[s, l, g * wl.G:(g + 1) * wl.G], o, "seq %d unit (%d,%d)" % (s, l, g))
     ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# Decode loop: policy + passes + attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("compaction", ["ordered", "hole_fill"])
+def test_decode_loop(compaction):
+    """A prompt of 300 rows, then 700 decode steps appending one fresh row each with a
+    threshold policy (budget 400, divide length 64, prompt protected): every pass runs
+    when the policy says, keeps the rows the oracle keeps on the same input (cutoff band)
+    with exact gathers, never touches the prompt rows; attention after the last step
+    matches the oracle over the rows held."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="loop", L=2, Hkv=2, Hq=8, k_type=Q8)
+    P, steps, cap = 300, 700, 1200
+    pol = tria.Policy(trigger=tria.TRIA_TRIGGER_THRESHOLD, protect_prefill=1, budget=400,
+                      divide_length=64, interval=1, sink=0, window=48)
+    assert tria.tria_policy_peak_rows(pol, P) <= cap
+    full = synth.make_case(wl, device="cpu", n=P + steps, cap=P + steps)
+    stats = (full["q_re"], full["q_im"], full["w"])
+    ctx = pu.make_ctx(wl, stats)
+    if compaction == "hole_fill":
+        tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    k = torch.zeros(wl.L, wl.Hkv, cap, full["k"].shape[-1], dtype=torch.uint8, device=DEV)
+    v = torch.zeros(wl.L, wl.Hkv, cap, full["v"].shape[-1], dtype=torch.uint8, device=DEV)
+    pos = torch.zeros(wl.L, wl.Hkv, cap, dtype=torch.int32, device=DEV)
+    src = [full[x].to(DEV) for x in ("k", "v", "pos")]
+    k[:, :, :P], v[:, :, :P], pos[:, :, :P] = src[0][:, :, :P], src[1][:, :, :P], src[2][:, :, :P]
+    st = tria.DecodeState(n_rows=P, n_prompt=P, steps=0, passes=0)
+    prompt_k = pu.host(k)[:, :, :P].copy()
+    n_pass = 0
+    for t in range(steps):
+        n = st.n_rows
+        k[:, :, n], v[:, :, n], pos[:, :, n] = src[0][:, :, P + t], src[1][:, :, P + t], src[2][:, :, P + t]
+        st.n_rows += 1
+        probe = tria.DecodeState(n_rows=st.n_rows, n_prompt=P, steps=st.steps + 1, passes=0)
+        due = tria.tria_policy_due(pol, probe)
+        before = [pu.host(x)[:, :, :st.n_rows].copy() for x in (k, v, pos)] if due else None
+        rows = tria.tria_decode_step(ctx, k, v, pos, pol, st)
+        if due is None:
+            assert rows == probe.n_rows
+            continue
+        n_pass += 1
+        b, s, w = due
+        assert (b, s) == (400 + P, P)
+        K = tria.tria_kept_count(probe.n_rows, b, s, w)
+        assert rows == K == st.n_rows
+        k0, v0, p0 = before
+        o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                         list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), probe.n_rows, b, s, w,
+                         *stats, compact=False)
+        ka, pa = pu.host(k), pu.host(pos)
+        for l in range(wl.L):
+            for g in range(wl.Hkv):
+                row_of = {int(p): i for i, p in enumerate(p0[l, g])}
+                gkeep = np.array(sorted(row_of[int(p)] for p in pa[l, g, :K]), np.int32)
+                pu.check_kept(gkeep, o["keep_idx"][l, g], o["agg"][l, g], probe.n_rows, b, s, w,
+                              "%s pass %d unit (%d,%d)" % (compaction, n_pass, l, g))
+                assert np.array_equal(ka[l, g, :P], prompt_k[l, g])
+    assert n_pass == st.passes == 1 + (steps - (400 + 64)) // 64
+    q = np.random.default_rng(90).standard_normal((wl.L, wl.Hq, wl.hd)).astype(np.float32)
+    out = pu.host(tria.tria_decode_attention(ctx, k, v, pos, st.n_rows, torch.from_numpy(q).to(DEV)))
+    kk, vv = pu.host(k), pu.host(v)
+    for l in range(wl.L):
+        for g in range(wl.Hkv):
+            o = oracle.decode_attention_unit(wl.k_type, wl.v_type, kk[l, g, :st.n_rows],
+                                             vv[l, g, :st.n_rows], wl.hd,
+                                             q[l, g * wl.G:(g + 1) * wl.G], 1.0 / np.sqrt(wl.hd))
+            _att_check(out[l, g * wl.G:(g + 1) * wl.G], o, "loop attention (%d,%d)" % (l, g))
+    ctx.close()
