@@ -53,52 +53,91 @@ __device__ __forceinline__ float row_elem(const uint8_t* row, int k_type, int e)
     return d * (float)(int8_t)blk[2 + (e & 31)];
 }
 
-// q_j . k for one row of an fp16 key (row 4-byte aligned).
+// q_j . k for one row of an fp16 key: 16-byte pieces (rows are 2*HD bytes,
+// 16-byte aligned), each converted and used at once.
 template <int HD, int GT>
 __device__ __forceinline__ void dot_f16(const uint8_t* row, const float* __restrict__ Q, int z,
                                         float (&s)[GT]) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
 #pragma unroll
     for (int j = 0; j < GT; ++j) s[j] = 0.0f;
-#pragma unroll 8
-    for (int e2 = 0; e2 < HD / 2; ++e2) {
-        const uint32_t x = w[e2];
-        const float a = half_of(x, 0), b = half_of(x, 1);
+#pragma unroll 2
+    for (int c = 0; c < HD / 8; ++c) {
+        const u32x4 x = r4[c];
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int j = 0; j < GT; ++j) {
-            s[j] = fmaf(Q[z + j * HD + 2 * e2], a, s[j]);
-            s[j] = fmaf(Q[z + j * HD + 2 * e2 + 1], b, s[j]);
+        for (int i = 0; i < 8; ++i) {
+            const float kv = half_of(w[i >> 1], i & 1);
+#pragma unroll
+            for (int j = 0; j < GT; ++j) s[j] = fmaf(Q[z + j * HD + 8 * c + i], kv, s[j]);
         }
     }
 }
 
-// q_j . k for one row of a q8_0 key (row 2-byte aligned): per block, the int8
-// values times q, then the block scale.
+// q_j . k for one row of a q8_0 key (34 * HD/32 bytes, so rows are 8-byte
+// aligned when HD/32 % 4 == 0, 4-byte aligned when it is even): the whole row
+// is read with 8- or 4-byte loads, else 2 bytes at a time; per block, the int8
+// values times q, then the scale.
 template <int HD, int GT>
 __device__ __forceinline__ void dot_q8(const uint8_t* row, const float* __restrict__ Q, int z,
                                        float (&s)[GT]) {
+    constexpr int NB = HD / 32;
 #pragma unroll
     for (int j = 0; j < GT; ++j) s[j] = 0.0f;
-#pragma unroll 1
-    for (int b = 0; b < HD / 32; ++b) {
-        const uint8_t* blk = row + 34 * b;
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(blk);
-        const float d = (float)__builtin_bit_cast(_Float16, h[0]);
-        float t[GT];
+    if constexpr (NB % 2 == 0) {
+        constexpr int W = 34 * NB / 4;
+        uint32_t wv[W];
+        if constexpr (NB % 4 == 0) {
+            const u32x2* r2 = reinterpret_cast<const u32x2*>(row);
 #pragma unroll
-        for (int j = 0; j < GT; ++j) t[j] = 0.0f;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) {
-            const uint16_t x = h[1 + i2];
-            const float a = (float)(int8_t)(x & 0xff), c = (float)(int8_t)(x >> 8);
-#pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                t[j] = fmaf(Q[z + j * HD + 32 * b + 2 * i2], a, t[j]);
-                t[j] = fmaf(Q[z + j * HD + 32 * b + 2 * i2 + 1], c, t[j]);
+            for (int i = 0; i < W / 2; ++i) {
+                const u32x2 t = r2[i];
+                wv[2 * i] = t.x;
+                wv[2 * i + 1] = t.y;
             }
+        } else {
+            const uint32_t* r1 = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+            for (int i = 0; i < W; ++i) wv[i] = r1[i];
         }
 #pragma unroll
-        for (int j = 0; j < GT; ++j) s[j] = fmaf(d, t[j], s[j]);
+        for (int b = 0; b < NB; ++b) {
+            const int o = 34 * b;
+            const float d = half_of(wv[o >> 2], (o & 2) != 0);
+            float t[GT];
+#pragma unroll
+            for (int j = 0; j < GT; ++j) t[j] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                const int ob = o + 2 + i;
+                const float kv = (float)(int8_t)(wv[ob >> 2] >> (8 * (ob & 3)));
+#pragma unroll
+                for (int j = 0; j < GT; ++j) t[j] = fmaf(Q[z + j * HD + 32 * b + i], kv, t[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < GT; ++j) s[j] = fmaf(d, t[j], s[j]);
+        }
+    } else {
+#pragma unroll 1
+        for (int b = 0; b < NB; ++b) {
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(row + 34 * b);
+            const float d = (float)__builtin_bit_cast(_Float16, h[0]);
+            float t[GT];
+#pragma unroll
+            for (int j = 0; j < GT; ++j) t[j] = 0.0f;
+#pragma unroll
+            for (int i2 = 0; i2 < 16; ++i2) {
+                const uint16_t x = h[1 + i2];
+                const float a = (float)(int8_t)(x & 0xff), c = (float)(int8_t)(x >> 8);
+#pragma unroll
+                for (int j = 0; j < GT; ++j) {
+                    t[j] = fmaf(Q[z + j * HD + 32 * b + 2 * i2], a, t[j]);
+                    t[j] = fmaf(Q[z + j * HD + 32 * b + 2 * i2 + 1], c, t[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < GT; ++j) s[j] = fmaf(d, t[j], s[j]);
+        }
     }
 }
 
@@ -113,13 +152,21 @@ struct AttPart {
     float m, l;
 };
 
+// V rows read as 16-byte pieces (8 fp16 values): LPR lanes cover a row, so a
+// wavefront reads 64 / LPR rows per instruction.  HD in {32, 64, 128, 256}.
+template <int HD>
+constexpr bool kVecV = HD == 32 || HD == 64 || HD == 128 || HD == 256;
+
 // grid (splits, units); q: [seq][L][Hq][HD] fp32; parts: [unit][split][G]
 // records, pacc: [unit][split][G][HD].  Heads j0 .. j0+GT-1 of each group.
-template <int HD, int GT>
+// VEC: fp16 V read in 16-byte pieces (see kVecV); else element by element.
+template <int HD, int GT, bool VEC>
 __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
     CacheView cv, Batch b, int G, int j0, int k_type, int v_type, const float* __restrict__ q,
     float scale, int rows_per_split, AttPart* __restrict__ parts, float* __restrict__ pacc) {
-    constexpr int DPL = (HD + 63) / 64;  // output dims per lane
+    constexpr int LPR = VEC ? HD / 8 : 64;         // lanes per V row
+    constexpr int RPI = 64 / LPR;                  // V rows per wavefront instruction
+    constexpr int NACC = VEC ? 8 : (HD + 63) / 64;  // output dims per lane
     __shared__ float p_sh[kAttWaves][GT][64];
     __shared__ float m_sh[kAttWaves][GT], l_sh[kAttWaves][GT];
     __shared__ float acc_sh[kAttWaves][GT][HD];
@@ -128,18 +175,19 @@ __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
     const SeqDesc& sd = b.seq[id.seq];
     const int64_t n = sd.n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int dg = lane % LPR, ro = lane / LPR;  // VEC: dims 8 dg .. 8 dg + 7 of rows = ro mod RPI
     const int64_t r_lo = (int64_t)split * rows_per_split;
     const int64_t r_hi = r_lo + rows_per_split < n ? r_lo + rows_per_split : n;
     const int Hq = cv.Hkv * G;
     const float* Qu = q + (((int64_t)id.seq * cv.L + id.l) * Hq + (int64_t)id.g * G + j0) * HD;
 
-    float m[GT], l[GT], acc[GT][DPL];
+    float m[GT], l[GT], acc[GT][NACC];
 #pragma unroll
     for (int j = 0; j < GT; ++j) {
         m[j] = -INFINITY;
         l[j] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[j][i] = 0.0f;
+        for (int i = 0; i < NACC; ++i) acc[j][i] = 0.0f;
     }
     const int kb = cv.kb, vb = cv.vb;
     for (int64_t t0 = r_lo + (int64_t)wave * 64; t0 < r_hi; t0 += kAttWaves * 64) {
@@ -165,26 +213,53 @@ __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
             l[j] = l[j] * alpha + wave_add_f32(p);
             m[j] = mn;
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) acc[j][i] *= alpha;
+            for (int i = 0; i < NACC; ++i) acc[j][i] *= alpha;
             p_sh[wave][j][lane] = p;
         }
-        // 3. lane = dims: accumulate the tile's V rows (LDS writes of this wave
-        //    are visible to its own later reads: one wavefront, in order)
+        // 3. accumulate the tile's V rows (LDS writes of this wave are visible to
+        //    its own later reads: one wavefront, in order)
         const int nt = (int)(r_hi - t0 < 64 ? r_hi - t0 : 64);
-        for (int rr = 0; rr < nt; ++rr) {
-            const uint8_t* vrow = cv.v + row_index(cv, id, t0 + rr) * vb;
-            float vv[DPL];
+        if constexpr (VEC) {
+            for (int rr = ro; rr < nt; rr += RPI) {
+                const uint8_t* vrow = cv.v + row_index(cv, id, t0 + rr) * vb;
+                const u32x4 x = reinterpret_cast<const u32x4*>(vrow)[dg];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                float vv[8];
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) {
-                const int e = lane + 64 * i;
-                vv[i] = e < HD ? row_elem(vrow, v_type, e) : 0.0f;
+                for (int i = 0; i < 8; ++i) vv[i] = half_of(w[i >> 1], i & 1);
+#pragma unroll
+                for (int j = 0; j < GT; ++j) {
+                    const float p = p_sh[wave][j][rr];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(p, vv[i], acc[j][i]);
+                }
             }
+        } else {
+            for (int rr = 0; rr < nt; ++rr) {
+                const uint8_t* vrow = cv.v + row_index(cv, id, t0 + rr) * vb;
+                float vv[NACC];
 #pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                const float p = p_sh[wave][j][rr];
+                for (int i = 0; i < NACC; ++i) {
+                    const int e = lane + 64 * i;
+                    vv[i] = e < HD ? row_elem(vrow, v_type, e) : 0.0f;
+                }
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) acc[j][i] = fmaf(p, vv[i], acc[j][i]);
+                for (int j = 0; j < GT; ++j) {
+                    const float p = p_sh[wave][j][rr];
+#pragma unroll
+                    for (int i = 0; i < NACC; ++i) acc[j][i] = fmaf(p, vv[i], acc[j][i]);
+                }
             }
+        }
+    }
+    // VEC: add the RPI row groups' partial sums (lanes dg, dg + LPR, ...)
+    if constexpr (VEC) {
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] += __shfl_xor(acc[j][i], o, 64);
         }
     }
     // merge the four wavefronts
@@ -194,10 +269,17 @@ __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
             m_sh[wave][j] = m[j];
             l_sh[wave][j] = l[j];
         }
+        if constexpr (VEC) {
+            if (ro == 0) {
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-            const int e = lane + 64 * i;
-            if (e < HD) acc_sh[wave][j][e] = acc[j][i];
+                for (int i = 0; i < 8; ++i) acc_sh[wave][j][8 * dg + i] = acc[j][i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NACC; ++i) {
+                const int e = lane + 64 * i;
+                if (e < HD) acc_sh[wave][j][e] = acc[j][i];
+            }
         }
     }
     __syncthreads();
@@ -247,8 +329,12 @@ template <int HD, int GT>
 void run_split(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int G, int j0,
                int kt, int vt, const float* q, float scale, int rps, AttPart* parts,
                float* pacc) {
-    hipLaunchKernelGGL((attention_split_kernel<HD, GT>), grid, dim3(kAttThreads), 0, s, cv, b, G,
-                       j0, kt, vt, q, scale, rps, parts, pacc);
+    if (kVecV<HD> && vt == TRIA_KV_F16)
+        hipLaunchKernelGGL((attention_split_kernel<HD, GT, kVecV<HD>>), grid, dim3(kAttThreads), 0,
+                           s, cv, b, G, j0, kt, vt, q, scale, rps, parts, pacc);
+    else
+        hipLaunchKernelGGL((attention_split_kernel<HD, GT, false>), grid, dim3(kAttThreads), 0, s,
+                           cv, b, G, j0, kt, vt, q, scale, rps, parts, pacc);
 }
 
 template <int HD>
