@@ -807,3 +807,57 @@ def test_decode_loop(compaction):
                                              q[l, g * wl.G:(g + 1) * wl.G], 1.0 / np.sqrt(wl.hd))
             _att_check(out[l, g * wl.G:(g + 1) * wl.G], o, "loop attention (%d,%d)" % (l, g))
     ctx.close()
+
+
+@pytest.mark.parametrize("k_type,v_type,hd", [(Q8, Q8, 128), (Q8, F16, 32), (F16, Q8, 160)],
+                         ids=["q8v_hd128", "q8k_hd32", "q8v_hd160"])
+def test_decode_attention_row_types(k_type, v_type, hd):
+    """q8_0 values (the element-by-element V path) and the 2-byte q8_0 key path."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="att_types", L=1, Hkv=2, Hq=6, hd=hd,
+                 k_type=k_type, v_type=v_type)
+    n = 900
+    pu.say("case attention types k%d v%d hd%d" % (k_type, v_type, hd))
+    case = synth.make_case(wl, device="cpu", n=n)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    q = np.random.default_rng(84 + hd).standard_normal((wl.L, wl.Hq, hd)).astype(np.float32)
+    ctx = pu.make_ctx(wl, stats)
+    out = pu.host(tria.tria_decode_attention(ctx, case["k"].to(DEV), case["v"].to(DEV),
+                                             case["pos"].to(DEV), n, torch.from_numpy(q).to(DEV)))
+    kk, vv = case["k"].numpy(), case["v"].numpy()
+    for g in range(wl.Hkv):
+        o = oracle.decode_attention_unit(k_type, v_type, kk[0, g, :n], vv[0, g, :n], hd,
+                                         q[0, g * wl.G:(g + 1) * wl.G], 1.0 / np.sqrt(hd))
+        _att_check(out[0, g * wl.G:(g + 1) * wl.G], o, "unit (0,%d)" % g)
+    ctx.close()
+
+
+@pytest.mark.parametrize("mode", sorted(MODES), ids=["per_kv_head", "global"])
+def test_shared_keep_mode_with_hole_fill(mode):
+    """Shared keep sets compacted by hole filling: every member holds the same rows in
+    the same order, and the rows are exactly the oracle's hole fill of the group's kept
+    rows."""
+    wl = variant(WL["qwen3_8b_layer_32k_f16"], name="shared_hole", L=3, Hkv=2, Hq=8, k_type=Q8)
+    n, B, S, W = 4000, 1000, 4, 128
+    case = synth.make_case(wl, device="cpu", n=n)
+    stats = (case["q_re"], case["q_im"], case["w"])
+    k0, v0, p0 = case["k"].numpy().copy(), case["v"].numpy().copy(), case["pos"].numpy().copy()
+    ctx = pu.make_ctx(wl, stats)
+    tria.tria_set_keep_mode(ctx, MODES[mode])
+    tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    K = tria.tria_evict(ctx, k, v, pos, n, B, S, W)
+    tria.tria_device_status(ctx)
+    o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                     list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, B, S, W, *stats,
+                     compact=False, keep_mode=mode)
+    ka, pa = pu.host(k), pu.host(pos)
+    for l in range(wl.L):
+        for g in range(wl.Hkv):
+            ref = pa[0, g if mode == oracle.KEEP_KV_HEAD else 0, :K]
+            assert np.array_equal(pa[l, g, :K], ref), "members differ"
+            gkeep = np.sort(pa[l, g, :K]).astype(np.int32)  # positions were 0..n-1
+            pu.check_kept(gkeep, o["keep_idx"][l, g], o["agg"][l, g], n, B, S, W,
+                          "unit (%d,%d)" % (l, g))
+            want, _ = oracle.compact_holefill(k0[l, g, :n], gkeep, n)
+            assert np.array_equal(ka[l, g, :K], want[:K])
+    ctx.close()
