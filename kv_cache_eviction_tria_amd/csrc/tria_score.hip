@@ -25,6 +25,16 @@
 // row's byte layout, scale bytes carry zero digits); the block scale d and sig
 // are applied once per block.  The |K_f| term dequantises q * d in fp32.
 //
+// fp16 rows with hd % 64 == 0 take the matrix-core path instead: the trig
+// series and the norm-term sum are both contractions of a row over its
+// dimensions (pairs) against G per-head coefficient vectors, i.e. a
+// [16 rows x hd] x [hd x 16 heads] product per step, run as
+// v_mfma_f32_16x16x32_f16 with the fp16 key as the B operand as stored and the
+// coefficients split into two fp16 parts (hi + lo, per-head power-of-two
+// scale) so the products keep fp32-level accuracy; |K_f| is formed on the
+// VALU and split the same way.  The VALU then only forms |K_f| and the
+// statistics, about half of its work in the row-per-lane kernel.
+//
 // Each wavefront also summarises its rows' scores per head (count, mean,
 // squared deviations; fp64) for the selector's z-normalisation, so the raw
 // scores are not read an extra time to form the head statistics.
@@ -321,6 +331,247 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     if (part) emit_moments<GT>(mom, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core scorer for fp16 rows (hd % 64 == 0).
+//
+// One wavefront scores a tile of kPartRows rows in steps of 16.  MFMA operand
+// layout (v_mfma_f32_16x16x32_f16, checked on gfx950): lane m + 16 g of the A
+// operand holds A[m][8 g + e], lane n + 16 g of the B operand holds
+// B[8 g + e][n] (e = 0..7), and lane n + 16 g of the result holds C[4 g + i][n]
+// (i = 0..3).  Here m = query head (of a chunk of up to 16), n = row of the
+// step, and "k = 8 g + e" is mapped as follows:
+//   trig step s (s < hd/32): dimension 32 s + 8 g + e of the row;
+//   norm step t (t < F/32):  pair f = 32 t + 8 g + e.
+// So lane (n, g) loads 16 bytes at dimension 32 s + 8 g for every s, which
+// also gives it both halves of pairs 32 t + 8 g + e (steps t and t + F/32) for
+// the norm term.  The A operands of the unit (coefficient hi and lo parts,
+// zero for heads past the chunk) are built once per workgroup into LDS.
+constexpr int kMfmaThreads = 256;
+constexpr int kMfmaSteps = kPartRows / 16;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Coefficient of query head j in the row-per-lane table (sub-group blocks of
+// [F][gt][3] = {Re C, Im C, w}).
+__device__ __forceinline__ float f16_table_coef(const float* C, int G, int F, int j, int comp, int f) {
+    const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
+    return C[(j0 * F + f * gt + (j - j0)) * 3 + comp];
+}
+
+// Sum over the 16 lanes of a row of the wavefront, returned to all 16.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141, 0xf>(v);  // row_half_mirror
+    v += dpp_f32<0x140, 0xf>(v);  // row_mirror
+    return v;
+}
+
+template <int HD>
+__global__ __launch_bounds__(kMfmaThreads) void score_f16_mfma_kernel(
+    CacheView cv, Batch b, int G, int c0, int gc, const float* __restrict__ coef, int coef_words,
+    float* __restrict__ raw, PartRec* __restrict__ part) {
+    constexpr int F = HD / 2;
+    constexpr int KS = HD / 32;  // trig steps
+    constexpr int NS = F / 32;   // norm steps
+    __shared__ u32x4 tab[(KS + NS) * 2 * 64];
+    __shared__ int maxbits[16];
+
+    const int u = blockIdx.y;
+    const UnitId id = unit_id(cv, u);
+    const int64_t n = b.seq[id.seq].n;
+    if ((int64_t)blockIdx.x * (kMfmaThreads / 64) * kPartRows >= n) return;  // whole block
+    const float* __restrict__ C = coef + coef_unit(b, cv, id) * coef_words;
+
+    // Per-head power-of-two scale: the largest |coefficient| of head m maps into
+    // [2^14, 2^15), inside the fp16 range with room for the lo part.
+    if (threadIdx.x < 16) maxbits[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < gc * (HD + F); i += kMfmaThreads) {
+        const int m = i / (HD + F), d = i - m * (HD + F);
+        const int comp = d < F ? 0 : (d < HD ? 1 : 2);
+        const int f = d < F ? d : (d < HD ? d - F : d - HD);
+        const float a = fabsf(f16_table_coef(C, G, F, c0 + m, comp, f));
+        atomicMax(&maxbits[m], __builtin_bit_cast(int, a));  // |x| orders like its bits
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < (KS + NS) * 64; i += kMfmaThreads) {
+        const int p = i >> 6, ln = i & 63, m = ln & 15, g = ln >> 4;
+        const float mx = __builtin_bit_cast(float, maxbits[m & 15]);
+        const int ex = (mx > 0.0f && isfinite(mx)) ? 14 - ilogbf(mx) : 0;
+        half8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = 0.0f;
+            if (m < gc) {
+                if (p < KS) {
+                    const int d = 32 * p + 8 * g + e;
+                    x = f16_table_coef(C, G, F, c0 + m, d < F ? 0 : 1, d < F ? d : d - F);
+                } else {
+                    x = f16_table_coef(C, G, F, c0 + m, 2, 32 * (p - KS) + 8 * g + e);
+                }
+                x = ldexpf(x, ex);
+            }
+            const _Float16 h = (_Float16)x;
+            hi[e] = h;
+            lo[e] = (_Float16)(x - (float)h);
+        }
+        tab[(2 * p) * 64 + ln] = __builtin_bit_cast(u32x4, hi);
+        tab[(2 * p + 1) * 64 + ln] = __builtin_bit_cast(u32x4, lo);
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, nn = lane & 15, kg = lane >> 4;
+    const int64_t tile = (int64_t)blockIdx.x * (kMfmaThreads / 64) + (threadIdx.x >> 6);
+    const int64_t t0 = tile * kPartRows;
+    if (t0 >= n) return;
+
+    // output scale of this lane's heads 4 kg + i (zero past the chunk)
+    float osc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * kg + i;
+        const float mx = __builtin_bit_cast(float, maxbits[m]);
+        const int ex = (mx > 0.0f && isfinite(mx)) ? 14 - ilogbf(mx) : 0;
+        osc[i] = m < gc ? ldexpf(1.0f, -ex) : 0.0f;
+    }
+    float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + c0;
+    const bool vec_store = (G % 4 == 0) && (c0 % 4 == 0) && (4 * kg + 3 < gc);
+
+    float shift[4], sd[4], sq[4], cf[4];
+    bool have[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        shift[i] = 0.0f; sd[i] = 0.0f; sq[i] = 0.0f; cf[i] = 0.0f; have[i] = false;
+    }
+
+    // One step: 16 rows, their K bytes already in B.
+    auto step = [&](const u32x4 (&B)[KS], int64_t r0) {
+        const int64_t r_out = r0 + nn;
+        // the table is re-read from LDS every step (an offset the compiler cannot
+        // see through), instead of being hoisted into ~100 registers
+        const u32x4* __restrict__ T = tab + lane + opaque_zero_s();
+        // three independent accumulation chains (low-half trig, high-half
+        // trig, norm term) so consecutive MFMAs do not wait on each other
+        f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, acc2 = acc0;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const half8 bl = __builtin_bit_cast(half8, B[t]);
+            const half8 bh = __builtin_bit_cast(half8, B[t + NS]);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, T[(2 * t) * 64]), bl, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, T[(2 * (t + NS)) * 64]), bh, acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, T[(2 * t + 1) * 64]), bl, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, T[(2 * (t + NS) + 1) * 64]), bh, acc1, 0, 0, 0);
+            // |K_f| for the lane's 8 pairs, split into fp16 hi + lo (round toward
+            // zero, so a magnitude past the fp16 range keeps its hi finite)
+            half8 mh, ml;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float k0r = (float)bl[e], k0i = (float)bh[e];
+                const float k1r = (float)bl[e + 1], k1i = (float)bh[e + 1];
+                const float m0 = __builtin_amdgcn_sqrtf(fmaf(k0r, k0r, k0i * k0i));
+                const float m1 = __builtin_amdgcn_sqrtf(fmaf(k1r, k1r, k1i * k1i));
+                const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(m0, m1));
+                const half2v l = __builtin_bit_cast(
+                    half2v, __builtin_amdgcn_cvt_pkrtz(m0 - (float)h[0], m1 - (float)h[1]));
+                mh[e] = h[0]; mh[e + 1] = h[1];
+                ml[e] = l[0]; ml[e + 1] = l[1];
+            }
+            const half8 wh = __builtin_bit_cast(half8, T[(2 * (KS + t)) * 64]);
+            const half8 wl = __builtin_bit_cast(half8, T[(2 * (KS + t) + 1) * 64]);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, mh, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl, mh, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, ml, acc2, 0, 0, 0);
+        }
+
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = ((acc0[i] + acc1[i]) + acc2[i]) * osc[i];
+        const bool row_ok = r_out < n;
+        if (row_ok) {
+            if (vec_store) {
+                *reinterpret_cast<float4*>(rout + r_out * G + 4 * kg) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * kg + i < gc) rout[r_out * G + 4 * kg + i] = v[i];
+            }
+        }
+        if (part) {
+            bool valid[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) valid[i] = row_ok && (4 * kg + i < gc) && isfinite(v[i]);
+            // shift = first finite score of the tile (row order) per head
+            if (__ballot(!(have[0] && have[1] && have[2] && have[3]))) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t mk = __ballot(valid[i]);
+                    const uint32_t gm = (uint32_t)(mk >> (16 * kg)) & 0xffffu;
+                    const int src = 16 * kg + (gm ? __builtin_ctz(gm) : 0);
+                    const float sv = __shfl(v[i], src);
+                    if (!have[i] && gm) {
+                        shift[i] = sv;
+                        have[i] = true;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = valid[i] ? v[i] - shift[i] : 0.0f;
+                sd[i] += d;
+                sq[i] = fmaf(d, d, sq[i]);
+                cf[i] += valid[i] ? 1.0f : 0.0f;
+            }
+        }
+    };
+    // Rows of the step starting at r0 (rows past the end repeat the last row).
+    auto load = [&](u32x4 (&B)[KS], int64_t r0) {
+        const int64_t r_out = r0 + nn;
+        const int64_t r = r_out < n ? r_out : n - 1;
+        const uint8_t* rp = cv.k + row_index(cv, id, r) * (HD * 2) + 16 * kg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) B[s] = *reinterpret_cast<const u32x4*>(rp + 64 * s);
+    };
+
+#pragma unroll 1
+    for (int st = 0; st < kMfmaSteps; ++st) {
+        const int64_t r0 = t0 + 16 * st;
+        if (r0 >= n) break;
+        u32x4 B[KS];
+        load(B, r0);
+        step(B, r0);
+    }
+    if (part) {
+        PartRec* out = part + (b.seq[id.seq].part_off +
+                               ((int64_t)id.l * cv.Hkv + id.g) * part_tiles(n) + tile) * G + c0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float c = row16_sum(cf[i]);
+            const float a = row16_sum(sd[i]);
+            const float q = row16_sum(sq[i]);
+            if (nn == 0 && 4 * kg + i < gc) out[4 * kg + i] = PartRec{c, shift[i], a, q};
+        }
+    }
+}
+
+template <int HD>
+hipError_t run_f16_mfma(const CacheView& cv, const Batch& b, int n_units, int64_t max_n, int G,
+                        const int32_t* coef, int words, float* raw, PartRec* part, hipStream_t s) {
+    const int64_t rows_per_block = (int64_t)(kMfmaThreads / 64) * kPartRows;
+    const dim3 grid((unsigned)((max_n + rows_per_block - 1) / rows_per_block), (unsigned)n_units);
+    for (int c0 = 0; c0 < G; c0 += 16) {
+        const int gc = G - c0 < 16 ? G - c0 : 16;
+        hipLaunchKernelGGL((score_f16_mfma_kernel<HD>), grid, dim3(kMfmaThreads), 0, s, cv, b, G, c0,
+                           gc, reinterpret_cast<const float*>(coef), words, raw, part);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int HD, int GT>
 void run_f16(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int G, int j0,
              const int32_t* coef, int words, float* raw, PartRec* part) {
@@ -381,6 +632,15 @@ hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_
     const int64_t tiles = (max_n + rows_per_block - 1) / rows_per_block;
     const dim3 grid((unsigned)tiles, (unsigned)n_units);
     const CoefGeom cg = coef_geom(k_type, hd, G);
+    if (k_type == TRIA_KV_F16 && hd % 64 == 0) {
+        switch (hd) {
+            case 64: return run_f16_mfma<64>(cv, b, n_units, max_n, G, coef, cg.words, raw, part, s);
+            case 128: return run_f16_mfma<128>(cv, b, n_units, max_n, G, coef, cg.words, raw, part, s);
+            case 192: return run_f16_mfma<192>(cv, b, n_units, max_n, G, coef, cg.words, raw, part, s);
+            case 256: return run_f16_mfma<256>(cv, b, n_units, max_n, G, coef, cg.words, raw, part, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     for (int j0 = 0; j0 < G;) {
         const int gt = subgroup_size(G, j0);
         Runner fn = pick_runner(k_type, hd, gt);
