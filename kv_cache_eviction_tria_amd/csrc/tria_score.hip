@@ -46,6 +46,8 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float half_lo(uint32_t x) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
 }
@@ -226,12 +228,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
     const int u = blockIdx.y;
     const UnitId id = unit_id(cv, u);
     const int64_t n = b.seq[id.seq].n;
+    if ((int64_t)blockIdx.x * (kScoreThreads / 64) * kPartRows >= n) return;  // whole block
     const int64_t wbase = wave_tile() * kPartRows;
-    if (wbase >= n) return;
     const CoefGeom cg = coef_geom(TRIA_KV_Q8_0, HD, G);
     const int32_t* __restrict__ T = coef + coef_unit(b, cv, id) * coef_words;
     const int32_t* __restrict__ HI = T + cg.hi_off + j0 * W;
     const int32_t* __restrict__ LO = T + cg.lo_off + j0 * W;
+    // The trig digits of this sub-group as matrix-core A operands: word k of
+    // head slot h (zero for slots past the sub-group), one table per digit.
+    constexpr int HS = GT < 4 ? 4 : GT;  // head slots, a multiple of 4
+    __shared__ uint32_t dtab[2][HS][W];
+    for (int i = threadIdx.x; i < 2 * HS * W; i += kScoreThreads) {
+        const int dg = i / (HS * W), h = (i / W) % HS, k = i % W;
+        dtab[dg][h][k] = h < GT ? (uint32_t)(dg ? HI : LO)[h * W + k] : 0u;
+    }
+    __syncthreads();
+    if (wbase >= n) return;
     const float* __restrict__ SIG = reinterpret_cast<const float*>(T + cg.sig_off) + j0 * NB;
     const float* __restrict__ WT = reinterpret_cast<const float*>(T + cg.w_off) + j0 * F;
     float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + j0;
@@ -296,21 +308,36 @@ __global__ __launch_bounds__(kScoreThreads) void score_q8_kernel(
         for (int j = 0; j < GT; ++j) acc[j] = 0.0f;
 
         // trig part: per block, integer dot product of the stored int8 values with the
-        // quantised coefficient digits, then one scale per (head, block)
+        // quantised coefficient digits, then one scale per (head, block).  The
+        // products run on the matrix cores as 4x4x4 int8 blocks (16 per
+        // instruction): block q of v_mfma_i32_4x4x4i8 is lanes 4q .. 4q + 3, its B
+        // operand is word k of those lanes' four rows, its A operand lane 4q + m
+        // holds head m's digits of word k, and the result lane 4q + n holds the
+        // four heads' sums of its own row n, so every lane keeps its row.
+        // (Words never hold quants of two blocks: a block's two scale bytes
+        // separate them, and the scale bytes carry zero digits.)
+        const uint32_t* __restrict__ dt = &dtab[0][0][0] + z + (threadIdx.x & 3) * W;
 #pragma unroll
         for (int bk = 0; bk < NB; ++bk) {
             sync_acc<GT>(acc);
             const int k0 = (34 * bk + 2) >> 2, k1 = (34 * bk + 33) >> 2;
+            i32x4 chi[HS / 4], clo[HS / 4];
 #pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                int hi = 0, lo = 0;
+            for (int c = 0; c < HS / 4; ++c) chi[c] = clo[c] = i32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int k = k0; k <= k1; ++k) {
-                    hi = __builtin_amdgcn_sdot4((int)wv[k], HI[z + j * W + k], hi, false);
-                    lo = __builtin_amdgcn_sdot4((int)wv[k], LO[z + j * W + k], lo, false);
+            for (int k = k0; k <= k1; ++k) {
+#pragma unroll
+                for (int c = 0; c < HS / 4; ++c) {
+                    const int ahi = (int)dt[(HS + 4 * c) * W + k];
+                    const int alo = (int)dt[(4 * c) * W + k];
+                    chi[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(ahi, (int)wv[k], chi[c], 0, 0, 0);
+                    clo[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(alo, (int)wv[k], clo[c], 0, 0, 0);
                 }
-                acc[j] = fmaf((float)(hi * 256 + lo), dsc[bk] * SIG[z + j * NB + bk], acc[j]);
             }
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+                acc[j] = fmaf((float)(chi[j >> 2][j & 3] * 256 + clo[j >> 2][j & 3]),
+                              dsc[bk] * SIG[z + j * NB + bk], acc[j]);
         }
         // |K_f| term
         constexpr int CPQ = GT >= 8 ? 2 : 16 / GT;
