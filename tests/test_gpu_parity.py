@@ -74,6 +74,12 @@ SHAPES = [
     (160, 1, 5, Q8, F16, 999, 222, 3, 33),
     (224, 1, 7, F16, Q8, 600, 100, 0, 0),
     (192, 2, 24, Q8, F16, 700, 350, 8, 16),
+    # fp16 keys on the matrix-core scorer: head chunks of 4 within a launch of up
+    # to 16 heads (G 3 and 5 leave partial chunks), and G 20 takes two launches
+    (128, 1, 3, F16, F16, 1100, 300, 2, 64),
+    (192, 2, 10, F16, F16, 777, 200, 1, 50),
+    (128, 1, 12, F16, Q8, 2049, 512, 0, 128),
+    (64, 1, 20, F16, F16, 1300, 333, 3, 100),
 ]
 
 
@@ -127,6 +133,26 @@ def test_nonfinite_rows_and_flat_heads():
     def poison8(case):
         case["k"][0, 0, 33, 0:2] = torch.tensor([0x00, 0x7C], dtype=torch.uint8)  # scale = +inf
     run_case(wl8, 400, 100, 2, 8, mutate=poison8)
+
+
+def test_f16_magnitudes_past_the_half_range():
+    """Key pairs whose |K_f| exceeds the fp16 range (both halves near 6e4) and
+    per-head statistics six orders of magnitude apart: the matrix-core scorer's
+    hi/lo splits and per-head scales keep every raw score within the bar."""
+    wl = variant(WL["tiny_1x1_4k_f16"], name="magnitudes", L=1, Hkv=2, Hq=8, hd=128)
+
+    def big(case):
+        k = case["k"].view(torch.float16)
+        k[0, 0, 5:40, :] = 60000.0 * torch.sign(k[0, 0, 5:40, :].float()).half()
+        k[0, 1, 100:110, 0:64] = 65000.0
+        k[0, 1, 100:110, 64:128] = -65000.0
+        case["q_re"][0, 0] *= 1e5
+        case["q_im"][0, 0] *= 1e5
+        case["w"][0, 0] *= 1e5
+        case["q_re"][0, 5] *= 1e-5
+        case["q_im"][0, 5] *= 1e-5
+        case["w"][0, 5] *= 1e-5
+    run_case(wl, 600, 150, 4, 32, mutate=big)
 
 
 def test_second_pass_uses_absolute_position():
