@@ -28,7 +28,9 @@
 //   4. rows equal to T are taken lowest row first, and the kept rows are
 //      written in ascending order: ranks in row order come from wave ballots
 //      plus a prefix over the (j, wave) counts.
-// Keys live in registers for n <= 32K rows, else in a global scratch array.
+// Bins live in registers for n <= 128K rows (keys are recomputed from the raw
+// scores for the few rows that need them), else keys go to a global scratch
+// array.
 #include "tria_group.h"
 
 namespace tria {
@@ -44,9 +46,13 @@ constexpr int kListCap = 2048;
 // rows per thread whose loads are in flight together (fewer for wide rows)
 template <int GV>
 constexpr int kBatchRows = GV >= 8 ? 2 : 8;
-// Loops over a thread's rows are fully unrolled when its keys live in registers.
+// Each row's histogram bin stays in registers up to 128 rows per thread
+// (n <= 128K); wider units keep their keys in a global scratch array.
 template <int RPT>
-constexpr int kRowUnroll = RPT <= 32 ? RPT : 4;
+constexpr bool kBinsInRegs = RPT <= 128;
+// Loops over a thread's rows are fully unrolled when its bins live in registers.
+template <int RPT>
+constexpr int kRowUnroll = kBinsInRegs<RPT> ? RPT : 4;
 
 __device__ __forceinline__ uint32_t order_key(float x) {
     x = x + 0.0f;  // -0 -> +0 so that equal scores compare equal
@@ -180,8 +186,9 @@ __device__ __forceinline__ float agg_of(const RowLoad<GV>& x, const float* R, in
     return bad ? -INFINITY : best + 0.0f;
 }
 
-// With the bins in registers (up to 32K rows) the kernel fits 64 registers, so
-// two 1024-thread workgroups share a CU and 512 units are selected at once.
+// Up to 32K rows the kernel fits 64 registers, so two 1024-thread workgroups
+// share a CU and 512 units are selected at once; up to 128K rows the bins take
+// up to 64 more registers (one workgroup per CU).
 template <int RPT>
 constexpr int kSelWavesPerEU = RPT <= 32 ? 8 : 4;
 
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     Batch b, int units_per_seq, int G, const float* __restrict__ raw,
     const PartRec* __restrict__ part, int32_t* __restrict__ keep, float* __restrict__ agg_out,
     uint32_t* __restrict__ key_scratch, int32_t* __restrict__ chunk_pb, uint32_t* ticket) {
-    constexpr bool kRegKeys = RPT <= 32;
+    constexpr bool kRegKeys = kBinsInRegs<RPT>;
     // the compaction that follows on this stream takes its tasks from *ticket
     if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
     const int u = blockIdx.x;
@@ -549,7 +556,7 @@ int64_t select_key_scratch_rows(const Batch& b, int units_per_seq, int G) {
         const int64_t e = sd.raw_off / G + (int64_t)units_per_seq * sd.n;
         end = e > end ? e : end;
     }
-    return max_n > 32 * kSelThreads ? end : 0;
+    return max_n > 128 * kSelThreads ? end : 0;
 }
 
 hipError_t launch_moments(const Batch& b, int units_per_seq, int G, const float* raw,
