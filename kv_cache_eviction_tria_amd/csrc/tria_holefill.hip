@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kHoleThreads = 256;
 constexpr int kHoleItems = 8;  // pieces per thread and array for a 64-row chunk
-constexpr int kHoleBlocksPerUnit = 8;  // phase A workgroups per unit
+constexpr int kHoleBlocksPerUnit = 8;  // phase A workgroups per unit, at most
 
 struct RunPlan {
     int run, lim, t0, m;  // trailing run, K - run, first tail, tail count
@@ -244,7 +244,17 @@ hipError_t launch_pv(const CacheView& cv, const Batch& b, int n_units, const int
     int rows = kHoleThreads * kHoleItems / ppr;
     rows = rows > kChunkRows ? kChunkRows : rows;
     if (rows < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((holefill_tails_kernel<PK, PV>), dim3(kHoleBlocksPerUnit, n_units),
+    // Phase A moves at most n - kept rows per unit (one per evicted row below
+    // the run), so it needs no more blocks than 64-row chunks of that bound;
+    // surplus blocks would only repeat the plan's binary searches and exit.
+    int64_t most = 0;
+    for (int i = 0; i < b.n_seq; ++i) {
+        const int64_t e = b.seq[i].n - b.seq[i].kept;
+        most = e > most ? e : most;
+    }
+    int64_t qa = (most + kChunkRows - 1) / kChunkRows;
+    qa = qa < 1 ? 1 : (qa > kHoleBlocksPerUnit ? kHoleBlocksPerUnit : qa);
+    hipLaunchKernelGGL((holefill_tails_kernel<PK, PV>), dim3((unsigned)qa, n_units),
                        dim3(kHoleThreads), 0, s, cv, b, keep);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
