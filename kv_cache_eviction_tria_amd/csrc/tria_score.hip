@@ -9,21 +9,23 @@
 // the G query heads of the row's KV head (llama.cpp page "TriAttention
 // KV-Cache Eviction (--triattention)", section 5 "Phase C").
 //
-// Mapping: one lane per cached row at a time; a wavefront scores a tile of 256
-// rows (four per lane), 1024 rows per workgroup.  Every lane of a wave needs
-// the same coefficient at the same time, so the unit's table (built by prep) is read through scalar
-// loads into SGPRs and fed to the VALU as the scalar operand; no LDS and no
-// cross-lane reduction.  Each lane reads its whole row with wide loads; one
-// load instruction touches a cache line per lane and the following loads of
-// the row hit the same lines in L1, so K crosses HBM once.  The sqrt of
-// |K_f|^2 is shared by all G heads.
+// Row-per-lane kernels (q8_0, and fp16 widths that are not a multiple of 64):
+// one lane per cached row at a time; a wavefront scores a tile of 256 rows
+// (four per lane), 1024 rows per workgroup.  Every lane of a wave needs the
+// same coefficient at the same time, so the unit's table (built by prep) is
+// read through scalar loads into SGPRs and fed to the VALU as the scalar
+// operand.  Each lane reads its whole row with wide loads; one load
+// instruction touches a cache line per lane and the following loads of the
+// row hit the same lines in L1, so K crosses HBM once.  The sqrt of |K_f|^2
+// is shared by all G heads.
 //
 // q8_0 rows: the trig part is an integer dot product per 32-value block:
 // sum_d q_d c_d = sig * sum_d q_d v_d with v the 16-bit quantised coefficient
-// split into two base-256 digits, accumulated with packed int8 dot products
-// (v_dot4_i32_i8) straight from the stored bytes (the digit tables follow the
-// row's byte layout, scale bytes carry zero digits); the block scale d and sig
-// are applied once per block.  The |K_f| term dequantises q * d in fp32.
+// split into two base-256 digits, taken straight from the stored bytes (the
+// digit tables follow the row's byte layout, scale bytes carry zero digits) on
+// the matrix cores as 4x4x4 int8 blocks whose lanes are the rows (see the
+// kernel); the block scale d and sig are applied once per block.  The |K_f|
+// term dequantises q * d in fp32.
 //
 // fp16 rows with hd % 64 == 0 take the matrix-core path instead: the trig
 // series and the norm-term sum are both contractions of a row over its
