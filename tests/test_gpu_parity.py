@@ -95,8 +95,9 @@ def test_shapes(shape):
     (1, 0, 0, 0), (1, 0, 0, 1), (2, 1, 0, 0), (5, 0, 0, 0), (300, 0, 0, 0), (300, 10, 200, 200),
     (300, 299, 0, 0), (300, 5, 3, 4), (1025, 1024, 0, 1), (1024, 1, 0, 0), (700, 600, 650, 0),
 ])
-def test_edge_budgets(n, budget, sink, window):
-    wl = variant(WL["tiny_1x1_4k_f16"], name="edge", L=1, Hkv=2, Hq=4, k_type=Q8, seed=n + 3)
+@pytest.mark.parametrize("k_type", [Q8, F16], ids=["q8", "f16"])
+def test_edge_budgets(n, budget, sink, window, k_type):
+    wl = variant(WL["tiny_1x1_4k_f16"], name="edge", L=1, Hkv=2, Hq=4, k_type=k_type, seed=n + 3)
     run_case(wl, n, budget, sink, window, cap=n + 1)
 
 
