@@ -13,16 +13,17 @@
 // it, and the only hazard is a write landing on a row that a smaller
 // destination still has to read.
 //
-// The destinations of a unit are cut into chunks of 64 rows; a task moves
-// one chunk of one unit (K, V and positions).  A task
+// The destinations of a unit are cut into chunks of CR rows (128 when a
+// chunk's pieces fit one workgroup's registers, else 64); a task moves one
+// chunk of one unit (K, V and positions).  A task
 //   1. loads the source rows of its chunk into registers,
 //   2. once they have arrived, publishes that (flag[unit][chunk] = epoch),
 //   3. waits until every earlier chunk that reads a row of its own
 //      destination range has published, and
 //   4. stores.
-// The chunks that read rows [64c, 64c+64) are exactly those holding the ranks
-// P(64c) .. P(64c+64)-1, P(x) = number of kept rows below x (the selector
-// writes P at chunk boundaries); a later chunk never reads them, because its
+// The chunks that read rows [CR c, CR c + CR) are exactly those holding the
+// ranks P(CR c) .. P(CR c + CR)-1, P(x) = number of kept rows below x (the
+// selector writes P every 64 rows); a later chunk never reads them, because its
 // sources lie above its own destinations.  So every read sees the original
 // row and no task waits on anything but loads that are already in flight.
 //
@@ -90,7 +91,7 @@ struct ItemWalk {
 
 // One array's part of a task: the pieces of the chunk's rows, dealt to the
 // threads in row-major order (consecutive threads move consecutive pieces).
-template <int PW>
+template <int PW, int CR>
 struct ArrayMove {
     using T = typename Piece<PW>::T;
     T buf[kItems];
@@ -99,7 +100,7 @@ struct ArrayMove {
         ItemWalk w(rb / PW, PW);
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
-            if (w.r < kChunkRows) {
+            if (w.r < CR) {
                 const int64_t s = src[w.r];
                 if (s >= 0) buf[k] = *reinterpret_cast<const T*>(base + s * rb + w.off);
             }
@@ -115,19 +116,24 @@ struct ArrayMove {
         ItemWalk w(rb / PW, PW);
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
-            if (w.r < kChunkRows && src[w.r] >= 0)
+            if (w.r < CR && src[w.r] >= 0)
                 *reinterpret_cast<T*>(base + dst[w.r] * rb + w.off) = buf[k];
             w.next();
         }
     }
 };
 
-template <int PK, int PV>
+// Destination chunks of CR rows per unit (a multiple of kChunkRows).
+template <int CR>
+__host__ __device__ inline int64_t flow_chunks(int64_t kept) { return (kept + CR - 1) / CR; }
+
+template <int PK, int PV, int CR>
 __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
     CacheView cv, Batch b, const int32_t* __restrict__ keep, const int32_t* __restrict__ pb,
     uint32_t* flags, int max_chunks, uint32_t epoch, int n_units, uint32_t* ticket, int* err) {
-    __shared__ int64_t src_row[kChunkRows];  // physical source row, -1 if the row stays
-    __shared__ int64_t dst_row[kChunkRows];
+    constexpr int kPerP = CR / kChunkRows;  // prefix-count entries per chunk
+    __shared__ int64_t src_row[CR];  // physical source row, -1 if the row stays
+    __shared__ int64_t dst_row[CR];
     __shared__ uint32_t first_sh;
     const int t = threadIdx.x;
     const uint32_t n_tasks = (uint32_t)max_chunks * (uint32_t)n_units;
@@ -145,14 +151,14 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
             const SeqDesc& sd = b.seq[id.seq];
             const int kept = (int)sd.kept, n = (int)sd.n;
             if (kept <= 0 || kept >= n) continue;  // nothing evicted: no row moves
-            if (c >= (int)chunk_count(kept)) continue;
+            if (c >= (int)flow_chunks<CR>(kept)) continue;
             const int uu = id.l * cv.Hkv + id.g;
             const int32_t* idx = keep + sd.keep_off + (int64_t)uu * kept;
             uint32_t* F = flags + (int64_t)u * max_chunks;
-            const int d0 = c * kChunkRows;
+            const int d0 = c * CR;
 
             // 1. the chunk's sources, then its loads
-            if (t < kChunkRows) {
+            if (t < CR) {
                 int64_t sr = -1, dr = -1;
                 const int d = d0 + t;
                 if (d < kept) {
@@ -166,12 +172,12 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
                 dst_row[t] = dr;
             }
             __syncthreads();
-            ArrayMove<PK> mk;
-            ArrayMove<PV> mv;
+            ArrayMove<PK, CR> mk;
+            ArrayMove<PV, CR> mv;
             uint32_t pos = 0;
             mk.load(cv.k, cv.kb, src_row);
             mv.load(cv.v, cv.vb, src_row);
-            const int64_t ps = t < kChunkRows ? src_row[t] : -1;
+            const int64_t ps = t < CR ? src_row[t] : -1;
             if (ps >= 0) pos = reinterpret_cast<const uint32_t*>(cv.pos)[ps];
             mk.wait();
             mv.wait();
@@ -182,9 +188,10 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
             if (t == 0) (void)__hip_atomic_exchange(&F[c], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (t < 64) {
                 const int32_t* P = pb + sd.pb_off + (int64_t)uu * chunk_bounds(kept);
-                const int p0 = P[c], p1 = P[c + 1];
-                const int lo = p0 / kChunkRows;
-                const int hi = min(c - 1, (p1 - 1) / kChunkRows);
+                const int nb = (int)chunk_count(kept);
+                const int p0 = P[kPerP * c], p1 = P[min(kPerP * c + kPerP, nb)];
+                const int lo = p0 / CR;
+                const int hi = min(c - 1, (p1 - 1) / CR);
                 if (p1 > p0) {
                     for (int base = lo; base <= hi; base += 64) {
                         const int cc = base + t;
@@ -250,22 +257,23 @@ int piece_width(int rb) {
 using FlowKernel = void (*)(CacheView, Batch, const int32_t*, const int32_t*, uint32_t*, int,
                             uint32_t, int, uint32_t*, int*);
 
-template <int PK>
+template <int PK, int CR>
 FlowKernel flow_for_v(int pv) {
     switch (pv) {
-        case 16: return compact_flow_kernel<PK, 16>;
-        case 8: return compact_flow_kernel<PK, 8>;
-        case 4: return compact_flow_kernel<PK, 4>;
-        default: return compact_flow_kernel<PK, 2>;
+        case 16: return compact_flow_kernel<PK, 16, CR>;
+        case 8: return compact_flow_kernel<PK, 8, CR>;
+        case 4: return compact_flow_kernel<PK, 4, CR>;
+        default: return compact_flow_kernel<PK, 2, CR>;
     }
 }
 
+template <int CR>
 FlowKernel flow_kernel(int pk, int pv) {
     switch (pk) {
-        case 16: return flow_for_v<16>(pv);
-        case 8: return flow_for_v<8>(pv);
-        case 4: return flow_for_v<4>(pv);
-        default: return flow_for_v<2>(pv);
+        case 16: return flow_for_v<16, CR>(pv);
+        case 8: return flow_for_v<8, CR>(pv);
+        case 4: return flow_for_v<4, CR>(pv);
+        default: return flow_for_v<2, CR>(pv);
     }
 }
 
@@ -281,6 +289,8 @@ int resident_groups(FlowKernel k, int threads) {
     return cus * per_cu;
 }
 
+// 64-row chunks of the largest kept count (flags are sized for these; a launch
+// with 128-row chunks uses half of them).
 int64_t max_chunks_of(const Batch& b) {
     int64_t m = 0;
     for (int i = 0; i < b.n_seq; ++i) {
@@ -317,13 +327,24 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
         pb = pb_scratch;
     }
     const int pk = piece_width(cv.kb), pv = piece_width(cv.vb);
-    const FlowKernel k = flow_kernel(pk, pv);
+    // 128-row chunks when each array's chunk fits kItems pieces per thread of a
+    // kMaxFlowThreads workgroup (fewer barriers and flag waits per byte, twice
+    // the bytes in flight per workgroup), else 64-row chunks
+    const int64_t ppr = cv.kb / pk > cv.vb / pv ? cv.kb / pk : cv.vb / pv;
+    const bool wide = 2 * kChunkRows * ppr <= (int64_t)kMaxFlowThreads * kItems;
+    const int cr = wide ? 2 * kChunkRows : kChunkRows;
+    const FlowKernel k = wide ? flow_kernel<2 * kChunkRows>(pk, pv) : flow_kernel<kChunkRows>(pk, pv);
     // threads such that each array's chunk is at most kItems pieces per thread
-    const int64_t pieces = (int64_t)kChunkRows * (cv.kb / pk > cv.vb / pv ? cv.kb / pk : cv.vb / pv);
+    const int64_t pieces = (int64_t)cr * ppr;
     int threads = 256;
     while ((int64_t)threads * kItems < pieces) threads *= 2;
     if (threads > kMaxFlowThreads) return hipErrorInvalidValue;
-    const int64_t tasks = max_chunks * n_units;
+    int64_t chunks = 0;  // chunks of cr rows of the largest kept count
+    for (int i = 0; i < b.n_seq; ++i) {
+        const int64_t c = (b.seq[i].kept + cr - 1) / cr;
+        chunks = c > chunks ? c : chunks;
+    }
+    const int64_t tasks = chunks * n_units;
     if (tasks >= (int64_t)1 << 31) return hipErrorInvalidValue;
     // as many workgroups as fit at once; residency is not required
     int grid = resident_groups(k, threads);
@@ -332,7 +353,7 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
     if (need < grid) grid = (int)need;
     st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value
     hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, s, cv, b, keep, pb, st.flags,
-                       (int)max_chunks, st.epoch, n_units, ticket, st.err);
+                       (int)chunks, st.epoch, n_units, ticket, st.err);
     return hipGetLastError();
 }
 
