@@ -13,8 +13,8 @@
 // it, and the only hazard is a write landing on a row that a smaller
 // destination still has to read.
 //
-// The destinations of a unit are cut into chunks of CR rows (128 when a
-// chunk's pieces fit one workgroup's registers, else 64); a task moves one
+// The destinations of a unit are cut into chunks of CR rows (256, 128 or 64:
+// the widest whose pieces fit one workgroup's registers); a task moves one
 // chunk of one unit (K, V and positions).  A task
 //   1. loads the source rows of its chunk into registers,
 //   2. once they have arrived, publishes that (flag[unit][chunk] = epoch),
@@ -290,7 +290,7 @@ int resident_groups(FlowKernel k, int threads) {
 }
 
 // 64-row chunks of the largest kept count (flags are sized for these; a launch
-// with 128-row chunks uses half of them).
+// with wider chunks uses fewer of them).
 int64_t max_chunks_of(const Batch& b) {
     int64_t m = 0;
     for (int i = 0; i < b.n_seq; ++i) {
@@ -327,13 +327,16 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
         pb = pb_scratch;
     }
     const int pk = piece_width(cv.kb), pv = piece_width(cv.vb);
-    // 128-row chunks when each array's chunk fits kItems pieces per thread of a
-    // kMaxFlowThreads workgroup (fewer barriers and flag waits per byte, twice
-    // the bytes in flight per workgroup), else 64-row chunks
+    // the widest chunk (256, 128 or 64 rows) whose pieces fit kItems per thread
+    // of a kMaxFlowThreads workgroup: fewer barriers and flag waits per byte and
+    // more bytes in flight per workgroup
     const int64_t ppr = cv.kb / pk > cv.vb / pv ? cv.kb / pk : cv.vb / pv;
-    const bool wide = 2 * kChunkRows * ppr <= (int64_t)kMaxFlowThreads * kItems;
-    const int cr = wide ? 2 * kChunkRows : kChunkRows;
-    const FlowKernel k = wide ? flow_kernel<2 * kChunkRows>(pk, pv) : flow_kernel<kChunkRows>(pk, pv);
+    const int64_t room = (int64_t)kMaxFlowThreads * kItems;
+    const int cr = 4 * kChunkRows * ppr <= room ? 4 * kChunkRows
+                 : (2 * kChunkRows * ppr <= room ? 2 * kChunkRows : kChunkRows);
+    const FlowKernel k = cr == 4 * kChunkRows   ? flow_kernel<4 * kChunkRows>(pk, pv)
+                       : cr == 2 * kChunkRows ? flow_kernel<2 * kChunkRows>(pk, pv)
+                                              : flow_kernel<kChunkRows>(pk, pv);
     // threads such that each array's chunk is at most kItems pieces per thread
     const int64_t pieces = (int64_t)cr * ppr;
     int threads = 256;
