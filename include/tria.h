@@ -351,9 +351,9 @@ int tria_calib_create(tria_calib **out, int32_t n_layers, int32_t n_q_heads, int
 /* Adds n_tokens query rows of one layer: q (device) holds row t at element
  * t * row_stride, head h's head_dim values at + h * head_dim (row_stride >=
  * n_q_heads * head_dim, e.g. the query slice of a fused projection), type
- * TRIA_Q_*.  Stream-ordered; q must stay valid until the work has run.  At
- * most 65535 * 32 tokens per call (TRIA_E_UNSUPPORTED beyond: add in batches).
- * Calls on one object must use one stream (or be ordered by the caller). */
+ * TRIA_Q_*.  Stream-ordered; q must stay valid until the work has run.  One
+ * kernel launch, no allocation.  Calls on one object must use one stream (or
+ * be ordered by the caller): they add into the same accumulators. */
 int tria_calib_add(tria_calib *c, int32_t layer, const void *q, int32_t q_type, int64_t n_tokens,
                    int64_t row_stride, hipStream_t stream);
 

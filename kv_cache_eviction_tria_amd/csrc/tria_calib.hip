@@ -9,15 +9,19 @@
 //   q_mean = sums / T,  q_abs = sum|q_f| / T,  w = q_abs - |q_mean|
 // (w: the norm-term weight; zero when every token's pair points the same way).
 //
-// Streaming: tria_calib_add takes one layer's query rows of one batch; every
-// workgroup covers 32 tokens of 256 (head, pair) slots: four consecutive pairs
-// per lane (one 16-byte load of the real halves and one of the imaginary
-// halves per token; consecutive lanes read consecutive bytes), the tokens
-// dealt over its four wavefronts and their sums combined in LDS; it writes
-// fp64 partial sums; a second kernel adds the partials into the
-// layer's accumulators in a fixed order, so the result does not depend on
-// scheduling.  The pair magnitude is formed in fp32 (the inputs are at most
-// fp32), the sums in fp64.
+// Streaming: tria_calib_add takes one layer's query rows of one batch in one
+// launch.  The layer keeps kCalSlots fp64 accumulators per (pair, sum); the
+// tokens are cut into chunks of 32, and workgroup (column, y) covers 256
+// (head, pair) slots of chunks y, y + S, y + 2S, ... (S = min(chunks,
+// kCalSlots)): four consecutive pairs per lane (one 16-byte load of the real
+// halves and one of the imaginary halves per token; consecutive lanes read
+// consecutive bytes), the tokens dealt over its four wavefronts and their sums
+// combined in LDS in a fixed order, then added into accumulator slot y -- which
+// no other workgroup of the launch touches, and adds on one stream run in
+// order.  tria_calib_finish adds a layer's slots in slot order.  So every sum
+// is formed in an order fixed by the call sequence, never by scheduling.  The
+// pair magnitude is formed in fp32 (the inputs are at most fp32), the sums in
+// fp64.
 #include <new>
 
 #include "tria_internal.h"
@@ -25,7 +29,8 @@
 namespace {
 
 constexpr int kCalThreads = 256;
-constexpr int kCalTok = 32;  // tokens per partial
+constexpr int kCalTok = 32;    // tokens per chunk
+constexpr int kCalSlots = 64;  // accumulator slots per layer (workgroup rows of a launch)
 constexpr int kCalMaxLayers = 128;  // layers finished per launch
 
 template <typename QT>
@@ -66,35 +71,37 @@ __device__ __forceinline__ float4 q_load4<uint16_t>(const uint16_t* p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
-// grid (pair blocks of 256, token chunks).  Lane j of every wavefront takes
-// pairs 4j .. 4j+3 of the block's 256 (F % 4 == 0: never across a head) and
-// wavefront w the tokens t0 + w, t0 + w + 4, ... of the chunk; the four
-// wavefronts' sums are added in LDS in a fixed order and written as
-// partial[(chunk * HF + pair) * 3 + {re, im, abs}].
 constexpr int kCalWaves = kCalThreads / 64;
 
+// grid (pair blocks of 256, S accumulator slots).  Lane j of every wavefront
+// takes pairs 4j .. 4j+3 of the block's 256 (F % 4 == 0: never across a head)
+// and wavefront w the tokens t0 + w, t0 + w + 4, ... of the block's chunks
+// (y, y + S, ...); the four wavefronts' sums are added in LDS in a fixed order
+// and then into slot y: slot[(y * HF + pair) * 3 + {re, im, abs}].
 template <typename QT>
 __global__ __launch_bounds__(kCalThreads) void calib_partial4_kernel(
     const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
-    double* __restrict__ partial) {
+    double* __restrict__ slot) {
     __shared__ double sums[kCalWaves][12][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p0 = blockIdx.x * 256 + 4 * lane;
     const bool in = p0 < HF;
     const int h = p0 / F, f = p0 - h * F;
-    const int64_t t0 = (int64_t)blockIdx.y * kCalTok;
-    const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
     const QT* base = q + (int64_t)h * hd + f;
     double sr[4] = {0.0, 0.0, 0.0, 0.0}, si[4] = {0.0, 0.0, 0.0, 0.0}, sa[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int64_t t = t0 + wave; in && t < t1; t += kCalWaves) {
-        const float4 re = q_load4<QT>(base + t * stride);
-        const float4 im = q_load4<QT>(base + t * stride + F);
-        const float r[4] = {re.x, re.y, re.z, re.w}, m[4] = {im.x, im.y, im.z, im.w};
+    for (int64_t t0 = (int64_t)blockIdx.y * kCalTok; in && t0 < T;
+         t0 += (int64_t)gridDim.y * kCalTok) {
+        const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
+        for (int64_t t = t0 + wave; t < t1; t += kCalWaves) {
+            const float4 re = q_load4<QT>(base + t * stride);
+            const float4 im = q_load4<QT>(base + t * stride + F);
+            const float r[4] = {re.x, re.y, re.z, re.w}, m[4] = {im.x, im.y, im.z, im.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sr[k] += (double)r[k];
-            si[k] += (double)m[k];
-            sa[k] += (double)__builtin_amdgcn_sqrtf(fmaf(r[k], r[k], m[k] * m[k]));
+            for (int k = 0; k < 4; ++k) {
+                sr[k] += (double)r[k];
+                si[k] += (double)m[k];
+                sa[k] += (double)__builtin_amdgcn_sqrtf(fmaf(r[k], r[k], m[k] * m[k]));
+            }
         }
     }
 #pragma unroll
@@ -105,51 +112,41 @@ __global__ __launch_bounds__(kCalThreads) void calib_partial4_kernel(
     }
     __syncthreads();
     if (wave == 0 && in) {
-        double* out = partial + ((int64_t)blockIdx.y * HF + p0) * 3;
+        double* out = slot + ((int64_t)blockIdx.y * HF + p0) * 3;
 #pragma unroll
         for (int j = 0; j < 12; ++j) {
             double s = sums[0][j][lane];
 #pragma unroll
             for (int w = 1; w < kCalWaves; ++w) s += sums[w][j][lane];
-            out[j] = s;
+            out[j] += s;
         }
     }
 }
 
-// Any F: one pair per thread.
+// Any F: one pair per thread, chunks y, y + S, ... into slot y.
 template <typename QT>
 __global__ __launch_bounds__(kCalThreads) void calib_partial_kernel(
     const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
-    double* __restrict__ partial) {
+    double* __restrict__ slot) {
     const int i = blockIdx.x * kCalThreads + threadIdx.x;
     if (i >= HF) return;
     const int h = i / F, f = i - h * F;
-    const int64_t t0 = (int64_t)blockIdx.y * kCalTok;
-    const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
     const QT* base = q + (int64_t)h * hd + f;
     double sr = 0.0, si = 0.0, sa = 0.0;
-    for (int64_t t = t0; t < t1; ++t) {
-        const float re = q_load<QT>(base + t * stride);
-        const float im = q_load<QT>(base + t * stride + F);
-        sr += (double)re;
-        si += (double)im;
-        sa += (double)__builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
+    for (int64_t t0 = (int64_t)blockIdx.y * kCalTok; t0 < T; t0 += (int64_t)gridDim.y * kCalTok) {
+        const int64_t t1 = t0 + kCalTok < T ? t0 + kCalTok : T;
+        for (int64_t t = t0; t < t1; ++t) {
+            const float re = q_load<QT>(base + t * stride);
+            const float im = q_load<QT>(base + t * stride + F);
+            sr += (double)re;
+            si += (double)im;
+            sa += (double)__builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
+        }
     }
-    double* out = partial + ((int64_t)blockIdx.y * HF + i) * 3;
-    out[0] = sr;
-    out[1] = si;
-    out[2] = sa;
-}
-
-// acc[j] += sum over chunks c (in order) of partial[c * 3HF + j], j < 3HF
-__global__ __launch_bounds__(kCalThreads) void calib_reduce_kernel(const double* __restrict__ partial,
-                                                                   int chunks, int n3,
-                                                                   double* __restrict__ acc) {
-    const int j = blockIdx.x * kCalThreads + threadIdx.x;
-    if (j >= n3) return;
-    double s = 0.0;
-    for (int c = 0; c < chunks; ++c) s += partial[(int64_t)c * n3 + j];
-    acc[j] += s;
+    double* out = slot + ((int64_t)blockIdx.y * HF + i) * 3;
+    out[0] += sr;
+    out[1] += si;
+    out[2] += sa;
 }
 
 // Token counts of up to kCalMaxLayers layers, passed by value.
@@ -168,8 +165,16 @@ __global__ __launch_bounds__(kCalThreads) void calib_finish_kernel(const double*
     const int l = l0 + (int)blockIdx.y;
     const int64_t count = cnt.n[blockIdx.y];
     const int64_t o = (int64_t)l * HF + i;
+    // the layer's slots, in slot order
+    const double* a = acc + ((int64_t)l * kCalSlots * HF + i) * 3;
+    double sr = 0.0, si = 0.0, sa = 0.0;
+    for (int y = 0; y < kCalSlots; ++y) {
+        sr += a[(int64_t)y * HF * 3];
+        si += a[(int64_t)y * HF * 3 + 1];
+        sa += a[(int64_t)y * HF * 3 + 2];
+    }
     const double inv = count > 0 ? 1.0 / (double)count : 0.0;
-    const double mr = acc[3 * o] * inv, mi = acc[3 * o + 1] * inv, ma = acc[3 * o + 2] * inv;
+    const double mr = sr * inv, mi = si * inv, ma = sa * inv;
     q_re[o] = (float)mr;
     q_im[o] = (float)mi;
     if (q_abs) q_abs[o] = (float)ma;
@@ -180,9 +185,7 @@ __global__ __launch_bounds__(kCalThreads) void calib_finish_kernel(const double*
 
 struct tria_calib {
     int L, Hq, hd, F, HF;
-    double* acc = nullptr;      // [L][HF][3]
-    double* partial = nullptr;  // [chunks][HF][3], grown on demand
-    size_t partial_bytes = 0;
+    double* acc = nullptr;      // [L][kCalSlots][HF][3]
     int64_t* count = nullptr;   // host [L]
 };
 
@@ -201,9 +204,10 @@ int tria_calib_create(tria_calib** out, int32_t n_layers, int32_t n_q_heads, int
     c->F = head_dim / 2;
     c->HF = n_q_heads * c->F;
     c->count = static_cast<int64_t*>(calloc((size_t)n_layers, sizeof(int64_t)));
-    const size_t bytes = (size_t)n_layers * c->HF * 3 * sizeof(double);
+    const size_t bytes = (size_t)n_layers * kCalSlots * c->HF * 3 * sizeof(double);
     hipError_t e = c->count ? hipMalloc(reinterpret_cast<void**>(&c->acc), bytes) : hipErrorOutOfMemory;
     if (e == hipSuccess) e = hipMemset(c->acc, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();  // zeroed before any stream's add
     if (e != hipSuccess) {
         tria_calib_free(c);
         return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
@@ -215,7 +219,6 @@ int tria_calib_create(tria_calib** out, int32_t n_layers, int32_t n_q_heads, int
 void tria_calib_free(tria_calib* c) {
     if (!c) return;
     if (c->acc) (void)hipFree(c->acc);
-    if (c->partial) (void)hipFree(c->partial);
     free(c->count);
     delete c;
 }
@@ -228,48 +231,29 @@ int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, 
         return TRIA_E_UNSUPPORTED;
     if (n_tokens == 0) return TRIA_OK;
     const int64_t chunks = (n_tokens + kCalTok - 1) / kCalTok;
-    if (chunks > 65535) return TRIA_E_UNSUPPORTED;  // grid.y; add in batches
-    const size_t need = (size_t)chunks * c->HF * 3 * sizeof(double);
-    if (need > c->partial_bytes) {
-        // earlier adds on this stream may still read the old buffer
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e == hipSuccess && c->partial) e = hipFree(c->partial);
-        c->partial = nullptr;
-        c->partial_bytes = 0;
-        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->partial), need);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
-        c->partial_bytes = need;
-    }
+    const unsigned S = (unsigned)(chunks < kCalSlots ? chunks : kCalSlots);
+    double* slot = c->acc + (int64_t)layer * kCalSlots * c->HF * 3;
     const bool vec = c->F % 4 == 0;
-    // vector path: 256 pairs per block; scalar path: one pair per thread
-    dim3 grid((unsigned)((c->HF + 255) / 256), (unsigned)chunks);
     // 16-byte (8-byte) loads need the rows aligned: the base and the stride
     const size_t esz = q_type == TRIA_Q_F32 ? 4 : 2;
     const bool aligned = (reinterpret_cast<uintptr_t>(q) % (4 * esz)) == 0 && row_stride % 4 == 0;
+    // vector path: 256 pairs per block; scalar path: one pair per thread
+    const dim3 grid(vec && aligned ? (unsigned)((c->HF + 255) / 256)
+                                   : (unsigned)((c->HF + kCalThreads - 1) / kCalThreads), S);
     if (q_type == TRIA_Q_F32) {
         auto k = vec && aligned ? calib_partial4_kernel<float> : calib_partial_kernel<float>;
-        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const float*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
     } else if (q_type == TRIA_Q_F16) {
         auto k = vec && aligned ? calib_partial4_kernel<_Float16> : calib_partial_kernel<_Float16>;
-        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const _Float16*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
     } else {
         auto k = vec && aligned ? calib_partial4_kernel<uint16_t> : calib_partial_kernel<uint16_t>;
-        if (!(vec && aligned)) grid.x = (unsigned)((c->HF + kCalThreads - 1) / kCalThreads);
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const uint16_t*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, c->partial);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return TRIA_E_HIP;
-    const int n3 = 3 * c->HF;
-    hipLaunchKernelGGL(calib_reduce_kernel, dim3((unsigned)((n3 + kCalThreads - 1) / kCalThreads)),
-                       dim3(kCalThreads), 0, stream, c->partial, (int)chunks, n3,
-                       c->acc + (int64_t)layer * n3);
-    e = hipGetLastError();
-    if (e != hipSuccess) return TRIA_E_HIP;
+    if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;
     c->count[layer] += n_tokens;
     return TRIA_OK;
 }
