@@ -91,6 +91,26 @@ def test_shapes(shape):
     run_case(wl, n, budget, sink, window, cap=n + 37)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configurations(seed):
+    """Seeded random configurations across every kernel variant: head dims 32-256
+    (matrix-core and row-per-lane scorers, every compaction chunk width), GQA
+    ratios 1-16, fp16/q8_0 K and V, row counts with ragged tails, and budgets,
+    sinks and windows from empty to covering."""
+    rng = np.random.default_rng(1000 + seed)
+    hd = int(rng.choice([32, 64, 96, 128, 160, 192, 224, 256]))
+    G = int(rng.integers(1, 17))
+    Hkv = int(rng.integers(1, 3))
+    kt, vt = int(rng.choice([F16, Q8])), int(rng.choice([F16, Q8]))
+    n = int(rng.integers(1, 2600))
+    budget = int(rng.integers(0, n + 2))
+    sink = int(rng.integers(0, 9))
+    window = int(rng.choice([0, int(rng.integers(0, n + 1)), int(rng.integers(0, 300))]))
+    wl = variant(WL["tiny_1x1_4k_f16"], name="random%d" % seed, L=int(rng.integers(1, 3)),
+                 Hkv=Hkv, Hq=Hkv * G, hd=hd, k_type=kt, v_type=vt, seed=seed + 50)
+    run_case(wl, n, budget, sink, window, cap=n + int(rng.integers(0, 40)))
+
+
 @pytest.mark.parametrize("n,budget,sink,window", [
     (1, 0, 0, 0), (1, 0, 0, 1), (2, 1, 0, 0), (5, 0, 0, 0), (300, 0, 0, 0), (300, 10, 200, 200),
     (300, 299, 0, 0), (300, 5, 3, 4), (1025, 1024, 0, 1), (1024, 1, 0, 0), (700, 600, 650, 0),
