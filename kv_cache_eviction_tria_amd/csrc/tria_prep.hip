@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 constexpr int kDigitMax = 32639;  // |v| <= 32639 has balanced base-256 digits in [-128, 127]
+constexpr int kPrepHeadDims = 2048;  // trig coefficients of a batch of heads in LDS
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     CacheView cv, Batch b, int k_type, int G, int hd, const float* __restrict__ q_re,
@@ -38,8 +39,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     if (sd.n <= 0) return;
 
     __shared__ double a_re[128], a_im[128];
-    __shared__ double c_full[256];  // one head's trig coefficients, [Re C_0..F-1, Im C_0..F-1]
-    __shared__ float sig_sh[8];
+    // a batch of heads' trig coefficients, head jj at [jj * hd]: [Re C_0..F-1, Im C_0..F-1]
+    __shared__ double c_all[kPrepHeadDims];
+    __shared__ float sig_sh[kPrepHeadDims / 32];
 
     const int64_t p = cv.pos[row_index(cv, id, sd.n - 1)];
     for (int f = threadIdx.x; f < F; f += kPrepThreads) {
@@ -69,49 +71,55 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 
     // q8_0: trig coefficients quantised per (head, 32-dim block) to 16-bit integers
     // v = round(c / sig), split into balanced base-256 digits so that the score
-    // kernel can accumulate sum_d q_d * v_d with packed int8 dot products.
+    // kernel can accumulate sum_d q_d * v_d with int8 products.  The heads are
+    // taken kPrepHeadDims / hd at a time, each phase over all of them at once.
     const int NB = cg.NB, W = cg.W, RB = 34 * NB;
-    for (int j = 0; j < G; ++j) {
-        const int64_t s0 = stat0 + (int64_t)j * F;
-        const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
-        for (int f = threadIdx.x; f < F; f += kPrepThreads) {
+    const int HB = kPrepHeadDims / hd;  // heads per batch (hd <= 256: at least 8)
+    for (int jb = 0; jb < G; jb += HB) {
+        const int nh = G - jb < HB ? G - jb : HB;
+        for (int i = threadIdx.x; i < nh * F; i += kPrepThreads) {
+            const int jj = i / F, f = i - jj * F, j = jb + jj;
+            const int64_t s0 = stat0 + (int64_t)j * F;
+            const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
             const double qr = q_re[s0 + f], qi = q_im[s0 + f];
-            c_full[f] = qr * a_re[f] - qi * a_im[f];
-            c_full[f + F] = qr * a_im[f] + qi * a_re[f];
+            c_all[jj * hd + f] = qr * a_re[f] - qi * a_im[f];
+            c_all[jj * hd + f + F] = qr * a_im[f] + qi * a_re[f];
             outf[cg.w_off + j0 * F + f * gt + (j - j0)] = norm_w[s0 + f];
         }
         __syncthreads();
-        if (threadIdx.x < NB) {
+        for (int i = threadIdx.x; i < nh * NB; i += kPrepThreads) {
+            const int jj = i / NB, blk = i - jj * NB;
             double m = 0.0;
-            for (int t = 0; t < 32; ++t) m = fmax(m, fabs(c_full[32 * threadIdx.x + t]));
+            for (int t = 0; t < 32; ++t) m = fmax(m, fabs(c_all[jj * hd + 32 * blk + t]));
             const float sg = (float)(m / kDigitMax);
-            sig_sh[threadIdx.x] = sg;
-            outf[cg.sig_off + j * NB + threadIdx.x] = sg;
+            sig_sh[jj * NB + blk] = sg;
+            outf[cg.sig_off + (jb + jj) * NB + blk] = sg;
         }
         __syncthreads();
-        for (int k = threadIdx.x; k < W; k += kPrepThreads) {
+        for (int i = threadIdx.x; i < nh * W; i += kPrepThreads) {
+            const int jj = i / W, k = i - jj * W, j = jb + jj;
             uint32_t hi_w = 0, lo_w = 0;
-            for (int i = 0; i < 4; ++i) {
-                const int byte = 4 * k + i;
+            for (int b4 = 0; b4 < 4; ++b4) {
+                const int byte = 4 * k + b4;
                 if (byte >= RB) continue;
                 const int blk = byte / 34, o = byte - 34 * blk;
                 if (o < 2) continue;  // scale bytes get a zero digit
-                const float sg = sig_sh[blk];
+                const float sg = sig_sh[jj * NB + blk];
                 int v = 0;
                 if (sg > 0.0f) {
-                    const double t = c_full[32 * blk + (o - 2)] / (double)sg;
+                    const double t = c_all[jj * hd + 32 * blk + (o - 2)] / (double)sg;
                     v = (int)llrint(t);
                     v = v > kDigitMax ? kDigitMax : (v < -kDigitMax ? -kDigitMax : v);
                 }
                 const int lo = ((v + 128) & 255) - 128;
                 const int hi = (v - lo) / 256;
-                hi_w |= (uint32_t)(hi & 255) << (8 * i);
-                lo_w |= (uint32_t)(lo & 255) << (8 * i);
+                hi_w |= (uint32_t)(hi & 255) << (8 * b4);
+                lo_w |= (uint32_t)(lo & 255) << (8 * b4);
             }
             out[cg.hi_off + j * W + k] = (int32_t)hi_w;
             out[cg.lo_off + j * W + k] = (int32_t)lo_w;
         }
-        __syncthreads();
+        __syncthreads();  // the batch's tables are rewritten by the next one
     }
 }
 
