@@ -74,6 +74,9 @@ extern "C" {
 
 /* Largest number of sequences in one tria_evict_paged_batch call. */
 #define TRIA_MAX_SEQ 64
+/* Largest number of rows (n_tokens) of one unit that any entry point takes;
+ * more gives TRIA_E_UNSUPPORTED before anything is enqueued. */
+#define TRIA_MAX_ROWS 262144
 /* Rows per block of a paged cache. */
 #define TRIA_BLOCK 16
 
@@ -144,7 +147,8 @@ int64_t tria_kept_count(int64_t n_tokens, int64_t budget, int64_t sink, int64_t 
 
 /* Raw per-query-head scores of the first n_tokens rows of every unit.
  *   raw_scores : device [L][Hkv][n_tokens][G] fp32, written.
- * 0 <= n_tokens <= cache->cap.  Returns TRIA_OK or an error code. */
+ * 0 <= n_tokens <= cache->cap, n_tokens <= TRIA_MAX_ROWS.  Returns TRIA_OK or
+ * an error code. */
 int tria_score(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, float *raw_scores,
                hipStream_t stream);
 
@@ -156,7 +160,7 @@ int tria_score(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, float *
  *   raw_scores : device [L][Hkv][n_tokens][G], read.
  *   keep_idx   : device [L][Hkv][kept], written (ascending rows).
  *   agg_out    : device [L][Hkv][n_tokens] fp32, written if not NULL.
- * Returns the kept count (>= 0) or an error code. */
+ * n_tokens <= TRIA_MAX_ROWS.  Returns the kept count (>= 0) or an error code. */
 int64_t tria_select(tria_ctx *ctx, const float *raw_scores, int64_t n_tokens, int64_t budget,
                     int64_t sink, int64_t window, int32_t *keep_idx, float *agg_out,
                     hipStream_t stream);
@@ -187,7 +191,7 @@ int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int
  * for all sequences.  n_tokens, budget: host [n_seq]; kept_out: host [n_seq],
  * written with each sequence's kept count.  Each sequence's rows beyond its
  * kept count are left unspecified; the caller may return those blocks.
- * 1 <= n_seq <= TRIA_MAX_SEQ. */
+ * 1 <= n_seq <= TRIA_MAX_SEQ; every n_tokens[i] <= TRIA_MAX_ROWS. */
 int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t n_seq,
                            const int64_t *n_tokens, const int64_t *budget, int64_t sink,
                            int64_t window, int64_t *kept_out, hipStream_t stream);

@@ -91,7 +91,7 @@ struct tria_ctx {
 
 namespace {
 
-constexpr int64_t kMaxRows = 1024 * 256;  // rows per unit the selector handles
+constexpr int64_t kMaxRows = TRIA_MAX_ROWS;  // rows per unit the selector handles
 
 int hip_fail(tria_ctx* ctx, hipError_t e) {
     if (ctx) ctx->last_hip = (int)e;

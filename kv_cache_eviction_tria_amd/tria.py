@@ -25,6 +25,7 @@ TRIA_E_DEVICE = -5
 TRIA_KV_F16 = 0
 TRIA_KV_Q8_0 = 1
 TRIA_MAX_SEQ = 64
+TRIA_MAX_ROWS = 262144
 TRIA_BLOCK = 16
 
 _lock = threading.Lock()

@@ -36,6 +36,18 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_the_header():
+    """Every #define of the header that the binding restates has the same value."""
+    src = open(os.path.join(ROOT, "include", "tria.h")).read()
+    defs = {m.group(1): int(m.group(2))
+            for m in re.finditer(r"#define\s+(TRIA_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", src)}
+    restated = [n for n in dir(tria) if n.startswith("TRIA_") and isinstance(getattr(tria, n), int)]
+    assert len(restated) >= 10
+    for n in restated:
+        assert n in defs, n
+        assert getattr(tria, n) == defs[n], n
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert tria.tria_strerror(code)

@@ -337,6 +337,39 @@ def test_full_hd256_48x4_128k():
     _full_size(wl, [(0, 0), (47, 3), (23, 2)])
 
 
+@pytest.mark.parametrize("n,k_type", [(131073, Q8), (tria.TRIA_MAX_ROWS, F16)],
+                         ids=["128k+1_q8", "max_f16"])
+def test_units_past_the_register_bins(n, k_type):
+    """Units of more than 128K rows, up to the largest a pass takes: the selector
+    keeps their keys in a global scratch array instead of registers."""
+    wl = variant(WL["tiny_1x1_4k_f16"], name="long", L=1, Hkv=2, Hq=4, hd=64, k_type=k_type,
+                 seed=n % 1000 + 7)
+    run_case(wl, n, n // 10, 4, 1024, cap=n + 5)
+
+
+def test_rows_past_the_maximum_are_refused():
+    """One row more than the largest unit a pass takes is refused before anything
+    is enqueued: the cache is left as it was."""
+    wl = variant(WL["tiny_1x1_4k_f16"], name="too_long", L=1, Hkv=1, Hq=1, hd=32, seed=5)
+    n = tria.TRIA_MAX_ROWS + 1
+    pu.say("case too_long: n %d" % n)
+    case = synth.make_case(wl, device="cpu", n=n, cap=n)
+    ctx = pu.make_ctx(wl, (case["q_re"], case["q_im"], case["w"]))
+    k, v, pos = case["k"].to(DEV), case["v"].to(DEV), case["pos"].to(DEV)
+    k0, v0, p0 = k.clone(), v.clone(), pos.clone()
+    raw = torch.empty(1, 1, n, 1, dtype=torch.float32, device=DEV)
+    keep = torch.empty(1, 1, n, dtype=torch.int32, device=DEV)
+    for call in (lambda: tria.tria_evict(ctx, k, v, pos, n, 1000, 0, 16),
+                 lambda: tria.tria_score(ctx, k, v, pos, n, raw),
+                 lambda: tria.tria_select(ctx, raw, n, 1000, 0, 16, keep)):
+        with pytest.raises(tria.TriaError) as e:
+            call()
+        assert e.value.code == tria.TRIA_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(k, k0) and torch.equal(v, v0) and torch.equal(pos, p0)
+    ctx.close()
+
+
 @pytest.mark.parametrize("k_type", [Q8, F16])
 def test_paged_batch(k_type):
     """Paged cache, 16-row blocks in shuffled physical order, several sequences of
