@@ -203,16 +203,36 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     const int u = blockIdx.x;
     const int seq = u / units_per_seq;
     const int uu = u - seq * units_per_seq;
-    const SeqDesc sd = b.seq[seq];
-    // row indices fit in 32 bits (at most 1024 * 256 rows per unit)
-    const int n = (int)sd.n;
-    if (n <= 0) return;
-    const float* __restrict__ R = raw + sd.raw_off + (int64_t)uu * n * G;
-    int32_t* __restrict__ KI = keep + sd.keep_off + (int64_t)uu * sd.kept;
-    float* AG = agg_out ? agg_out + sd.raw_off / G + (int64_t)uu * n : nullptr;
-    uint32_t* KS = kRegKeys ? nullptr : key_scratch + sd.raw_off / G + (int64_t)uu * n;
-    const int64_t tiles = part_tiles(n);
-    const PartRec* __restrict__ P = part ? part + (sd.part_off + (int64_t)uu * tiles) * G : nullptr;
+    // Everything the kernel needs from the sequence's descriptor is taken here,
+    // as 32-bit values where they fit (at most 1024 * 256 rows per unit): the
+    // descriptor itself is not kept live in scalar registers through the
+    // unrolled loops below.
+    int n, kept, cand_lo, n_cand;
+    const float* __restrict__ R;
+    int32_t* __restrict__ KI;
+    float* AG;
+    uint32_t* KS;
+    const PartRec* __restrict__ P;
+    int32_t* PB;
+    int nb = 0;
+    int64_t tiles;
+    {
+        const SeqDesc& sd = b.seq[seq];
+        n = (int)sd.n;
+        if (n <= 0) return;
+        kept = (int)sd.kept;
+        // candidates: rows [s_end, w_start) (all below n)
+        cand_lo = (int)sd.s_end;
+        n_cand = (int)(sd.w_start - sd.s_end);
+        R = raw + sd.raw_off + (int64_t)uu * n * G;
+        KI = keep + sd.keep_off + (int64_t)uu * kept;
+        AG = agg_out ? agg_out + sd.raw_off / G + (int64_t)uu * n : nullptr;
+        KS = kRegKeys ? nullptr : key_scratch + sd.raw_off / G + (int64_t)uu * n;
+        tiles = part_tiles(n);
+        P = part ? part + (sd.part_off + (int64_t)uu * tiles) * G : nullptr;
+        if (chunk_pb) nb = (int)chunk_bounds(kept);
+        PB = chunk_pb ? chunk_pb + sd.pb_off + (int64_t)uu * nb : nullptr;
+    }
 
     __shared__ HeadNorm norm_sh[64];
     __shared__ uint32_t hist[kBins];
@@ -239,8 +259,6 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     nrm.load(norm_sh);
 
     // 2. aggregated score -> key, histogram of the candidates
-    const int cand_lo = (int)sd.s_end, n_cand = (int)(sd.w_start - sd.s_end);
-    // candidates: rows [s_end, w_start) (all below n)
     auto is_cand = [&](int r) -> bool { return (unsigned)(r - cand_lo) < (unsigned)n_cand; };
     // kRegKeys: each row's histogram bin stays in registers (two per word) and
     // the full key is recomputed from the raw scores for the few rows that
@@ -293,7 +311,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     };
 
     // 3. threshold: the k-th largest candidate key T; krem rows equal to T are taken
-    const int64_t k_take = sd.kept - (n - n_cand);
+    const int k_take = kept - (n - n_cand);
     const bool radix = k_take > 0 && k_take < n_cand;
     const bool take_all = k_take >= n_cand;
     uint32_t T = 0;
@@ -415,11 +433,20 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     // 4. ties at T go to the lowest rows; then write kept rows in order.
     // Row order is (j, wave, lane); ranks = prefix over the (j, wave) counts
     // plus the lane's rank within its wave's ballot.
-    auto ordered_ranks = [&](auto flag_of, auto use_rank) {
-#pragma unroll kRowUnroll<RPT>
-        for (int j = 0; j < RPT; ++j) {
-            const uint64_t m = __ballot(flag_of(j));
-            if (lane == 0) cnt_sh[j * kWaves + wid] = __popcll(m);
+    // Row j * 1024 + t of this thread is bit j % 32 of word j / 32 of a flag
+    // array.  The words are walked with fixed indices and the bits with a loop
+    // counter, so each ballot's lane mask is formed right before its use
+    // (formed all at once, 32 masks of 64 bits spill the scalar registers).
+    auto ordered_ranks = [&](const uint32_t(&bits)[kMW], auto use_rank) {
+#pragma unroll
+        for (int w = 0; w < kMW; ++w) {
+            const uint32_t bw = bits[w];
+            const int jn = RPT - 32 * w < 32 ? RPT - 32 * w : 32;
+#pragma unroll 4
+            for (int jj = 0; jj < jn; ++jj) {
+                const uint64_t m = __ballot((bw >> jj) & 1u);
+                if (lane == 0) cnt_sh[(32 * w + jj) * kWaves + wid] = __popcll(m);
+            }
         }
         __syncthreads();
         constexpr int kPer = (RPT * kWaves + kSelThreads - 1) / kSelThreads;
@@ -438,11 +465,16 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
             if (e < RPT * kWaves) cnt_sh[e] = base + loc[q];
         }
         __syncthreads();
-#pragma unroll kRowUnroll<RPT>
-        for (int j = 0; j < RPT; ++j) {
-            const bool f = flag_of(j);
-            const uint64_t m = __ballot(f);
-            if (f) use_rank(j, cnt_sh[j * kWaves + wid] + lane_rank(m));
+#pragma unroll
+        for (int w = 0; w < kMW; ++w) {
+            const uint32_t bw = bits[w];
+            const int jn = RPT - 32 * w < 32 ? RPT - 32 * w : 32;
+#pragma unroll 4
+            for (int jj = 0; jj < jn; ++jj) {
+                const bool f = ((bw >> jj) & 1u) != 0;
+                const uint64_t m = __ballot(f);
+                if (f) use_rank(w, jj, cnt_sh[(32 * w + jj) * kWaves + wid] + lane_rank(m));
+            }
         }
         __syncthreads();
     };
@@ -469,22 +501,17 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
             }
     }
     if (rank_ties) {
-        ordered_ranks([&](int j) { return ((tiew[j >> 5] >> (j & 31)) & 1u) != 0; },
-                      [&](int j, int rank) {
-                          if (rank < krem) set_keep(j);
-                      });
+        ordered_ranks(tiew, [&](int w, int jj, int rank) {
+            if (rank < krem) kbits[w] |= 1u << jj;
+        });
     }
-    ordered_ranks([&](int j) { return ((kbits[j >> 5] >> (j & 31)) & 1u) != 0; },
-                  [&](int j, int rank) {
-                      if (rank < sd.kept) KI[rank] = (int32_t)row_of(j);
-                  });
+    ordered_ranks(kbits, [&](int w, int jj, int rank) {
+        if (rank < kept) KI[rank] = (int32_t)row_of(32 * w + jj);
+    });
     // The scan's prefix at (j, wave) is the number of kept rows below row
     // 64 (16 j + wave): write it at the compaction's chunk boundaries.
-    if (chunk_pb) {
-        const int nb = (int)chunk_bounds(sd.kept);
-        int32_t* PB = chunk_pb + sd.pb_off + (int64_t)uu * nb;
-        for (int e = t; e < nb; e += kSelThreads)
-            PB[e] = e < RPT * kWaves ? cnt_sh[e] : (int32_t)sd.kept;
+    if (PB) {
+        for (int e = t; e < nb; e += kSelThreads) PB[e] = e < RPT * kWaves ? cnt_sh[e] : kept;
     }
 }
 
