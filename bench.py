@@ -57,8 +57,6 @@ def parse():
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="run one plain streaming kernel (uint8 xor) over this many bytes before "
                          "the timed steps, as the byte reference for profiler counters")
-    ap.add_argument("--layers-per-group", type=int, default=0,
-                    help="tria_set_pipeline: 0 = one group; > 0 = overlapped layer groups")
     ap.add_argument("--keep-mode", choices=sorted(KEEP_MODES), default="per_unit",
                     help="tria_set_keep_mode: who shares a keep set")
     ap.add_argument("--compaction", choices=sorted(COMPACTIONS), default="ordered",
@@ -144,6 +142,33 @@ def log(msg):
     print("# " + msg, file=sys.stderr, flush=True)
 
 
+def dtype_of(wl):
+    """The number formats the pass computes in."""
+    from kv_cache_eviction_tria_amd import synth
+    v = "q8_0" if wl.v_type == synth.KV_Q8_0 else "f16"
+    if wl.k_type == synth.KV_Q8_0 and wl.hd % 128 == 0:
+        k = ("q8_0 K: trig term int8 values (exact in fp16) x fp16 hi/lo coefficients on MFMA "
+             "(fp32 accumulate)")
+    elif wl.k_type == synth.KV_Q8_0:
+        k = ("q8_0 K: trig term int8 x 32-bit coefficient digits on MFMA (i32 accumulate, "
+             "fp32 combine)")
+    else:
+        k = ("f16 K: trig and norm sums on f16 MFMA with hi/lo fp16 coefficient splits "
+             "(fp32 accumulate)")
+    return "%s; norm term |K_f| in fp32; z-norm statistics fp64; %s V moved as bytes" % (k, v)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def bench_contiguous(args, wl):
     tkey = traffic_key_fn(args)
     import numpy as np
@@ -161,7 +186,6 @@ def bench_contiguous(args, wl):
     k0, v0, p0 = k.clone(), v.clone(), pos.clone()
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
-    tria.tria_set_pipeline(ctx, args.layers_per_group)
     tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
     tria.tria_set_compaction(ctx, COMPACTIONS[args.compaction][0])
     K = tria.tria_kept_count(n, B, S, W)
@@ -276,15 +300,14 @@ def bench_contiguous(args, wl):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/f16 in, f32 accumulate" if wl.k_type == synth.KV_Q8_0
-        else "f16 in, f32 accumulate",
+        "dtype": dtype_of(wl),
         "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales; "
                 "lognormal/uniform-phase statistics)",
         "config": {"workload": wl.name, "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.hd, "tokens": n, "budget": B, "sink": S, "window": W,
                    "kept": K, "k_type": "q8_0" if wl.k_type else "f16",
                    "v_type": "q8_0" if wl.v_type else "f16", "parallelism": "single GPU",
-                   "layers_per_group": args.layers_per_group, "keep_mode": args.keep_mode,
+                   "keep_mode": args.keep_mode,
                    "compaction": args.compaction},
         "pass_ms_p10_p90": [float(np.percentile(t_pass, 10)), float(np.percentile(t_pass, 90))],
         "tokens_per_s": n / (ms * 1e-3),
@@ -329,7 +352,6 @@ def bench_paged(args, wl):
     pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, wl.seed, dev)
     ctx = tria.tria_load_stats(wl.L, wl.Hkv, wl.Hq, wl.hd, wl.k_type, wl.v_type, wl.theta,
                                list(wl.offsets), *stats)
-    tria.tria_set_pipeline(ctx, args.layers_per_group)
     tria.tria_set_keep_mode(ctx, KEEP_MODES[args.keep_mode][0])
     tria.tria_set_compaction(ctx, COMPACTIONS[args.compaction][0])
     pools = [pg[x] for x in ("k_pool", "v_pool", "pos_pool", "block_table")]
@@ -416,7 +438,7 @@ def bench_paged(args, wl):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/f16 in, f32 accumulate",
+        "dtype": dtype_of(wl),
         "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales; "
                 "lognormal/uniform-phase statistics; shuffled block order)",
         "config": {"workload": wl.name, "sequences": wl.n_seq, "lengths": lens,
@@ -517,8 +539,7 @@ def bench_decode(args, wl):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/f16 in, f32 accumulate" if wl.k_type == synth.KV_Q8_0
-        else "f16 in, f32 accumulate",
+        "dtype": dtype_of(wl),
         "data": "synthetic (seeded N(0,1) K/V with lognormal channel scales)",
         "config": {"workload": wl.name, "layers": wl.L, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.hd, "start_rows": n0, "budget": wl.budget,
@@ -616,9 +637,9 @@ def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0, compact_mode=0):
 
     import oracle
     log("cpu baseline: oracle on whole passes, about %.0f s" % seconds)
-    times = []
+    times, stages = [], []
     spent = 0.0
-    while not times or (spent < seconds and len(times) < 50):
+    while len(times) < 3 or (spent < seconds and len(times) < 50):
         k, v, pos = k0.copy(), v0.copy(), p0.copy()
         t = time.perf_counter()
         oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
@@ -627,10 +648,15 @@ def cpu_baseline(wl, stats, k0, v0, p0, seconds, keep_mode=0, compact_mode=0):
                      compact_mode=compact_mode)
         dt = time.perf_counter() - t
         times.append(dt)
+        stages.append(oracle.last_stage_seconds())
         spent += dt
     rows = wl.L * wl.Hkv * wl.n
     med = float(np.median(times))
+    st = np.median(np.array(stages), axis=0) * 1e3
     return {"value": rows / med, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "pass_ms_median": med * 1e3,
+            "stage_ms_median": {"score_and_aggregate": float(st[0]), "select": float(st[1]),
+                                "compact": float(st[2])},
             "sample": "%d whole passes (%d units x %d tokens each), %.1f s of CPU time; "
                       "median pass %.3f s" % (len(times), wl.L * wl.Hkv, wl.n, spent, med)}
 

@@ -177,13 +177,11 @@ int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
                  const int32_t *keep_idx, int64_t kept, hipStream_t stream);
 
 /* One whole eviction pass: tria_score, tria_select, tria_compact with the
- * context's own scratch for the scores and kept indices.  Returns the kept
- * count.  budget >= n_tokens enqueues nothing and returns n_tokens.
- * With layer groups (tria_set_pipeline) the compaction of a group runs on a
- * second stream owned by the context while later groups are scored on
- * `stream`; the second stream waits for an event recorded on
- * `stream` and `stream` waits for it before the call returns, so the pass is
- * ordered with respect to `stream` like a single-stream pass. */
+ * context's own scratch for the scores and kept indices, all on `stream`.
+ * Returns the kept count.  budget >= n_tokens enqueues nothing and returns
+ * n_tokens.  The context's scratch grows (hipMalloc) when a pass needs more
+ * than an earlier one; tria_evict_noalloc is the variant that never
+ * allocates. */
 int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
                    int64_t sink, int64_t window, hipStream_t stream);
 
@@ -195,15 +193,6 @@ int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int
 int tria_evict_paged_batch(tria_ctx *ctx, const tria_paged_cache *cache, int32_t n_seq,
                            const int64_t *n_tokens, const int64_t *budget, int64_t sink,
                            int64_t window, int64_t *kept_out, hipStream_t stream);
-
-/* Pipelining of tria_evict / tria_evict_paged_batch.  layers_per_group = 0
- * (the default): every layer is scored, then selected, then compacted, all on
- * the caller's stream.  > 0: the layers are processed in groups of that many
- * (at most 8 groups; larger groups if needed): each group is scored and
- * selected on the caller's stream and compacted on the context's second
- * stream while the later groups are scored (see tria_evict).  Results are
- * identical either way.  Returns TRIA_OK or TRIA_E_INVAL. */
-int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
 
 /* Who shares a keep set in tria_select / tria_evict / tria_evict_paged_batch.
  *   TRIA_KEEP_PER_UNIT (default): every (layer, KV head) unit selects on its
@@ -224,9 +213,7 @@ int tria_set_pipeline(tria_ctx *ctx, int32_t layers_per_group);
  * and the group keeps the protected rows plus its highest-scoring candidates.
  * The raw scores, kept counts and compaction are those of the per-unit pass;
  * keep_idx (and agg_out) are written for every unit, equal within a group.
- * A shared mode runs tria_evict without layer groups (tria_set_pipeline has
- * no effect), since a group spans all layers.  Returns TRIA_OK, or
- * TRIA_E_INVAL for another mode. */
+ * Returns TRIA_OK, or TRIA_E_INVAL for another mode. */
 #define TRIA_KEEP_PER_UNIT 0
 #define TRIA_KEEP_PER_KV_HEAD 1
 #define TRIA_KEEP_GLOBAL 2

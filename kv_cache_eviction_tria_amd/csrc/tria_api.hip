@@ -2,9 +2,11 @@
 // context (device statistics and scratch), and the launch sequence of one
 // pass: prep -> score -> select -> compact, all stream-ordered.
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 
 #include "tria_group.h"
@@ -28,10 +30,6 @@ hipError_t launch_select_impl(const Batch& b, int units_per_seq, int G, const fl
 }  // namespace tria
 
 using namespace tria;
-
-namespace {
-constexpr int kMaxGroups = 8;  // layer groups of one pass (tria_set_pipeline)
-}
 
 struct tria_ctx {
     int L, Hkv, Hq, G, hd, F, k_type, v_type;
@@ -59,11 +57,6 @@ struct tria_ctx {
     size_t pb_bytes = 0;
     CompactState cst = {nullptr, 0, 0, nullptr, nullptr};
     size_t flag_bytes = 0;
-    // second stream and events for overlapping compaction with scoring
-    hipStream_t aux = nullptr;
-    hipEvent_t ev_join = nullptr;
-    hipEvent_t ev_group[8] = {};
-    int layers_per_group = 0;  // 0: one group (tria_set_pipeline)
     // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
     int keep_mode = TRIA_KEEP_PER_UNIT;
     int compact_mode = TRIA_COMPACT_ORDERED;  // tria_set_compaction
@@ -158,13 +151,13 @@ int reserve_flags(tria_ctx* ctx, const Batch& b, int units, hipStream_t s) {
 // A compaction launch, timed when timing is on.  pb: the selector's chunk
 // prefix counts, or nullptr to derive them from keep into ctx->pb.
 int compact_timed(tria_ctx* ctx, const CacheView& cv, const Batch& b, int units,
-                  const int32_t* keep, const int32_t* pb, hipStream_t s, int group = 0) {
+                  const int32_t* keep, const int32_t* pb, hipStream_t s) {
     int slot;
     hipError_t e = timed_begin(ctx, TRIA_STAGE_COMPACT, s, &slot);
     if (e == hipSuccess && ctx->compact_mode == TRIA_COMPACT_HOLE_FILL)
         e = launch_holefill(cv, b, units, keep, s);
     else if (e == hipSuccess)
-        e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, ctx->cst.ticket + group, s);
+        e = launch_compact(cv, b, units, keep, pb, ctx->pb, ctx->cst, ctx->cst.ticket, s);
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
 }
@@ -317,10 +310,9 @@ int reserve_shared(tria_ctx* ctx, const Batch& b, hipStream_t s) {
 // scorer already wrote the moment partials of these scores into ctx->part.
 // A shared keep mode needs all layers (layers < 0).
 int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, float* agg,
-               bool have_part, hipStream_t s, int layers = -1, int group = 0) {
-    const int ups = (layers < 0 ? ctx->L : layers) * ctx->Hkv;
+               bool have_part, hipStream_t s) {
+    const int ups = ctx->L * ctx->Hkv;
     const bool shared = ctx->keep_mode != TRIA_KEEP_PER_UNIT;
-    if (shared && layers >= 0 && layers != ctx->L) return TRIA_E_INVAL;
     int rc = reserve_select(ctx, b, ups, s);
     if (!rc && shared) rc = reserve_shared(ctx, b, s);
     if (rc) return rc;
@@ -331,10 +323,10 @@ int run_select(tria_ctx* ctx, const Batch& b, const float* raw, int32_t* keep, f
         if (shared)
             e = launch_shared_select(b, ctx->L, ctx->Hkv, ctx->G, ctx->keep_mode, raw, ctx->part,
                                      ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb, ctx->keys, keep,
-                                     ctx->pb, agg, ctx->cst.ticket + group, s);
+                                     ctx->pb, agg, ctx->cst.ticket, s);
         else
             e = launch_select_impl(b, ups, ctx->G, raw, ctx->part, keep, agg, ctx->keys, ctx->pb,
-                                   ctx->cst.ticket + group, s);
+                                   ctx->cst.ticket, s);
     }
     if (e == hipSuccess) e = timed_end(ctx, slot, s);
     if (e != hipSuccess) return hip_fail(ctx, e);
@@ -353,71 +345,21 @@ CacheView sub_view(const CacheView& cv, int l0, int lg) {
     return s;
 }
 
-// Per-sequence offsets of the raw-score and kept-index blocks of layers l0...
-Batch sub_batch(const Batch& b, int l0, int L, int Hkv, int G) {
-    Batch s = b;
-    for (int i = 0; i < b.n_seq; ++i) {
-        s.seq[i].raw_off += (int64_t)l0 * Hkv * b.seq[i].n * G;
-        s.seq[i].keep_off += (int64_t)l0 * Hkv * b.seq[i].kept;
-        s.seq[i].part_off += (int64_t)l0 * Hkv * part_tiles(b.seq[i].n);
-        s.seq[i].pb_off += (int64_t)l0 * Hkv * chunk_bounds(b.seq[i].kept);
-    }
-    s.coef_L = b.coef_L ? b.coef_L : L;
-    s.coef_l0 = b.coef_l0 + l0;
-    return s;
-}
-
-
-// One whole pass (score -> select -> compact).  With more than one group of
-// layers (tria_set_pipeline): the coefficient tables of all layers are built
-// first, then each group is scored and selected on `s`, and its compaction
-// runs on the context's second stream (after an event recorded on `s`) while
-// the next groups are scored.  Each group's compaction takes its tasks from
-// its own ticket counter, which that group's selection resets.  `s` waits for
-// the last compaction, so the pass stays ordered with respect to `s`.
+// One whole pass (score -> select -> compact) over every unit of the batch, on `s`.
 int run_pass(tria_ctx* ctx, const CacheView& cv, const Batch& b, hipStream_t s) {
-    const int L = ctx->L, n_seq = b.n_seq;
-    // a shared keep set spans all layers: no layer groups
-    const int lpg = ctx->layers_per_group > 0 && ctx->keep_mode == TRIA_KEEP_PER_UNIT
-                        ? ctx->layers_per_group
-                        : L;
-    int ng = (L + lpg - 1) / lpg;
-    ng = ng > kMaxGroups ? kMaxGroups : ng;
-    const int all_units = n_seq * L * ctx->Hkv;
+    const int all_units = b.n_seq * ctx->L * ctx->Hkv;
     // all scratch is sized for the whole pass before any work is queued
-    int rc = reserve_select(ctx, b, L * ctx->Hkv, s);
+    int rc = reserve_select(ctx, b, ctx->L * ctx->Hkv, s);
     if (rc) return rc;
     rc = reserve_flags(ctx, b, all_units, s);
     if (rc) return rc;
     rc = run_prep(ctx, cv, b, all_units, s);
     if (rc) return rc;
-    if (ng <= 1 || !ctx->aux) {
-        rc = run_score_only(ctx, cv, b, all_units, ctx->raw, ctx->part, s);
-        if (rc) return rc;
-        rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, true, s);
-        if (rc) return rc;
-        return compact_timed(ctx, cv, b, all_units, ctx->keep, ctx->pb, s);
-    }
-    const int per = (L + ng - 1) / ng;
-    hipError_t e = hipSuccess;
-    for (int g = 0, l0 = 0; l0 < L; ++g, l0 += per) {
-        const int lg = (L - l0) < per ? (L - l0) : per;
-        const CacheView sv = sub_view(cv, l0, lg);
-        const Batch sb = sub_batch(b, l0, L, ctx->Hkv, ctx->G);
-        const int units = n_seq * lg * ctx->Hkv;
-        rc = run_score_only(ctx, sv, sb, units, ctx->raw, ctx->part, s);
-        if (rc) return rc;
-        rc = run_select(ctx, sb, ctx->raw, ctx->keep, nullptr, true, s, lg, g);
-        if (rc) return rc;
-        e = hipEventRecord(ctx->ev_group[g], s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(ctx->aux, ctx->ev_group[g], 0);
-        if (e != hipSuccess) return hip_fail(ctx, e);
-        rc = compact_timed(ctx, sv, sb, units, ctx->keep, ctx->pb, ctx->aux, g);
-        if (rc) return rc;
-    }
-    e = hipEventRecord(ctx->ev_join, ctx->aux);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, ctx->ev_join, 0);
-    return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+    rc = run_score_only(ctx, cv, b, all_units, ctx->raw, ctx->part, s);
+    if (rc) return rc;
+    rc = run_select(ctx, b, ctx->raw, ctx->keep, nullptr, true, s);
+    if (rc) return rc;
+    return compact_timed(ctx, cv, b, all_units, ctx->keep, ctx->pb, s);
 }
 
 // One decode step's attention over every unit of the batch (q, out: [seq][L]
@@ -437,6 +379,35 @@ int run_attention(tria_ctx* ctx, const CacheView& cv, const Batch& b, const floa
                                           q, scale, n_split, rps, ctx->att_parts, ctx->att_acc,
                                           out, s);
     return e == hipSuccess ? TRIA_OK : hip_fail(ctx, e);
+}
+
+// Why a model is outside the kernels' eligibility gate, or nullptr (llama.cpp
+// page, section 4 "GPU scoring requirements": integer GQA ratio, head_dim <=
+// 256 and a multiple of 32; every dimension rotary, which tria_model_desc
+// cannot express otherwise).
+const char* gate_reason(const tria_model_desc* d) {
+    if (d->n_q_heads % d->n_kv_heads != 0) return "query heads not a multiple of KV heads";
+    if (d->n_q_heads / d->n_kv_heads > 64) return "more than 64 query heads per KV head";
+    if (d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0)
+        return "head_dim not a multiple of 32 in [32, 256]";
+    if (d->k_type != TRIA_KV_F16 && d->k_type != TRIA_KV_Q8_0) return "unknown K type";
+    if (d->v_type != TRIA_KV_F16 && d->v_type != TRIA_KV_Q8_0) return "unknown V type";
+    return nullptr;
+}
+
+// With TRIA_DEBUG set (and not "0") in the environment, the first model
+// description a process passes to tria_load_stats is reported on stderr, once:
+// its shape and whether the kernels take it (the llama.cpp page prints the same
+// decision once at startup).
+void log_gate_once(const tria_model_desc* d, const char* why) {
+    static std::atomic<int> done{0};
+    const char* env = getenv("TRIA_DEBUG");
+    if (!env || !env[0] || (env[0] == '0' && !env[1])) return;
+    if (done.exchange(1)) return;
+    auto kt = [](int t) { return t == TRIA_KV_F16 ? "f16" : (t == TRIA_KV_Q8_0 ? "q8_0" : "?"); };
+    fprintf(stderr, "tria: gpu gate - k=%s v=%s nq=%d nkv=%d hd=%d nonrot=0 -> %s%s\n",
+            kt(d->k_type), kt(d->v_type), d->n_q_heads, d->n_kv_heads, d->head_dim,
+            why ? "not eligible: " : "eligible", why ? why : "");
 }
 
 }  // namespace
@@ -521,10 +492,6 @@ void tria_free(tria_ctx* ctx) {
                     ctx->norms, ctx->gagg, ctx->gkeep, ctx->gpb, ctx->att_parts, ctx->att_acc};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
-    if (ctx->aux) (void)hipStreamDestroy(ctx->aux);
-    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
-    for (hipEvent_t ev : ctx->ev_group)
-        if (ev) (void)hipEventDestroy(ev);
     for (auto& pr : ctx->tev)
         for (hipEvent_t ev : pr)
             if (ev) (void)hipEventDestroy(ev);
@@ -545,11 +512,9 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
         if (i > 0 && d->offsets[i] <= d->offsets[i - 1]) return TRIA_E_INVAL;
     }
     // eligibility gate (llama.cpp page, section 4 "GPU scoring requirements")
-    if (d->n_q_heads % d->n_kv_heads != 0) return TRIA_E_UNSUPPORTED;
-    if (d->n_q_heads / d->n_kv_heads > 64) return TRIA_E_UNSUPPORTED;
-    if (d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0) return TRIA_E_UNSUPPORTED;
-    if (tria_row_bytes(d->k_type, d->head_dim) < 0 || tria_row_bytes(d->v_type, d->head_dim) < 0)
-        return TRIA_E_UNSUPPORTED;
+    const char* why = gate_reason(d);
+    log_gate_once(d, why);
+    if (why) return TRIA_E_UNSUPPORTED;
 
     tria_ctx* ctx = new (std::nothrow) tria_ctx();
     if (!ctx) return TRIA_E_NOMEM;
@@ -600,14 +565,8 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
     // error word of the compaction's bounded waits, and its task ticket
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.err), sizeof(int));
     if (e == hipSuccess) e = hipMemset(ctx->cst.err, 0, sizeof(int));
-    if (e == hipSuccess)
-        e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), kMaxGroups * sizeof(uint32_t));
-    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, kMaxGroups * sizeof(uint32_t));
-    // second stream (default priority) and events for overlapped passes
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->aux, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
-    for (int i = 0; i < kMaxGroups && e == hipSuccess; ++i)
-        e = hipEventCreateWithFlags(&ctx->ev_group[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, sizeof(uint32_t));
     if (e != hipSuccess) {
         const int rc = e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
         tria_free(ctx);
@@ -738,12 +697,6 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
     cv.kb = ctx->kb;
     cv.vb = ctx->vb;
     return run_pass(ctx, cv, b, stream);
-}
-
-int tria_set_pipeline(tria_ctx* ctx, int32_t layers_per_group) {
-    if (!ctx || layers_per_group < 0) return TRIA_E_INVAL;
-    ctx->layers_per_group = layers_per_group;
-    return TRIA_OK;
 }
 
 int tria_set_compaction(tria_ctx* ctx, int32_t mode) {

@@ -222,13 +222,24 @@ __host__ __device__ inline int subgroup_start(int G, int j) {
 // Per-head arrays are stored sub-group by sub-group so that the score kernel
 // addresses its sub-group with compile-time strides:
 //   f16 : float, sub-group block at j0*F*3: [F][gt][3] = {Re C, Im C, w}
-//   q8_0: int32 hi[G][W], int32 lo[G][W], float sig[G][NB],
+//   q8_0, hd % 128 == 0 (q8_f16): trig coefficients as fp16 pairs hi + lo,
+//         laid out like the stored row: for stored word k (bytes 4k..4k+3) of
+//         head j, the coefficients of those four bytes (zero for scale bytes)
+//         as four halves in two words: hi[G][W][2], lo[G][W][2]; each head's
+//         coefficients carry a power-of-two scale, undone by osc[G] (float);
 //         float w with sub-group block at j0*F: [F][gt]
-//         (hi, lo: balanced base-256 digits of the quantised trig coefficients,
-//          packed in the byte order of the stored row; W = words per row)
+//   q8_0, other widths: int32 digit[kCoefDigits][G][W], float sig[G][NB],
+//         float w with sub-group block at j0*F: [F][gt]
+//         (digit i: base-256 digit i, least significant first, of the
+//          32-bit quantised trig coefficients, packed in the byte order of the
+//          stored row; W = words per row)
+constexpr int kCoefDigits = 4;
 struct CoefGeom {
     int hd, F, G, NB, W;
-    int hi_off, lo_off, sig_off, w_off;
+    bool q8_f16;
+    int hi_off, lo_off, osc_off;  // q8_f16
+    int digit_off, sig_off;       // integer digits
+    int w_off;
     int words;
 };
 
@@ -239,13 +250,19 @@ __host__ __device__ inline CoefGeom coef_geom(int k_type, int hd, int G) {
     cg.G = G;
     cg.NB = hd / 32;
     cg.W = (34 * cg.NB + 3) / 4;
+    cg.q8_f16 = k_type == TRIA_KV_Q8_0 && hd % 128 == 0;
+    cg.hi_off = cg.lo_off = cg.osc_off = cg.digit_off = cg.sig_off = cg.w_off = 0;
     if (k_type == TRIA_KV_F16) {
-        cg.hi_off = cg.lo_off = cg.sig_off = cg.w_off = 0;
         cg.words = cg.F * G * 3;
-    } else {
+    } else if (cg.q8_f16) {
         cg.hi_off = 0;
-        cg.lo_off = G * cg.W;
-        cg.sig_off = 2 * G * cg.W;
+        cg.lo_off = 2 * G * cg.W;
+        cg.osc_off = 4 * G * cg.W;
+        cg.w_off = cg.osc_off + G;
+        cg.words = cg.w_off + cg.F * G;
+    } else {
+        cg.digit_off = 0;  // digit i of head j at i * G * W + j * W
+        cg.sig_off = kCoefDigits * G * cg.W;
         cg.w_off = cg.sig_off + G * cg.NB;
         cg.words = cg.w_off + cg.F * G;
     }

@@ -21,7 +21,8 @@ namespace tria {
 namespace {
 
 constexpr int kPrepThreads = 256;
-constexpr int kDigitMax = 32639;  // |v| <= 32639 has balanced base-256 digits in [-128, 127]
+// |v| <= 127 * (2^24 + 2^16 + 2^8 + 1) has four balanced base-256 digits in [-128, 127]
+constexpr int64_t kDigitMax = 2139062143;
 constexpr int kPrepHeadDims = 2048;  // trig coefficients of a batch of heads in LDS
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
@@ -69,10 +70,70 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
         return;
     }
 
-    // q8_0: trig coefficients quantised per (head, 32-dim block) to 16-bit integers
-    // v = round(c / sig), split into balanced base-256 digits so that the score
-    // kernel can accumulate sum_d q_d * v_d with int8 products.  The heads are
-    // taken kPrepHeadDims / hd at a time, each phase over all of them at once.
+    if (cg.q8_f16) {
+        // q8_0, hd % 128 == 0: each head's trig coefficients scaled by 2^e (its
+        // largest magnitude into [2^14, 2^15), inside the fp16 range with room
+        // below) and split into fp16 hi + lo, about 22 significant bits of every
+        // coefficient whatever its size against the others; osc = 2^-e undoes
+        // the scale.  Coefficients are placed at the byte positions of the
+        // stored row (zero at the block scales), four per stored word.
+        const int W = cg.W, RB = 34 * cg.NB;
+        __shared__ int ex_sh[64];
+        for (int j = threadIdx.x; j < G; j += kPrepThreads) {
+            const int64_t s0 = stat0 + (int64_t)j * F;
+            double m = 0.0;
+            for (int f = 0; f < F; ++f) {
+                const double qr = q_re[s0 + f], qi = q_im[s0 + f];
+                m = fmax(m, fmax(fabs(qr * a_re[f] - qi * a_im[f]), fabs(qr * a_im[f] + qi * a_re[f])));
+            }
+            int ex = 0;
+            if (m > 0.0 && isfinite(m)) ex = 14 - ilogb(m);
+            ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
+            ex_sh[j] = ex;
+            outf[cg.osc_off + j] = ldexpf(1.0f, -ex);
+        }
+        for (int i = threadIdx.x; i < F * G; i += kPrepThreads) {
+            const int j = i / F, f = i - j * F;
+            const int j0 = subgroup_start(G, j), gt = subgroup_size(G, j0);
+            outf[cg.w_off + j0 * F + f * gt + (j - j0)] = norm_w[stat0 + (int64_t)j * F + f];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < G * W; i += kPrepThreads) {
+            const int j = i / W, k = i - j * W;
+            const int64_t s0 = stat0 + (int64_t)j * F;
+            uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+            for (int b4 = 0; b4 < 4; ++b4) {
+                const int byte = 4 * k + b4;
+                if (byte >= RB) continue;
+                const int blk = byte / 34, o = byte - 34 * blk;
+                if (o < 2) continue;  // scale bytes: zero coefficients
+                const int d = 32 * blk + (o - 2);
+                const int f = d < F ? d : d - F;
+                const double qr = q_re[s0 + f], qi = q_im[s0 + f];
+                const double c = d < F ? qr * a_re[f] - qi * a_im[f] : qr * a_im[f] + qi * a_re[f];
+                const float x = (float)ldexp(c, ex_sh[j]);
+                const _Float16 h = (_Float16)x;
+                const _Float16 l = (_Float16)(x - (float)h);
+                hw[b4 >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, h) << (16 * (b4 & 1));
+                lw[b4 >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, l) << (16 * (b4 & 1));
+            }
+            out[cg.hi_off + (j * W + k) * 2 + 0] = (int32_t)hw[0];
+            out[cg.hi_off + (j * W + k) * 2 + 1] = (int32_t)hw[1];
+            out[cg.lo_off + (j * W + k) * 2 + 0] = (int32_t)lw[0];
+            out[cg.lo_off + (j * W + k) * 2 + 1] = (int32_t)lw[1];
+        }
+        return;
+    }
+
+    // q8_0: trig coefficients quantised per (head, 32-dim block) to 32-bit integers
+    // v = round(c / sig), sig = (block max) / kDigitMax, split into four balanced
+    // base-256 digits so that the score kernel can accumulate sum_d q_d * v_d
+    // with int8 products.  The error of a coefficient is at most sig / 2, about
+    // 2^-32 of the block maximum: a coefficient 1e4 times smaller than its
+    // block's largest still keeps about 18 significant bits (16-bit integers
+    // kept 2 or 3, too few when the keys are large on exactly those dimensions).
+    // The heads are taken kPrepHeadDims / hd at a time, each phase over all of
+    // them at once.
     const int NB = cg.NB, W = cg.W, RB = 34 * NB;
     const int HB = kPrepHeadDims / hd;  // heads per batch (hd <= 256: at least 8)
     for (int jb = 0; jb < G; jb += HB) {
@@ -91,33 +152,34 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
             const int jj = i / NB, blk = i - jj * NB;
             double m = 0.0;
             for (int t = 0; t < 32; ++t) m = fmax(m, fabs(c_all[jj * hd + 32 * blk + t]));
-            const float sg = (float)(m / kDigitMax);
+            const float sg = (float)(m / (double)kDigitMax);
             sig_sh[jj * NB + blk] = sg;
             outf[cg.sig_off + (jb + jj) * NB + blk] = sg;
         }
         __syncthreads();
         for (int i = threadIdx.x; i < nh * W; i += kPrepThreads) {
             const int jj = i / W, k = i - jj * W, j = jb + jj;
-            uint32_t hi_w = 0, lo_w = 0;
+            uint32_t dw[kCoefDigits] = {};
             for (int b4 = 0; b4 < 4; ++b4) {
                 const int byte = 4 * k + b4;
                 if (byte >= RB) continue;
                 const int blk = byte / 34, o = byte - 34 * blk;
-                if (o < 2) continue;  // scale bytes get a zero digit
+                if (o < 2) continue;  // scale bytes get zero digits
                 const float sg = sig_sh[jj * NB + blk];
-                int v = 0;
+                int64_t v = 0;
                 if (sg > 0.0f) {
                     const double t = c_all[jj * hd + 32 * blk + (o - 2)] / (double)sg;
-                    v = (int)llrint(t);
+                    v = llrint(t);
                     v = v > kDigitMax ? kDigitMax : (v < -kDigitMax ? -kDigitMax : v);
                 }
-                const int lo = ((v + 128) & 255) - 128;
-                const int hi = (v - lo) / 256;
-                hi_w |= (uint32_t)(hi & 255) << (8 * b4);
-                lo_w |= (uint32_t)(lo & 255) << (8 * b4);
+                for (int dg = 0; dg < kCoefDigits; ++dg) {
+                    const int64_t d = ((v + 128) & 255) - 128;  // balanced digit
+                    dw[dg] |= (uint32_t)(d & 255) << (8 * b4);
+                    v = (v - d) / 256;
+                }
             }
-            out[cg.hi_off + j * W + k] = (int32_t)hi_w;
-            out[cg.lo_off + j * W + k] = (int32_t)lo_w;
+            for (int dg = 0; dg < kCoefDigits; ++dg)
+                out[cg.digit_off + (dg * G + j) * W + k] = (int32_t)dw[dg];
         }
         __syncthreads();  // the batch's tables are rewritten by the next one
     }

@@ -20,8 +20,8 @@
 // is shared by all G heads.
 //
 // q8_0 rows: the trig part is an integer dot product per 32-value block:
-// sum_d q_d c_d = sig * sum_d q_d v_d with v the 16-bit quantised coefficient
-// split into two base-256 digits, taken straight from the stored bytes (the
+// sum_d q_d c_d = sig * sum_d q_d v_d with v the 32-bit quantised coefficient
+// split into four base-256 digits, taken straight from the stored bytes (the
 // digit tables follow the row's byte layout, scale bytes carry zero digits) on
 // the matrix cores as 4x4x4 int8 blocks whose lanes are the rows (see the
 // kernel); the block scale d and sig are applied once per block.  The |K_f|
@@ -241,15 +241,13 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(k
     const int64_t wbase = wave_tile() * kPartRows;
     const CoefGeom cg = coef_geom(TRIA_KV_Q8_0, HD, G);
     const int32_t* __restrict__ T = coef + coef_unit(b, cv, id) * coef_words;
-    const int32_t* __restrict__ HI = T + cg.hi_off + j0 * W;
-    const int32_t* __restrict__ LO = T + cg.lo_off + j0 * W;
     // The trig digits of this sub-group as matrix-core A operands: word k of
     // head slot h (zero for slots past the sub-group), one table per digit.
     constexpr int HS = GT < 4 ? 4 : GT;  // head slots, a multiple of 4
-    __shared__ uint32_t dtab[2][HS][W];
-    for (int i = threadIdx.x; i < 2 * HS * W; i += kScoreThreads) {
+    __shared__ uint32_t dtab[kCoefDigits][HS][W];
+    for (int i = threadIdx.x; i < kCoefDigits * HS * W; i += kScoreThreads) {
         const int dg = i / (HS * W), h = (i / W) % HS, k = i % W;
-        dtab[dg][h][k] = h < GT ? (uint32_t)(dg ? HI : LO)[h * W + k] : 0u;
+        dtab[dg][h][k] = h < GT ? (uint32_t)T[cg.digit_off + (dg * G + j0 + h) * W + k] : 0u;
     }
     __syncthreads();
     if (wbase >= n) return;
@@ -321,32 +319,40 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(k
         // products run on the matrix cores as 4x4x4 int8 blocks (16 per
         // instruction): block q of v_mfma_i32_4x4x4i8 is lanes 4q .. 4q + 3, its B
         // operand is word k of those lanes' four rows, its A operand lane 4q + m
-        // holds head m's digits of word k, and the result lane 4q + n holds the
+        // holds head m's digit of word k, and the result lane 4q + n holds the
         // four heads' sums of its own row n, so every lane keeps its row.
         // (Words never hold quants of two blocks: a block's two scale bytes
-        // separate them, and the scale bytes carry zero digits.)
+        // separate them, and the scale bytes carry zero digits.)  The four
+        // digits' sums e_i (|e_i| <= 32 * 127 * 128 < 2^19) form two exact
+        // 32-bit integers, e3 * 256 + e2 (weight 2^16) and e1 * 256 + e0, each
+        // rounded once to fp32 and accumulated with the (head, block) scale.
+        // Digits go two at a time, so two accumulators per head slot are live.
         const uint32_t* __restrict__ dt = &dtab[0][0][0] + z + (threadIdx.x & 3) * W;
 #pragma unroll
         for (int bk = 0; bk < NB; ++bk) {
-            sync_acc<GT>(acc);
             const int k0 = (34 * bk + 2) >> 2, k1 = (34 * bk + 33) >> 2;
-            i32x4 chi[HS / 4], clo[HS / 4];
 #pragma unroll
-            for (int c = 0; c < HS / 4; ++c) chi[c] = clo[c] = i32x4{0, 0, 0, 0};
+            for (int half = 1; half >= 0; --half) {
+                sync_acc<GT>(acc);
+                i32x4 chi[HS / 4], clo[HS / 4];
 #pragma unroll
-            for (int k = k0; k <= k1; ++k) {
+                for (int c = 0; c < HS / 4; ++c) chi[c] = clo[c] = i32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int c = 0; c < HS / 4; ++c) {
-                    const int ahi = (int)dt[(HS + 4 * c) * W + k];
-                    const int alo = (int)dt[(4 * c) * W + k];
-                    chi[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(ahi, (int)wv[k], chi[c], 0, 0, 0);
-                    clo[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(alo, (int)wv[k], clo[c], 0, 0, 0);
+                for (int k = k0; k <= k1; ++k) {
+#pragma unroll
+                    for (int c = 0; c < HS / 4; ++c) {
+                        const int ahi = (int)dt[((2 * half + 1) * HS + 4 * c) * W + k];
+                        const int alo = (int)dt[((2 * half) * HS + 4 * c) * W + k];
+                        chi[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(ahi, (int)wv[k], chi[c], 0, 0, 0);
+                        clo[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(alo, (int)wv[k], clo[c], 0, 0, 0);
+                    }
                 }
-            }
+                const float wgt = half ? 65536.0f : 1.0f;
 #pragma unroll
-            for (int j = 0; j < GT; ++j)
-                acc[j] = fmaf((float)(chi[j >> 2][j & 3] * 256 + clo[j >> 2][j & 3]),
-                              dsc[bk] * SIG[z + j * NB + bk], acc[j]);
+                for (int j = 0; j < GT; ++j)
+                    acc[j] = fmaf((float)(chi[j >> 2][j & 3] * 256 + clo[j >> 2][j & 3]),
+                                  dsc[bk] * (wgt * SIG[z + j * NB + bk]), acc[j]);
+            }
         }
         // |K_f| term
         constexpr int CPQ = GT >= 8 ? 2 : 16 / GT;
@@ -367,6 +373,169 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(k
     if (part) emit_moments<GT>(mom, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
 }
 
+
+// ---------------------------------------------------------------------------
+// q8_0 rows with hd % 128 == 0: row-per-lane, the trig products on the matrix
+// cores in fp16.
+//
+// The row's int8 values are exact in fp16, so each stored word (four bytes) is
+// fed as four halves to v_mfma_f32_4x4x4f16, blocked like the integer kernel
+// above: block q of the instruction is lanes 4q .. 4q + 3, its B operand the
+// four halves of one stored word of those lanes' rows, its A operand lane
+// 4q + m head m's coefficients of the same four bytes (fp16 hi, then lo, each
+// head scaled by a power of two; zero at the block scales), the result lane
+// 4q + n the four heads' sums of row n.  Coefficients keep ~22 bits each, the
+// products are exact and the sums fp32.  A Re dimension d < hd/2 and its Im
+// partner d + hd/2 sit 17 * NB bytes apart, a whole number of words when
+// NB % 4 == 0, so words k and k + 17 NB / 4 are taken together: their int8
+// values are converted once (to fp32, then packed to fp16 for the matrix
+// cores) and serve both the trig products of their two blocks and the |K_f|
+// of the pairs they hold.  Per Re block b (and its Im block b + NB/2) the
+// products accumulate unscaled and are scaled by the blocks' d and the heads'
+// 2^-e once.
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int HD, int GT>
+__global__ __launch_bounds__(kScoreThreads) void score_q8_f16_kernel(
+    CacheView cv, Batch b, int G, int j0, const int32_t* __restrict__ coef, int coef_words,
+    float* __restrict__ raw, PartRec* __restrict__ part) {
+    constexpr int F = HD / 2;
+    constexpr int NB = HD / 32;
+    constexpr int RB = 34 * NB;       // row bytes (a multiple of 8)
+    constexpr int W = RB / 4;         // words per row
+    constexpr int OFFW = 17 * NB / 4; // Re word k pairs with Im word k + OFFW
+    static_assert(NB % 4 == 0, "pairs must be whole words apart");
+    const int u = blockIdx.y;
+    const UnitId id = unit_id(cv, u);
+    const int64_t n = b.seq[id.seq].n;
+    if ((int64_t)blockIdx.x * (kScoreThreads / 64) * kPartRows >= n) return;  // whole block
+    const int64_t wbase = wave_tile() * kPartRows;
+    const CoefGeom cg = coef_geom(TRIA_KV_Q8_0, HD, G);
+    const int32_t* __restrict__ T = coef + coef_unit(b, cv, id) * coef_words;
+    // A operands of this sub-group: [head slot][word] = {hi halves, lo halves}
+    // (zero past the sub-group)
+    constexpr int HS = GT < 4 ? 4 : GT;
+    __shared__ u32x4 atab[HS][W];
+    for (int i = threadIdx.x; i < HS * W; i += kScoreThreads) {
+        const int h = i / W, k = i % W;
+        u32x4 a = {0u, 0u, 0u, 0u};
+        if (h < GT) {
+            const int32_t* hi = T + cg.hi_off + ((j0 + h) * W + k) * 2;
+            const int32_t* lo = T + cg.lo_off + ((j0 + h) * W + k) * 2;
+            a = u32x4{(uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)lo[0], (uint32_t)lo[1]};
+        }
+        atab[h][k] = a;
+    }
+    __syncthreads();
+    if (wbase >= n) return;
+    const float* __restrict__ OSC = reinterpret_cast<const float*>(T + cg.osc_off) + j0;
+    const float* __restrict__ WT = reinterpret_cast<const float*>(T + cg.w_off) + j0 * F;
+    float* rout = raw + b.seq[id.seq].raw_off + ((int64_t)id.l * cv.Hkv + id.g) * n * G + j0;
+    const bool packed = (G == GT);
+    WaveMoments<GT> mom;
+
+#pragma unroll 1
+    for (int it = 0; it < kPartLaneRows; ++it) {
+        const int64_t r0 = wbase + it * 64;
+        if (r0 >= n) break;
+        const int r_out = (int)r0 + (int)(threadIdx.x & 63);  // n < 2^31
+        const int64_t r = r_out < n ? r_out : n - 1;
+        const int z = opaque_zero_s();
+        const uint8_t* rp = cv.k + row_index(cv, id, r) * RB;
+        uint32_t wv[W];
+        if constexpr (RB % 16 == 0) {
+            const u32x4* p4 = reinterpret_cast<const u32x4*>(rp);
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i) {
+                const u32x4 t = p4[i];
+                wv[4 * i] = t.x; wv[4 * i + 1] = t.y; wv[4 * i + 2] = t.z; wv[4 * i + 3] = t.w;
+            }
+        } else {
+            const u32x2* p2 = reinterpret_cast<const u32x2*>(rp);
+#pragma unroll
+            for (int i = 0; i < W / 2; ++i) {
+                const u32x2 t = p2[i];
+                wv[2 * i] = t.x; wv[2 * i + 1] = t.y;
+            }
+        }
+        float dsc[NB];
+#pragma unroll
+        for (int bk = 0; bk < NB; ++bk) {
+            const int o = 34 * bk;
+            dsc[bk] = (o & 2) ? half_hi(wv[o >> 2]) : half_lo(wv[o >> 2]);
+        }
+        float acc[GT];
+#pragma unroll
+        for (int j = 0; j < GT; ++j) acc[j] = 0.0f;
+        const u32x4* __restrict__ at = &atab[0][0] + z + (threadIdx.x & 3) * W;
+
+#pragma unroll
+        for (int bk = 0; bk < NB / 2; ++bk) {  // Re block bk with Im block bk + NB/2
+            sync_acc<GT>(acc);
+            const int k0 = (34 * bk + 2) >> 2, k1 = (34 * bk + 33) >> 2;
+            f32x4v cre[HS / 4], cim[HS / 4];
+#pragma unroll
+            for (int c = 0; c < HS / 4; ++c) cre[c] = cim[c] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = k0; k <= k1; ++k) {
+                // the word's int8 values as fp32 (0 at scale bytes, whose coefficients
+                // are zero), packed to fp16 for the matrix cores (exact: |q| <= 127)
+                float xr[4], xi[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = 4 * k + e - 34 * bk;
+                    const bool quant = o >= 2 && o < 34;
+                    xr[e] = quant ? sbyte(wv[k], e) : 0.0f;
+                    xi[e] = quant ? sbyte(wv[k + OFFW], e) : 0.0f;
+                }
+                const half4v bre = __builtin_bit_cast(
+                    half4v, u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xr[0], xr[1])),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xr[2], xr[3]))});
+                const half4v bim = __builtin_bit_cast(
+                    half4v, u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xi[0], xi[1])),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xi[2], xi[3]))});
+#pragma unroll
+                for (int c = 0; c < HS / 4; ++c) {
+                    const u32x4* a = at + (4 * c) * W;
+                    const u32x4 ar = a[k], ai = a[k + OFFW];
+                    cre[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        __builtin_bit_cast(half4v, u32x2{ar.x, ar.y}), bre, cre[c], 0, 0, 0);
+                    cim[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        __builtin_bit_cast(half4v, u32x2{ai.x, ai.y}), bim, cim[c], 0, 0, 0);
+                    cre[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        __builtin_bit_cast(half4v, u32x2{ar.z, ar.w}), bre, cre[c], 0, 0, 0);
+                    cim[c] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                        __builtin_bit_cast(half4v, u32x2{ai.z, ai.w}), bim, cim[c], 0, 0, 0);
+                }
+                // |K_f| of the pairs whose Re value is in this word (block bk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = 4 * k + e - 34 * bk;
+                    if (o < 2 || o >= 34) continue;  // a scale byte
+                    const int f = 32 * bk + (o - 2);
+                    const float kr = xr[e] * dsc[bk];
+                    const float ki = xi[e] * dsc[bk + NB / 2];
+                    const float mag = __builtin_amdgcn_sqrtf(fmaf(kr, kr, ki * ki));
+#pragma unroll
+                    for (int j = 0; j < GT; ++j) acc[j] = fmaf(WT[z + f * GT + j], mag, acc[j]);
+                }
+                // keep the next words' operand loads from being hoisted above this
+                // word's work (they would hold registers the waves need)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                const float sr = dsc[bk] * OSC[z + j], si = dsc[bk + NB / 2] * OSC[z + j];
+                acc[j] = fmaf(cre[j >> 2][j & 3], sr, acc[j]);
+                acc[j] = fmaf(cim[j >> 2][j & 3], si, acc[j]);
+            }
+        }
+        if (r_out < n) store_scores<GT>(rout + (int64_t)r_out * G, acc, packed);
+        if (part) add_moments<GT>(mom, acc, r_out < n);
+    }
+    if (part) emit_moments<GT>(mom, b.seq[id.seq], id, cv.Hkv, n, G, j0, part);
+}
 
 // ---------------------------------------------------------------------------
 // Matrix-core scorer for fp16 rows (hd % 64 == 0).
@@ -617,8 +786,12 @@ void run_f16(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int 
 template <int HD, int GT>
 void run_q8(dim3 grid, hipStream_t s, const CacheView& cv, const Batch& b, int G, int j0,
             const int32_t* coef, int words, float* raw, PartRec* part) {
-    hipLaunchKernelGGL((score_q8_kernel<HD, GT>), grid, dim3(kScoreThreads), 0, s, cv, b, G, j0,
-                       coef, words, raw, part);
+    if constexpr (HD % 128 == 0)
+        hipLaunchKernelGGL((score_q8_f16_kernel<HD, GT>), grid, dim3(kScoreThreads), 0, s, cv, b, G,
+                           j0, coef, words, raw, part);
+    else
+        hipLaunchKernelGGL((score_q8_kernel<HD, GT>), grid, dim3(kScoreThreads), 0, s, cv, b, G,
+                           j0, coef, words, raw, part);
 }
 
 using Runner = void (*)(dim3, hipStream_t, const CacheView&, const Batch&, int, int,

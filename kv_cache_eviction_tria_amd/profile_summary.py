@@ -3,8 +3,11 @@
   python -m kv_cache_eviction_tria_amd.profile_summary trace DB_DIR  > summary.md
   python -m kv_cache_eviction_tria_amd.profile_summary traffic FETCH_DIR WRITE_DIR \\
          WORKLOAD CAL_BYTES OUT_DIR
+  python -m kv_cache_eviction_tria_amd.profile_summary counters PATTERN DIR [DIR ...]
 
 `trace` lists the average duration of every kernel of a --kernel-trace run.
+`counters` lists, for every kernel whose name contains PATTERN, the mean per
+dispatch of every counter the --pmc runs in the DIRs collected.
 `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)
 into HBM bytes per launch of each eviction-pass kernel, each counter scaled by
 what it reads for the calibration kernel (bench.py --calibrate-bytes: a uint8
@@ -84,6 +87,24 @@ def counter_means(d, counter):
     return acc
 
 
+def counters(pattern, dirs):
+    acc = {}  # kernel -> counter -> (mean, dispatches)
+    for d in dirs:
+        for db in _dbs(d):
+            c = sqlite3.connect(db)
+            for name, cn, v, n in c.execute(
+                    "select kernel_name, counter_name, avg(value), count(*) from "
+                    "counters_collection group by kernel_name, counter_name"):
+                if pattern in name:
+                    acc.setdefault(short(name), {})[cn] = (float(v), int(n))
+    out = []
+    for k, cs in sorted(acc.items()):
+        out.append("%s:" % k)
+        for cn, (v, n) in sorted(cs.items()):
+            out.append("    %-32s %16.1f   (mean of %d dispatches)" % (cn, v, n))
+    return "\n".join(out)
+
+
 def traffic(fetch_dir, write_dir, workload, cal_bytes, out_dir):
     fetch = counter_means(fetch_dir, "FETCH_SIZE")
     write = counter_means(write_dir, "WRITE_SIZE")
@@ -121,6 +142,8 @@ def traffic(fetch_dir, write_dir, workload, cal_bytes, out_dir):
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         print(trace(sys.argv[2]))
+    elif sys.argv[1] == "counters":
+        print(counters(sys.argv[2], sys.argv[3:]))
     elif sys.argv[1] == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6]))
     else:

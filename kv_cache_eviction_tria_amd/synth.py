@@ -158,7 +158,8 @@ def gen_cache(L: int, Hkv: int, hd: int, cap: int, n: int, k_type: int, v_type: 
               device="cpu"):
     """Contiguous cache: K, V uint8 [L, Hkv, cap, row_bytes]; pos int32 [L, Hkv, cap].
 
-    Rows n..cap-1 are zero.  Generated layer by layer to bound temporaries.
+    Rows n..cap-1 are zero.  Generated a layer at a time (all KV heads of the
+    layer at once) to bound temporaries and the number of device launches.
     """
     device = torch.device(device)
     gen = _gen(device, seed * 1000003 + 1)
@@ -168,10 +169,9 @@ def gen_cache(L: int, Hkv: int, hd: int, cap: int, n: int, k_type: int, v_type: 
     ks = torch.exp(0.5 * torch.randn(L, Hkv, 1, hd, generator=gen, device=device))
     vs = torch.exp(0.5 * torch.randn(L, Hkv, 1, hd, generator=gen, device=device))
     for l in range(L):
-        for g in range(Hkv):
-            if n > 0:
-                k[l, g, :n] = encode(gen_values((n,), hd, gen, device, ks[l, g]), k_type)
-                v[l, g, :n] = encode(gen_values((n,), hd, gen, device, vs[l, g]), v_type)
+        if n > 0:
+            k[l, :, :n] = encode(gen_values((Hkv, n), hd, gen, device, ks[l]), k_type)
+            v[l, :, :n] = encode(gen_values((Hkv, n), hd, gen, device, vs[l]), v_type)
     pos = torch.zeros(L, Hkv, cap, dtype=torch.int32, device=device)
     pos[:, :, :n] = torch.arange(n, dtype=torch.int32, device=device)
     return k, v, pos

@@ -105,8 +105,6 @@ def lib():
             L.tria_evict_paged_batch.restype = ctypes.c_int
             L.tria_evict_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32, vp, vp, i64,
                                                  i64, vp, vp]
-            L.tria_set_pipeline.restype = ctypes.c_int
-            L.tria_set_pipeline.argtypes = [vp, i32]
             L.tria_set_keep_mode.restype = ctypes.c_int
             L.tria_set_keep_mode.argtypes = [vp, i32]
             L.tria_set_compaction.restype = ctypes.c_int
@@ -317,11 +315,6 @@ def tria_decode_attention_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, bl
                                                    _stream(stream)),
            "tria_decode_attention_paged_batch")
     return out
-
-
-def tria_set_pipeline(ctx: TriaCtx, layers_per_group: int) -> None:
-    """0: one group (default); > 0: layer groups overlapped on two streams."""
-    _check(lib().tria_set_pipeline(ctx.handle, int(layers_per_group)), "tria_set_pipeline")
 
 
 TRIA_KEEP_PER_UNIT = 0

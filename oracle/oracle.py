@@ -117,6 +117,8 @@ def _load():
             lib.orc_calib_stats.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
             lib.orc_num_threads.restype = i32
             lib.orc_num_threads.argtypes = []
+            lib.orc_last_stage_seconds.restype = None
+            lib.orc_last_stage_seconds.argtypes = [vp]
             _lib = lib
     return _lib
 
@@ -131,6 +133,14 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return _load().orc_num_threads()
+
+
+def last_stage_seconds():
+    """Wall-clock seconds of the last evict() call's stages: (raw scores and per-unit
+    z-normalised maxima, group scores and selection, compaction)."""
+    out = np.zeros(3, np.float64)
+    _load().orc_last_stage_seconds(_p(out))
+    return tuple(float(x) for x in out)
 
 
 def half_to_double(bits: int) -> float:

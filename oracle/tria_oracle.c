@@ -402,6 +402,26 @@ int64_t orc_compact_holefill(uint8_t *rows, int64_t row_bytes, const int32_t *ke
 #define ORC_KEEP_GLOBAL 2
 
 /* Group of unit (l, g) and number of groups under a keep mode. */
+/* Wall-clock seconds of the stages of the last orc_evict_ex call (benchmark
+ * reporting only): [0] raw scores and per-unit z-normalised maxima, [1] group
+ * scores and selection, [2] compaction. */
+static double orc_stage_s[3];
+
+static double orc_now(void)
+{
+#ifdef _OPENMP
+    extern double omp_get_wtime(void);
+    return omp_get_wtime();
+#else
+    return 0.0;
+#endif
+}
+
+void orc_last_stage_seconds(double *out)
+{
+    for (int i = 0; i < 3; i++) out[i] = orc_stage_s[i];
+}
+
 static int orc_n_groups(int mode, int L, int Hkv)
 {
     return mode == ORC_KEEP_UNIT ? L * Hkv : (mode == ORC_KEEP_KV_HEAD ? Hkv : 1);
@@ -444,6 +464,7 @@ int64_t orc_evict_ex(int keep_mode, int compact_mode, int k_type, int v_type, in
     double *ga = (double *)malloc(sizeof(double) * (size_t)(NG * nn)); /* group score */
     int32_t *gk = (int32_t *)malloc(sizeof(int32_t) * (size_t)(NG * nn));
     int failed = !rs || !ua || !ga || !gk;
+    double t0 = orc_now(), t1 = t0, t2 = t0;
     if (!failed && n > 0) {
         /* 1. raw scores and the unit's z-normalised GQA max */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -462,6 +483,7 @@ int64_t orc_evict_ex(int keep_mode, int compact_mode, int k_type, int v_type, in
                 failed = 1;
             }
         }
+        t1 = orc_now();
         /* 2. group score: max over the member units' z-maxima (a unit's value is
          *    -inf exactly when one of its head scores is not finite, and then the
          *    group's is -inf too) */
@@ -488,6 +510,7 @@ int64_t orc_evict_ex(int keep_mode, int compact_mode, int k_type, int v_type, in
                 failed = 1;
             }
         }
+        t2 = orc_now();
         /* 4. every unit gathers its rows with its group's keep set */
 #pragma omp parallel for schedule(dynamic, 1)
         for (int u = 0; u < U; u++) {
@@ -511,6 +534,9 @@ int64_t orc_evict_ex(int keep_mode, int compact_mode, int k_type, int v_type, in
             }
         }
     }
+    orc_stage_s[0] = t1 - t0;
+    orc_stage_s[1] = t2 - t1;
+    orc_stage_s[2] = orc_now() - t2;
     if (!raw) free(rs);
     free(ua);
     free(ga);

@@ -76,21 +76,31 @@ def cutoff(agg_o, n, budget, sink, window):
     return float(cand[order[k - 1]])
 
 
-def check_kept(g_keep, o_keep, agg_o, n, budget, sink, window, where=""):
-    g = set(np.asarray(g_keep).tolist())
-    o = set(np.asarray(o_keep).tolist())
-    assert len(g) == len(o) == len(np.asarray(g_keep)), where + ": kept size differs"
+def check_kept(g_keep, o_keep, agg_o, n, budget, sink, window, where="", stats=None):
+    """Kept sets: same size, strictly ascending; rows in the symmetric difference lie
+    inside the cutoff band.  Returns the number of differing rows.  `stats`, a dict,
+    collects the worst |agg_o - tau| / max(|tau|, 1) over differing rows ("worst_band")
+    and how many of them lie outside the strict band 1e-3 * max(|tau|, 1)
+    ("outside_strict"): the bar's band is twice the score tolerance, and this shows how
+    much of that width was used."""
     gk = np.asarray(g_keep)
+    ok = np.asarray(o_keep)
+    assert len(gk) == len(ok), where + ": kept size differs"
     assert np.all(np.diff(gk) > 0), where + ": kept rows not strictly ascending"
-    diff = g ^ o
-    if not diff:
+    if np.array_equal(gk, ok):
         return 0
+    diff = np.setxor1d(gk, ok, assume_unique=True)
     tau = cutoff(agg_o, n, budget, sink, window)
     assert tau is not None, where + ": kept sets differ with no cutoff band"
-    for r in diff:
-        a = float(agg_o[r])
-        assert abs(a - tau) <= CUT_TOL * max(abs(tau), 1.0), \
-            "%s: row %d (agg %.6g) differs, cutoff %.6g" % (where, r, a, tau)
+    a = np.asarray(agg_o, np.float64)[diff]
+    rel = np.abs(a - tau) / max(abs(tau), 1.0)
+    worst = int(np.argmax(rel))
+    assert rel[worst] <= CUT_TOL, "%s: row %d (agg %.6g) differs, cutoff %.6g" % (
+        where, int(diff[worst]), float(a[worst]), tau)
+    if stats is not None:
+        stats["worst_band"] = max(stats.get("worst_band", 0.0), float(rel[worst]))
+        stats["outside_strict"] = stats.get("outside_strict", 0) + int(np.sum(rel > AGG_TOL))
+        stats["differing"] = stats.get("differing", 0) + len(diff)
     return len(diff)
 
 
@@ -139,13 +149,16 @@ def oracle_pass(wl, stats, k, v, pos, n, budget, sink, window, k_type=None, v_ty
     return out
 
 
-def compare_pass(g, o, n, budget, sink, window, where=""):
+def compare_pass(g, o, n, budget, sink, window, where="", stats=None):
     L, Hkv = g["raw"].shape[0], g["raw"].shape[1]
-    check_raw(g["raw"], o["raw"], where)
-    check_agg(g["agg"], o["agg"], where)
+    wr = check_raw(g["raw"], o["raw"], where)
+    wa = check_agg(g["agg"], o["agg"], where)
+    if stats is not None:
+        stats["worst_raw"] = max(stats.get("worst_raw", 0.0), wr)
+        stats["worst_agg"] = max(stats.get("worst_agg", 0.0), wa)
     nd = 0
     for l in range(L):
         for h in range(Hkv):
             nd += check_kept(g["keep"][l, h], o["keep_idx"][l, h], o["agg"][l, h], n, budget,
-                             sink, window, "%s unit (%d,%d)" % (where, l, h))
+                             sink, window, "%s unit (%d,%d)" % (where, l, h), stats)
     return nd

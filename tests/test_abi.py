@@ -117,3 +117,41 @@ def test_null_arguments_are_rejected(lib):
                                       None) == tria.TRIA_E_INVAL
     lib.tria_free(None)
     assert lib.tria_last_hip_error(None) == 0
+
+
+GATE_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import numpy as np
+from kv_cache_eviction_tria_amd import tria
+L = tria.lib()
+offs = (ctypes.c_int64 * 2)(1, 2)
+stats = np.zeros(4096, np.float32)
+p = stats.ctypes.data_as(ctypes.c_void_p)
+for hd in (100, 96, 128):
+    d = tria.ModelDesc(1, 2, 8, hd, 1, 0, 1e6, 2, offs)
+    h = ctypes.c_void_p()
+    rc = L.tria_load_stats(ctypes.byref(h), ctypes.byref(d), p, p, p, None)
+    print("rc", hd, rc)
+    if h.value:
+        L.tria_free(h)
+"""
+
+
+@pytest.mark.parametrize("env,lines", [("1", 1), ("0", 0), (None, 0)])
+def test_gate_log_is_printed_once_when_asked(lib, env, lines):
+    """TRIA_DEBUG=1: the first model description is reported once on stderr with the
+    gate's decision (the later calls of the process print nothing); otherwise silent."""
+    import subprocess
+    import sys
+    e = dict(os.environ)
+    e.pop("TRIA_DEBUG", None)
+    if env is not None:
+        e["TRIA_DEBUG"] = env
+    r = subprocess.run([sys.executable, "-c", GATE_SCRIPT % ROOT], env=e, capture_output=True,
+                       text=True, timeout=120)
+    assert "rc 100 %d" % tria.TRIA_E_UNSUPPORTED in r.stdout, r.stdout + r.stderr
+    gate = [l for l in r.stderr.splitlines() if l.startswith("tria: gpu gate")]
+    assert len(gate) == lines, r.stderr
+    if lines:
+        assert "hd=100" in gate[0] and "not eligible" in gate[0] and "k=q8_0" in gate[0]

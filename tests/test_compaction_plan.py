@@ -1,58 +1,116 @@
-"""The in-place compaction's ordering rule, checked on the CPU.
+"""The in-place compaction's ordering rule, checked on the CPU, as the GPU kernel
+applies it.
 
-The GPU kernel moves 64-row destination chunks as independent tasks: a task
-loads its sources, publishes, waits for the earlier chunks that read its
-destination rows -- the chunks holding ranks P(64c) .. P(64c+64)-1, with P(x)
-the number of kept rows below x -- and then stores.  Here the same rule drives
-a randomised interleaving of loads and stores over a plain array; every
-interleaving the rule allows must leave the exact gather.  A model with the
-waits removed must fail on the same inputs (the test is not vacuous).
+The kernel moves destination chunks of CR rows (CR = 256, 128 or 64, the widest
+whose pieces fit a workgroup's registers) of every unit as tasks numbered
+chunk * units + unit.  Workgroups take tasks four per ticket from a counter and
+run the tasks of a ticket one after another; a task loads its sources,
+publishes, waits for the earlier chunks of its unit that read its destination
+rows, and then stores.  The readers of chunk c's rows are found from the
+selector's prefix counts P[e] = (kept rows below row 64 e), e = 0 .. nb with
+nb = ceil(kept / 64): ranks P[kPerP c] .. P[min(kPerP c + kPerP, nb)] - 1,
+kPerP = CR / 64, i.e. chunks lo = P[kPerP c] // CR .. hi = min(c - 1,
+(P[...] - 1) // CR).  Here the same rule drives randomised interleavings of
+loads, publishes and stores over plain arrays; every interleaving the rule
+allows must leave the exact gather in every unit, and a model with the waits
+removed must fail on the same inputs (the test is not vacuous).
 """
 import numpy as np
 import pytest
 
-CHUNK = 64
+ROWS64 = 64          # granularity of the prefix counts
+TICKET_TASKS = 4     # tasks taken per ticket
 
 
-def prefix_bounds(keep, n_chunks):
-    """P(64 e) for e = 0 .. n_chunks (number of kept rows below 64 e)."""
-    return np.searchsorted(keep, np.arange(n_chunks + 1) * CHUNK, side="left")
+def prefix_counts(keep):
+    """P[e] for e = 0 .. nb: kept rows below row 64 e (nb = 64-row chunks of kept)."""
+    nb = (len(keep) + ROWS64 - 1) // ROWS64
+    return np.searchsorted(keep, np.arange(nb + 1) * ROWS64, side="left"), nb
 
 
-def simulate(keep, n, rng, respect_waits=True):
-    """Tasks start in chunk order (a persistent grid takes them in order), but a
-    started task's loads complete at any later time, in any order across tasks."""
-    K = len(keep)
-    rows = np.arange(n) * 7 + 1  # distinct row contents
-    mem = rows.copy()
-    nch = (K + CHUNK - 1) // CHUNK
-    P = prefix_bounds(keep, nch)
-    started = 0
-    loaded = [None] * nch  # the values a task read, once its loads completed
-    stored = [False] * nch
-    while not all(stored):
+def wait_range(P, nb, c, cr):
+    """Chunks of cr rows (same unit) that chunk c waits for, as (lo, hi), or None."""
+    per = cr // ROWS64
+    p0, p1 = P[per * c], P[min(per * c + per, nb)]
+    if p1 <= p0:
+        return None
+    return p0 // cr, min(c - 1, (p1 - 1) // cr)
+
+
+def simulate(units, cr, n_workers, rng, respect_waits=True):
+    """units: list of (keep, n).  Workers take TICKET_TASKS consecutive tasks per ticket
+    and run them in order; a task's loads complete at any later time, and the steps of
+    different workers interleave at random."""
+    U = len(units)
+    mems, wants, plans = [], [], []
+    for u, (keep, n) in enumerate(units):
+        rows = np.arange(n) * 7 + 1000 * u + 1  # distinct row contents
+        mems.append(rows.copy())
+        wants.append(rows[keep])
+        P, nb = prefix_counts(keep)
+        plans.append((keep, n, P, nb))
+    max_chunks = max((len(k) + cr - 1) // cr for k, _ in units)
+    n_tasks = max_chunks * U
+    published = set()
+    ticket = 0
+    workers = [[] for _ in range(n_workers)]  # pending tasks of a worker's ticket
+    state = [None] * n_workers  # (task, stage, loaded values)
+    done = 0
+
+    def live(task):
+        c, u = divmod(task, U)
+        keep, n, P, nb = plans[u]
+        K = len(keep)
+        return 0 < K < n and c < (K + cr - 1) // cr
+
+    while True:
         choices = []
-        if started < nch:
-            choices.append(("start", started))
-        for c in range(started):
-            if loaded[c] is None:
-                choices.append(("load", c))
-            elif not stored[c]:
-                lo, hi = P[c] // CHUNK, min(c - 1, (P[c + 1] - 1) // CHUNK)
-                ready = P[c + 1] <= P[c] or all(loaded[cc] is not None for cc in range(lo, hi + 1))
-                if ready or not respect_waits:
-                    choices.append(("store", c))
-        kind, c = choices[rng.integers(len(choices))]
-        if kind == "start":
-            started += 1
-        elif kind == "load":
-            d = np.arange(c * CHUNK, min((c + 1) * CHUNK, K))
-            loaded[c] = (d, mem[keep[d]].copy())  # published once loaded
+        for w in range(n_workers):
+            if state[w] is None:
+                if workers[w]:
+                    choices.append((w, "begin"))
+                elif ticket < n_tasks:
+                    choices.append((w, "ticket"))
+            else:
+                task, stage, _ = state[w]
+                if stage == "issued":
+                    choices.append((w, "arrive"))
+                else:  # published: store once every reader of its rows has loaded
+                    c, u = divmod(task, U)
+                    keep, n, P, nb = plans[u]
+                    rng_ = wait_range(P, nb, c, cr)
+                    ready = rng_ is None or all((cc * U + u) in published
+                                                for cc in range(rng_[0], rng_[1] + 1))
+                    if ready or not respect_waits:
+                        choices.append((w, "store"))
+        if not choices:
+            break
+        w, kind = choices[rng.integers(len(choices))]
+        if kind == "ticket":
+            workers[w] = list(range(ticket, min(ticket + TICKET_TASKS, n_tasks)))
+            ticket += TICKET_TASKS
+        elif kind == "begin":
+            task = workers[w].pop(0)
+            if live(task):
+                state[w] = (task, "issued", None)
+            else:
+                done += 1  # nothing to move in this unit / chunk
+        elif kind == "arrive":
+            task, _, _ = state[w]
+            c, u = divmod(task, U)
+            keep = plans[u][0]
+            d = np.arange(c * cr, min((c + 1) * cr, len(keep)))
+            vals = mems[u][keep[d]].copy()
+            published.add(task)
+            state[w] = (task, "published", (d, vals))
         else:
-            d, vals = loaded[c]
-            mem[d] = vals
-            stored[c] = True
-    return mem[:K], rows[keep]
+            task, _, (d, vals) = state[w]
+            c, u = divmod(task, U)
+            mems[u][d] = vals
+            state[w] = None
+            done += 1
+    assert done == n_tasks
+    return [m[:len(k)] for m, (k, _) in zip(mems, units)], wants
 
 
 def patterns(rng):
@@ -63,35 +121,53 @@ def patterns(rng):
     yield "alternate", np.arange(1, n, 2), n
     yield "head_run", np.concatenate([np.arange(0, 900), np.arange(1000, n, 3)]), n
     yield "dense_gap", np.concatenate([np.arange(0, 64), np.arange(200, n)]), n
+    yield "ragged", np.sort(rng.choice(1777, 1000, replace=False)), 1777
+    yield "keep_all", np.arange(500), 500  # kept == n: no task moves anything
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_rule_gives_the_exact_gather(seed):
-    rng = np.random.default_rng(seed)
-    for name, keep, n in patterns(rng):
-        got, want = simulate(keep, n, rng)
-        assert np.array_equal(got, want), name
+def unit_sets(seed):
+    """Groups of three units with different patterns (and sizes) in one launch."""
+    pats = list(patterns(np.random.default_rng(seed)))
+    for i in range(0, len(pats), 2):
+        trio = [pats[i], pats[(i + 1) % len(pats)], pats[(i + 5) % len(pats)]]
+        yield "+".join(p[0] for p in trio), [(p[1].astype(np.int64), p[2]) for p in trio]
 
 
-def test_without_waits_it_breaks():
+@pytest.mark.parametrize("cr", [64, 128, 256])
+@pytest.mark.parametrize("seed", range(3))
+def test_rule_gives_the_exact_gather(cr, seed):
+    rng = np.random.default_rng(100 + seed)
+    for name, units in unit_sets(seed):
+        got, want = simulate(units, cr, 5, rng)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), (name, cr)
+
+
+@pytest.mark.parametrize("cr", [64, 128, 256])
+def test_without_waits_it_breaks(cr):
     rng = np.random.default_rng(11)
     broken = 0
-    for seed in range(4):
-        for name, keep, n in patterns(np.random.default_rng(seed)):
-            got, want = simulate(keep, n, rng, respect_waits=False)
-            broken += not np.array_equal(got, want)
+    for seed in range(3):
+        for name, units in unit_sets(seed):
+            got, want = simulate(units, cr, 5, rng, respect_waits=False)
+            broken += sum(not np.array_equal(g, w) for g, w in zip(got, want))
     assert broken > 0
 
 
-def test_readers_of_a_chunk_are_earlier_or_itself():
-    """The moves reading rows [64c, 64c+64) have ranks in [P(64c), P(64c+64)); none
-    of them belongs to a later chunk, since sources lie at or above destinations."""
+@pytest.mark.parametrize("cr", [64, 128, 256])
+def test_readers_of_a_chunk_are_earlier_or_itself(cr):
+    """The moves reading the destination rows of chunk c have ranks inside the range
+    the prefix counts give; none of them belongs to a later chunk, since sources lie
+    at or above destinations."""
     rng = np.random.default_rng(5)
     for name, keep, n in patterns(rng):
-        nch = (len(keep) + CHUNK - 1) // CHUNK
-        P = prefix_bounds(keep, nch)
-        for c in range(nch):
-            readers = np.nonzero((keep >= c * CHUNK) & (keep < (c + 1) * CHUNK))[0]
+        K = len(keep)
+        P, nb = prefix_counts(keep)
+        per = cr // ROWS64
+        for c in range((K + cr - 1) // cr):
+            dst_hi = min((c + 1) * cr, K)
+            readers = np.nonzero((keep >= c * cr) & (keep < dst_hi))[0]
             if len(readers):
-                assert readers.min() == P[c] and readers.max() == P[c + 1] - 1, name
-                assert readers.max() // CHUNK <= c, name
+                assert readers.min() >= P[per * c], name
+                assert readers.max() <= P[min(per * c + per, nb)] - 1, name
+                assert readers.max() // cr <= c, name

@@ -74,6 +74,11 @@ SHAPES = [
     (160, 1, 5, Q8, F16, 999, 222, 3, 33),
     (224, 1, 7, F16, Q8, 600, 100, 0, 0),
     (192, 2, 24, Q8, F16, 700, 350, 8, 16),
+    # q8_0 keys on the fp16 matrix-core trig path (hd 128, 256): head sub-groups of
+    # 8, 4, 2 and 1
+    (128, 1, 8, Q8, F16, 1234, 300, 4, 64),
+    (128, 2, 6, Q8, Q8, 900, 250, 0, 100),
+    (256, 1, 3, Q8, F16, 800, 200, 2, 32),
     # fp16 keys on the matrix-core scorer: head chunks of 4 within a launch of up
     # to 16 heads (G 3 and 5 leave partial chunks), and G 20 takes two launches
     (128, 1, 3, F16, F16, 1100, 300, 2, 64),
@@ -176,6 +181,45 @@ def test_f16_magnitudes_past_the_half_range():
     run_case(wl, 600, 150, 4, 32, mutate=big)
 
 
+def _wide_block(case, hd, pair, key_ratio):
+    """One frequency pair's mean query 1e4 times the others of its 32-dim blocks (every
+    query head), and, with key_ratio > 1, keys key_ratio times larger on the other
+    dimensions of those blocks than on the pair's own two dimensions (outlier key
+    channels where the coefficients are small)."""
+    F = hd // 2
+    for x in ("q_re", "q_im", "w"):
+        case[x][:, :, pair] *= 1e4
+    if key_ratio > 1.0:
+        L, Hkv, cap = case["pos"].shape
+        n = case["n"]
+        g = torch.Generator().manual_seed(31)
+        scale = torch.ones(hd)
+        for d0 in ((pair // 32) * 32, F + (pair // 32) * 32):
+            scale[d0:d0 + 32] = key_ratio
+        scale[pair] = 1.0
+        scale[F + pair] = 1.0
+        x = torch.randn(L, Hkv, n, hd, generator=g) * scale
+        k_type = synth.KV_Q8_0 if case["k"].shape[-1] != 2 * hd else synth.KV_F16
+        case["k"][:, :, :n] = synth.encode(x, k_type)
+
+
+@pytest.mark.parametrize("key_ratio", [1.0, 1e3], ids=["big_pair", "big_keys_on_small_pairs"])
+@pytest.mark.parametrize("k_type,hd,Hq", [(Q8, 128, 8), (Q8, 256, 16), (Q8, 96, 6), (Q8, 64, 2),
+                                          (F16, 128, 8)],
+                         ids=["q8_hd128", "q8_hd256", "q8_hd96", "q8_hd64", "f16_hd128"])
+def test_coefficients_across_a_wide_block_range(k_type, hd, Hq, key_ratio):
+    """Trig coefficients 1e4 apart inside one 32-dim block (one pair's mean query much
+    larger than the rest), alone and with the keys large exactly where the coefficients
+    are small: each coefficient must keep its own precision, not the block maximum's,
+    for the raw scores to stay within the bar.  q8_0 at hd 128 and 256 takes the
+    fp16 matrix-core trig path, at hd 96 and 64 the 32-bit integer digits."""
+    wl = variant(WL["tiny_1x1_4k_f16"], name="wide_block", L=2, Hkv=2, Hq=Hq, hd=hd,
+                 k_type=k_type, seed=11)
+    pair = min(40, hd // 2 - 3)
+    run_case(wl, 3000, 900, 4, 128, mutate=lambda c: _wide_block(c, wl.hd, pair, key_ratio),
+             where="wide_block k%d hd%d keys x%g" % (k_type, hd, key_ratio))
+
+
 def test_second_pass_uses_absolute_position():
     """After a compaction the newest row's position exceeds the row count; a second
     pass on the compacted cache plus appended rows must match the oracle."""
@@ -202,16 +246,15 @@ def test_second_pass_uses_absolute_position():
     ctx.close()
 
 
-@pytest.mark.parametrize("L,lpg", [(2, 0), (14, 0), (14, 4), (14, 5)])
-def test_evict_equals_the_three_stages(L, lpg):
-    """tria_evict (one group, or layer groups overlapped on two streams) leaves the
-    same cache as score -> select -> compact run one after the other."""
+@pytest.mark.parametrize("L", [2, 14])
+def test_evict_equals_the_three_stages(L):
+    """tria_evict leaves the same cache as score -> select -> compact run one after
+    the other."""
     wl = variant(WL["qwen3_8b_layer_32k_f16"], name="stages", L=L, Hkv=4, Hq=16, k_type=Q8)
     n, B, S, W = 9000, 2000, 4, 512
     case = synth.make_case(wl, device="cpu", n=n, cap=n + 5)
     stats = (case["q_re"], case["q_im"], case["w"])
     ctx = pu.make_ctx(wl, stats)
-    tria.tria_set_pipeline(ctx, lpg)
     a = [case[x].to(DEV) for x in ("k", "v", "pos")]
     b = [t.clone() for t in a]
     assert tria.tria_evict(ctx, *a, n, B, S, W) == B
@@ -265,9 +308,22 @@ def test_compaction_patterns(pattern):
     ctx.close()
 
 
-def _full_size(wl, sample_units):
-    """Full-size pass in the launch configuration the benchmark times; sampled units are
-    checked against the oracle one by one, the compaction of every unit on the device."""
+def _oracle_layers(wl, stats, k0, p0, l0, nl):
+    """The oracle's scores, aggregates and kept rows for layers [l0, l0 + nl) of a
+    device cache, from host copies of just those layers (bounds host memory)."""
+    kk = pu.host(k0[l0:l0 + nl]).copy()
+    pp = pu.host(p0[l0:l0 + nl]).copy()
+    sl = [x[l0:l0 + nl] for x in stats]
+    vv = np.zeros((1,), np.uint8)  # V is not read without compaction
+    return oracle.evict(wl.k_type, wl.v_type, nl, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                        list(wl.offsets), kk, vv, pp, wl.n, wl.budget, wl.sink, wl.window, *sl,
+                        compact=False)
+
+
+def _full_size(wl, layers_per_check):
+    """Full-size pass in the launch configuration the benchmark times.  Every unit's raw
+    scores, aggregates and kept rows are compared with the oracle's (a few layers at a
+    time), and every unit's compaction is checked as an exact gather on the device."""
     pu.say("full-size case %s" % wl.name)
     stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, wl.seed)
     k, v, pos = synth.gen_cache(wl.L, wl.Hkv, wl.hd, wl.n, wl.n, wl.k_type, wl.v_type, wl.seed,
@@ -294,26 +350,27 @@ def _full_size(wl, sample_units):
     if S:
         assert torch.equal(kl[:, :, :S].cpu(), torch.arange(S).expand(wl.L, wl.Hkv, S))
     assert torch.equal(kl[:, :, K - W:].cpu(), torch.arange(n - W, n).expand(wl.L, wl.Hkv, W))
-    for (l, h) in sample_units:
-        G0 = h * G
-        st = slice(G0, G0 + G)
-        rows = pu.host(k0[l, h, :n])
-        o_raw = oracle.raw_scores_unit(wl.k_type, rows, wl.hd, stats[0][l, st], stats[1][l, st],
-                                       stats[2][l, st], wl.theta, int(p0[l, h, n - 1]),
-                                       list(wl.offsets))
-        o_agg, _, _ = oracle.aggregate_unit(o_raw)
-        o_keep = oracle.select_unit(o_agg, B, S, W)
-        where = "%s unit (%d,%d)" % (wl.name, l, h)
-        pu.check_raw(pu.host(raw[l, h]), o_raw, where)
-        pu.check_agg(pu.host(agg[l, h]), o_agg, where)
-        nd = pu.check_kept(pu.host(keep[l, h]), o_keep, o_agg, n, B, S, W, where)
-        pu.say("  %s ok (%d in band)" % (where, nd))
-    # The whole pass as the benchmark times it (tria_evict: layer groups, selection
-    # and compaction overlapped with scoring on a second stream), several times in
-    # a row: the same cache as the staged calls, and no compaction wait given up.
+    # every unit against the oracle
+    st = {}
+    nd = 0
+    for l0 in range(0, wl.L, layers_per_check):
+        nl = min(layers_per_check, wl.L - l0)
+        o = _oracle_layers(wl, stats, k0, p0, l0, nl)
+        g = dict(raw=pu.host(raw[l0:l0 + nl]), agg=pu.host(agg[l0:l0 + nl]),
+                 keep=pu.host(keep[l0:l0 + nl]))
+        nd += pu.compare_pass(g, o, n, B, S, W, "%s layers %d..%d" % (wl.name, l0, l0 + nl - 1),
+                              st)
+        del o, g
+        pu.say("  layers %d..%d: every unit within the bar" % (l0, l0 + nl - 1))
+    pu.say("  all %d units: worst raw rel err %.3g, worst agg err %.3g of the 1e-3 bound, "
+           "%d kept rows differ (all in the cutoff band, worst %.3g of max(|tau|,1), %d outside "
+           "the strict 1e-3 band)" % (wl.L * wl.Hkv, st.get("worst_raw", 0.0),
+                                      st.get("worst_agg", 0.0), nd, st.get("worst_band", 0.0),
+                                      st.get("outside_strict", 0)))
+    # The whole pass as the benchmark times it (tria_evict), several times in a row:
+    # the same cache as the staged calls, and no compaction wait given up.
     kk, vv, pp = k[:, :, :K].clone(), v[:, :, :K].clone(), pos[:, :, :K].clone()
-    for rep, lpg in enumerate((0, 0, 6, 6)):
-        tria.tria_set_pipeline(ctx, lpg)
+    for rep in range(3):
         k.copy_(k0)
         v.copy_(v0)
         pos.copy_(p0)
@@ -321,20 +378,18 @@ def _full_size(wl, sample_units):
         tria.tria_device_status(ctx)
         assert torch.equal(k[:, :, :K], kk) and torch.equal(v[:, :, :K], vv)
         assert torch.equal(pos[:, :, :K], pp)
-        pu.say("  tria_evict rep %d (layers per group %d) identical" % (rep, lpg))
+        pu.say("  tria_evict rep %d identical" % rep)
     ctx.close()
     del k, v, pos, k0, v0, p0, raw, agg, keep, kk, vv, pp
     torch.cuda.empty_cache()
 
 
 def test_full_qwen3_8b_32k_q8():
-    wl = WL["qwen3_8b_full_32k_q8"]
-    _full_size(wl, [(0, 0), (7, 3), (18, 5), (35, 7), (21, 1)])
+    _full_size(WL["qwen3_8b_full_32k_q8"], 12)
 
 
 def test_full_hd256_48x4_128k():
-    wl = WL["hd256_48x4_128k_f16"]
-    _full_size(wl, [(0, 0), (47, 3), (23, 2)])
+    _full_size(WL["hd256_48x4_128k_f16"], 4)
 
 
 @pytest.mark.parametrize("n,k_type", [(131073, Q8), (tria.TRIA_MAX_ROWS, F16)],
@@ -412,6 +467,113 @@ def test_paged_batch(k_type):
                 pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
                 pu.check_gather(v0[l, h], va[l, h], keep, K, where + " V")
     ctx.close()
+
+
+def _pre_rows_of(post_pos, pre_pos):
+    """Row of the pre-pass cache that holds each position (positions are unique within
+    a unit): [..., K] positions, [..., n] pre-pass positions -> [..., K] rows."""
+    out = np.empty(post_pos.shape, np.int64)
+    for u in np.ndindex(*post_pos.shape[:-1]):
+        order = np.argsort(pre_pos[u], kind="stable")
+        sp = pre_pos[u][order]
+        j = np.searchsorted(sp, post_pos[u])
+        assert np.all(j < len(sp)) and np.array_equal(sp[j], post_pos[u]), \
+            "unit %s holds a position the pass did not start with" % (u,)
+        out[u] = order[j]
+    return out
+
+
+@pytest.mark.parametrize("compaction", ["ordered", "hole_fill"])
+def test_full_paged16_rounds(compaction):
+    """The paged workload at its stated size: 16 sequences of 8K..64K rows (36 layers x
+    8 KV / 32 query heads, hd 128, q8_0 K / fp16 V) in 16-row blocks in shuffled physical
+    order, budget 30 %, window 512, one batched call per pass.  The initial pass and
+    two steady-state rounds of 128 appended rows per sequence are each checked against
+    the oracle sequence by sequence on the logical rows: every unit's kept rows within
+    the cutoff band of the oracle's, and its compacted K, V and positions exactly the
+    rule's rearrangement of the pre-pass rows (the ordered gather, or the hole fill of
+    the GPU's own kept rows)."""
+    wl = WL["paged16_qwen3_8b_q8"]
+    paged_rounds(wl, synth.paged_lengths(wl), compaction, 3, DEV)
+
+
+def paged_rounds(wl, lens, compaction, rounds, dev):
+    """Initial pass plus rounds - 1 steady-state rounds over a paged cache, each checked
+    against the oracle sequence by sequence (see test_full_paged16_rounds)."""
+    budgets = [int(wl.budget_frac * x) for x in lens]
+    S, W, m = wl.sink, wl.window, wl.append
+    L, Hkv = wl.L, wl.Hkv
+    pu.say("case paged16 %s: lengths %s" % (compaction, lens))
+    stats = synth.gen_stats(L, wl.Hq, wl.hd, wl.seed)
+    pg = synth.gen_paged(L, Hkv, wl.hd, wl.k_type, wl.v_type, lens, wl.seed, dev)
+    ctx = pu.make_ctx(wl, stats)
+    if compaction == "hole_fill":
+        tria.tria_set_compaction(ctx, tria.TRIA_COMPACT_HOLE_FILL)
+    names = ("k_pool", "v_pool", "pos_pool")
+    bt = pg["block_table"]
+    li = torch.arange(L, device=dev)[:, None, None]
+    hi = torch.arange(Hkv, device=dev)[None, :, None]
+    vdummy = np.zeros((1,), np.uint8)  # V is not read without compaction
+    n_now = list(lens)
+    st = {}
+    for r in range(rounds):
+        if r > 0:
+            for s in range(len(lens)):
+                row = synth.paged_rows(pg["pos_pool"][:1, :, :1], bt[s], n_now[s])
+                last = int(row[0, 0, n_now[s] - 1])
+                synth.append_paged(pg, s, n_now[s], m, last + 1, L, Hkv, wl.hd, wl.k_type,
+                                   wl.v_type, 4100 + 64 * r + s)
+                n_now[s] += m
+        snap = {x: pg[x].clone() for x in names}
+        torch.cuda.synchronize()
+        pu.say("  round %d: rows %s" % (r, n_now))
+        kept = tria.tria_evict_paged_batch(ctx, pg["k_pool"], pg["v_pool"], pg["pos_pool"], bt,
+                                           n_now, budgets, S, W)
+        tria.tria_device_status(ctx)
+        nd = 0
+        for s in range(len(lens)):
+            n, b = n_now[s], budgets[s]
+            K = oracle.kept_count(n, b, S, W)
+            assert kept[s] == K
+            kh = np.ascontiguousarray(pu.host(synth.paged_rows(snap["k_pool"], bt[s], n)))
+            ph = np.ascontiguousarray(pu.host(synth.paged_rows(snap["pos_pool"], bt[s], n)))
+            o = oracle.evict(wl.k_type, wl.v_type, L, Hkv, wl.Hq, wl.hd, wl.theta,
+                             list(wl.offsets), kh, vdummy, ph, n, b, S, W, *stats,
+                             want_raw=False, compact=False)
+            del kh
+            post = pu.host(synth.paged_rows(pg["pos_pool"], bt[s], n)[:, :, :K])
+            rows = _pre_rows_of(post, ph)
+            gkeep = np.sort(rows, axis=-1)
+            for l in range(L):
+                for h in range(Hkv):
+                    nd += pu.check_kept(gkeep[l, h], o["keep_idx"][l, h], o["agg"][l, h], n, b,
+                                        S, W, "round %d seq %d unit (%d,%d)" % (r, s, l, h), st)
+            if compaction == "ordered":
+                src = gkeep
+                assert np.array_equal(rows, gkeep), "seq %d: kept rows out of order" % s
+            else:
+                ids = np.arange(n, dtype=np.int32)
+                src = np.empty_like(gkeep)
+                for l in range(L):
+                    for h in range(Hkv):
+                        src[l, h] = oracle.compact_holefill(ids, gkeep[l, h], n)[0][:K]
+            src_t = torch.from_numpy(src).to(dev)
+            for x in names:
+                pre = synth.paged_rows(snap[x], bt[s], n)
+                now = synth.paged_rows(pg[x], bt[s], n)[:, :, :K]
+                assert torch.equal(now, pre[li, hi, src_t]), \
+                    "round %d seq %d: %s is not the rule's rearrangement" % (r, s, x)
+            del o, post, rows, gkeep, src, src_t
+            n_now[s] = K
+        del snap
+        torch.cuda.empty_cache()
+        pu.say("  round %d: all %d units of %d sequences within the bar; %d kept rows differ "
+               "(in the cutoff band, worst %.3g of max(|tau|,1), %d outside the strict 1e-3 "
+               "band)" % (r, L * Hkv * len(lens), len(lens), nd, st.get("worst_band", 0.0),
+                          st.get("outside_strict", 0)))
+    ctx.close()
+    del pg
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
