@@ -185,6 +185,25 @@ int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
 int64_t tria_evict(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, int64_t budget,
                    int64_t sink, int64_t window, hipStream_t stream);
 
+/* tria_evict for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same pass with the
+ * same results, whose scratch (coefficient tables, raw scores, moment
+ * partials, kept indices, chunk prefix counts, compaction flags and task
+ * counter) lives in one fixed array of TRIA_NOALLOC_SCRATCH_BYTES per GPU in
+ * the library's code object, held until the process ends.  The call makes no
+ * hipMalloc, hipFree or hipMemset; its address is looked up once per device
+ * (in tria_load_stats, or on the first call on a device).  Layers are processed
+ * in as few groups as the array holds (one layer of a 36 x 8 x 32K q8_0 cache
+ * needs about 4.5 MiB).  Returns the kept count, or TRIA_E_UNSUPPORTED before
+ * anything is enqueued if one layer does not fit, or if a shared keep mode is
+ * set (tria_set_keep_mode); otherwise the errors of tria_evict.  Every call on
+ * a GPU uses that GPU's one array: calls that overlap on one GPU (concurrent
+ * streams, several threads) race and give wrong results; a call must finish on
+ * the GPU before the next one starts, which calls on one stream do. */
+#define TRIA_NOALLOC_SCRATCH_BYTES 67108864 /* 64 MiB */
+int64_t tria_evict_noalloc(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
+                           int64_t budget, int64_t sink, int64_t window, hipStream_t stream);
+
 /* The same pass over n_seq sequences of a paged cache, one launch per kernel
  * for all sequences.  n_tokens, budget: host [n_seq]; kept_out: host [n_seq],
  * written with each sequence's kept count.  Each sequence's rows beyond its

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include "tria_group.h"
@@ -410,9 +411,143 @@ void log_gate_once(const tria_model_desc* d, const char* why) {
             why ? "not eligible: " : "eligible", why ? why : "");
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of tria_evict_noalloc: one fixed array per GPU, in the library's code
+// object, so that the call itself allocates nothing.  Layout:
+//   [0, kNaFlagBytes)                compaction flags (only ever written with
+//                                    compaction epochs, so a stale word never
+//                                    equals a later epoch)
+//   [kNaFlagBytes, + 256)            the compaction's task counter
+//   [kNaDataOff, kNoAllocScratchBytes) coefficient tables of every unit, then
+//                                    one group of layers' raw scores, moment
+//                                    partials, kept indices, chunk prefix
+//                                    counts and (above 128K rows) selector keys
+constexpr size_t kNaFlagBytes = (size_t)1 << 20;
+constexpr size_t kNaDataOff = kNaFlagBytes + 256;
+constexpr int kNaMaxDevices = 64;
+
+struct NoAllocDevice {
+    uint8_t* ptr = nullptr;  // device address of `scratch` on this GPU
+    uint32_t epoch = 0;      // last compaction epoch stamped into its flags
+};
+std::mutex g_na_mu;
+NoAllocDevice g_na[kNaMaxDevices];
+
+}  // namespace
+
+// In host code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device is ever used.
+static __device__ __align__(256) uint8_t scratch[TRIA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's scratch address, looked up once per device (with that
+// device current).  TRIA_E_HIP if the lookup fails.
+int noalloc_device(tria_ctx* ctx, int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    if (dev < 0 || dev >= kNaMaxDevices) return TRIA_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_na_mu);
+    if (!g_na[dev].ptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(ctx, e != hipSuccess ? e : hipErrorUnknown);
+        g_na[dev].ptr = static_cast<uint8_t*>(p);
+    }
+    *dev_out = dev;
+    return TRIA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bytes one layer of a pass needs in the data region (per-layer buffers).
+struct NaLayer {
+    size_t raw, part, keep, pb, keys;
+    int64_t flag_words;
+    size_t total() const { return raw + part + keep + pb + keys; }
+};
+
+NaLayer noalloc_layer(const tria_ctx* ctx, int64_t n, int64_t kept) {
+    NaLayer x;
+    const int64_t H = ctx->Hkv, G = ctx->G;
+    x.raw = align256((size_t)(H * n * G) * sizeof(float));
+    x.part = align256((size_t)(H * part_tiles(n) * G) * sizeof(PartRec));
+    x.keep = align256((size_t)(H * kept) * sizeof(int32_t));
+    x.pb = align256((size_t)(H * chunk_bounds(kept)) * sizeof(int32_t));
+    x.keys = n > (int64_t)128 * 1024 ? align256((size_t)(H * n) * sizeof(uint32_t)) : 0;
+    x.flag_words = H * chunk_count(kept);
+    return x;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t tria_evict_noalloc(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens,
+                           int64_t budget, int64_t sink, int64_t window, hipStream_t stream) {
+    if (!ctx) return TRIA_E_INVAL;
+    int rc = check_cache(cache, n_tokens);
+    if (rc) return rc;
+    if (budget < 0 || sink < 0 || window < 0) return TRIA_E_INVAL;
+    const Protect p = protect(n_tokens, budget, sink, window);
+    if (p.kept == n_tokens) return n_tokens;  // nothing to evict: no work, no writes
+    if (ctx->keep_mode != TRIA_KEEP_PER_UNIT) return TRIA_E_UNSUPPORTED;
+    // layers per group: as many as the data region holds (at least one)
+    const CoefGeom cg = coef_geom(ctx->k_type, ctx->hd, ctx->G);
+    const size_t coef_bytes = align256((size_t)ctx->L * ctx->Hkv * cg.words * 4);
+    const NaLayer per = noalloc_layer(ctx, n_tokens, p.kept);
+    const size_t room = TRIA_NOALLOC_SCRATCH_BYTES - kNaDataOff;
+    if (coef_bytes + per.total() > room || per.flag_words > (int64_t)(kNaFlagBytes / 4))
+        return TRIA_E_UNSUPPORTED;
+    int lg = (int)((room - coef_bytes) / per.total());
+    const int lf = (int)((int64_t)(kNaFlagBytes / 4) / (per.flag_words > 0 ? per.flag_words : 1));
+    lg = lg < lf ? lg : lf;
+    lg = lg < ctx->L ? lg : ctx->L;
+    int dev = 0;
+    rc = noalloc_device(ctx, &dev);
+    if (rc) return rc;
+
+    uint8_t* base = g_na[dev].ptr;
+    uint32_t* flags = reinterpret_cast<uint32_t*>(base);
+    uint32_t* ticket = reinterpret_cast<uint32_t*>(base + kNaFlagBytes);
+    int32_t* coef = reinterpret_cast<int32_t*>(base + kNaDataOff);
+    uint8_t* grp = base + kNaDataOff + coef_bytes;
+    float* raw = reinterpret_cast<float*>(grp);
+    PartRec* part = reinterpret_cast<PartRec*>(grp + (size_t)lg * per.raw);
+    int32_t* keep = reinterpret_cast<int32_t*>(grp + (size_t)lg * (per.raw + per.part));
+    int32_t* pb = reinterpret_cast<int32_t*>(grp + (size_t)lg * (per.raw + per.part + per.keep));
+    uint32_t* keys = per.keys ? reinterpret_cast<uint32_t*>(
+                                    grp + (size_t)lg * (per.raw + per.part + per.keep + per.pb))
+                              : nullptr;
+
+    const CacheView cv = view_of(ctx, cache);
+    Batch b = one_seq(n_tokens, p);
+    const int units = ctx->L * ctx->Hkv;
+    hipError_t e = launch_prep(cv, b, units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
+                               ctx->w, ctx->omega, ctx->m_re, ctx->m_im, coef, stream);
+    std::lock_guard<std::mutex> lk(g_na_mu);  // the device's epoch counter
+    CompactState cs = {flags, (int64_t)(kNaFlagBytes / 4), g_na[dev].epoch, ticket, ctx->cst.err};
+    for (int l0 = 0; l0 < ctx->L && e == hipSuccess; l0 += lg) {
+        const int lc = ctx->L - l0 < lg ? ctx->L - l0 : lg;
+        const CacheView sv = sub_view(cv, l0, lc);
+        Batch gb = b;  // this group's buffers start at offset 0
+        gb.coef_L = ctx->L;
+        gb.coef_l0 = l0;
+        const int gu = lc * ctx->Hkv;
+        e = launch_score(sv, gb, gu, ctx->k_type, ctx->G, ctx->hd, coef, raw, part, stream);
+        if (e == hipSuccess)
+            e = launch_select_impl(gb, gu, ctx->G, raw, part, keep, nullptr, keys, pb, ticket,
+                                   stream);
+        if (e == hipSuccess && ctx->compact_mode == TRIA_COMPACT_HOLE_FILL)
+            e = launch_holefill(sv, gb, gu, keep, stream);
+        else if (e == hipSuccess)
+            e = launch_compact(sv, gb, gu, keep, pb, nullptr, cs, ticket, stream);
+    }
+    g_na[dev].epoch = cs.epoch;
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return p.kept;
+}
 
 int tria_decode_attention(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, const float* q,
                           float scale, float* out, hipStream_t stream) {
@@ -569,6 +704,13 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
     if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, sizeof(uint32_t));
     if (e != hipSuccess) {
         const int rc = e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
+        tria_free(ctx);
+        return rc;
+    }
+    // the current device's tria_evict_noalloc scratch address, looked up once
+    int dev = 0;
+    const int rc = noalloc_device(ctx, &dev);
+    if (rc) {
         tria_free(ctx);
         return rc;
     }

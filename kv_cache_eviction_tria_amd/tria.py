@@ -102,6 +102,8 @@ def lib():
             L.tria_compact.argtypes = [vp, ctypes.POINTER(Cache), i64, vp, i64, vp]
             L.tria_evict.restype = i64
             L.tria_evict.argtypes = [vp, ctypes.POINTER(Cache), i64, i64, i64, i64, vp]
+            L.tria_evict_noalloc.restype = i64
+            L.tria_evict_noalloc.argtypes = [vp, ctypes.POINTER(Cache), i64, i64, i64, i64, vp]
             L.tria_evict_paged_batch.restype = ctypes.c_int
             L.tria_evict_paged_batch.argtypes = [vp, ctypes.POINTER(PagedCache), i32, vp, vp, i64,
                                                  i64, vp, vp]
@@ -262,6 +264,18 @@ def tria_evict(ctx: TriaCtx, k, v, pos, n_tokens: int, budget: int, sink: int, w
     c = _cache(k, v, pos)
     return int(_check(lib().tria_evict(ctx.handle, ctypes.byref(c), n_tokens, budget, sink,
                                        window, _stream(stream)), "tria_evict"))
+
+
+def tria_evict_noalloc(ctx: TriaCtx, k, v, pos, n_tokens: int, budget: int, sink: int,
+                       window: int, stream=None) -> int:
+    """tria_evict with the library's fixed per-GPU scratch (no allocation in the call)."""
+    c = _cache(k, v, pos)
+    return int(_check(lib().tria_evict_noalloc(ctx.handle, ctypes.byref(c), n_tokens, budget,
+                                               sink, window, _stream(stream)),
+                      "tria_evict_noalloc"))
+
+
+TRIA_NOALLOC_SCRATCH_BYTES = 67108864  # 64 MiB
 
 
 def tria_evict_paged_batch(ctx: TriaCtx, k_pool, v_pool, pos_pool, block_table, n_tokens,
