@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work the oracle baseline aims for (whole passes, at least one)")
     ap.add_argument("--staged-steps", type=int, default=5)
+    ap.add_argument("--seq-rounds", type=int, default=-1,
+                    help="paged workload: rounds of per-sequence passes after the batched "
+                         "rounds (default: as many as --steps; 0: none)")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="between steps, read (default) or write 512 MB to evict the Infinity "
                          "Cache, or leave it as the restore left it")
@@ -419,6 +422,36 @@ def bench_paged(args, wl):
             moved_total += sum(int((a != b_).sum().item()) for a, b_ in zip(after, before))
     tria.tria_timing_enable(ctx, False)
     tria.tria_device_status(ctx)  # raises if a compaction gave up a wait
+
+    # Per-sequence passes: after its 128 appends each sequence is evicted on its own (a
+    # one-sequence batch), as a loop serving the sequences one at a time would; the
+    # steady-state pass latency per sequence, timed like the rounds.
+    seq_rounds = args.steps if args.seq_rounds < 0 else args.seq_rounds
+    log("per-sequence rounds: %d" % seq_rounds)
+    t_seq = [[] for _ in range(wl.n_seq)]
+    for r in range(seq_rounds):
+        append(total + r)
+        for s in range(wl.n_seq):
+            bt_s = pg["block_table"][s:s + 1]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            k_s = tria.tria_evict_paged_batch(ctx, pg["k_pool"], pg["v_pool"], pg["pos_pool"],
+                                              bt_s, [n_now[s]], [budgets[s]], wl.sink,
+                                              wl.window, stream)
+            torch.cuda.synchronize()
+            t_seq[s].append((time.perf_counter() - t0) * 1e3)
+            assert k_s == [budgets[s]]
+            n_now[s] = budgets[s]
+    tria.tria_device_status(ctx)
+    seq_all = [t for ts in t_seq for t in ts] or [float("nan")]
+    seq_rows = [wl.L * wl.Hkv * (b + m) for b in budgets]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_paged(wl, stats, pg, n_now, budgets, m, args.cpu_seconds,
+                                 KEEP_MODES[args.keep_mode][1], COMPACTIONS[args.compaction][1],
+                                 total + seq_rounds)
+
     ms = float(np.median(t_round))
     rows = sum(wl.L * wl.Hkv * (b + m) for b in budgets)
     per_step_ms = {s: st_ms[s] / args.steps for s in tria.STAGES}
@@ -460,10 +493,60 @@ def bench_paged(args, wl):
                              tkey(dom)),
         "roofline_all": {s: roofline(s, per_step_ms[s], per_step_n[s], alg[s], wl.name, tkey(s))
                          for s in tria.STAGES},
-        "cpu_baseline": None,
+        "seq_pass_ms_median": float(np.median(seq_all)),
+        "seq_pass_ms_p10_p90": [float(np.percentile(seq_all, 10)),
+                                float(np.percentile(seq_all, 90))],
+        "seq_pass_ms_by_sequence": [float(np.median(ts)) if ts else None for ts in t_seq],
+        "seq_pass_rows_per_s": float(np.median([r_ / (np.median(ts) * 1e-3)
+                                                for r_, ts in zip(seq_rows, t_seq)]))
+        if seq_rounds else None,
+        "seq_pass_timing": "each sequence's own pass (n = budget + 128 -> budget), "
+                           "%d rounds after the batched ones; host clock, device synchronised "
+                           "on both sides, enqueue included" % seq_rounds,
+        "cpu_baseline": cpu,
     }
     ctx.close()
     return out
+
+
+def cpu_baseline_paged(wl, stats, pg, n_now, budgets, m, seconds, keep_mode, compact_mode,
+                       round0):
+    """The oracle on sequence passes of the same steady state: sequence by sequence, 128
+    rows are appended on the device, the logical rows (n = budget + 128) are copied to
+    the host and the oracle runs the whole pass on them; until about `seconds`."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_eviction_tria_amd import synth
+    log("cpu baseline: oracle on sequence passes, about %.0f s" % seconds)
+    times, stages, rows, done = [], [], 0, []
+    for s in range(wl.n_seq):
+        if times and sum(times) >= seconds:
+            break
+        n = n_now[s]
+        row = synth.paged_rows(pg["pos_pool"][:1, :, :1], pg["block_table"][s], n)
+        synth.append_paged(pg, s, n, m, int(row[0, 0, n - 1]) + 1, wl.L, wl.Hkv, wl.hd,
+                           wl.k_type, wl.v_type, wl.seed * 100003 + round0 * 64 + s)
+        n += m
+        host = [np.ascontiguousarray(synth.paged_rows(pg[x], pg["block_table"][s], n).cpu()
+                                     .numpy()) for x in ("k_pool", "v_pool", "pos_pool")]
+        t = time.perf_counter()
+        oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                     list(wl.offsets), *host, n, budgets[s], wl.sink, wl.window, *stats,
+                     want_raw=False, want_agg=False, keep_mode=keep_mode,
+                     compact_mode=compact_mode)
+        times.append(time.perf_counter() - t)
+        stages.append(oracle.last_stage_seconds())
+        rows += wl.L * wl.Hkv * n
+        done.append(s)
+    st = np.median(np.array(stages), axis=0) * 1e3
+    return {"value": rows / sum(times), "unit": UNIT, "cores": oracle.num_threads(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "seq_pass_ms_median": float(np.median(times)) * 1e3,
+            "stage_ms_median": {"score_and_aggregate": float(st[0]), "select": float(st[1]),
+                                "compact": float(st[2])},
+            "sample": "%d sequence passes (sequences %s, n = budget + %d each), %.1f s of CPU "
+                      "time" % (len(times), done, m, sum(times))}
 
 
 def bench_decode(args, wl):

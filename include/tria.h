@@ -260,6 +260,14 @@ int tria_set_keep_mode(tria_ctx *ctx, int32_t mode);
  * Returns TRIA_OK, or TRIA_E_INVAL for another mode. */
 #define TRIA_COMPACT_ORDERED 0
 #define TRIA_COMPACT_HOLE_FILL 1
+
+/* Cap on the workgroups of the order-preserving compaction (tria_compact,
+ * tria_evict and its variants).  0 (the default): as many as the GPU holds at
+ * once.  1: one workgroup takes every chunk task in order, so no task ever
+ * waits for another: the serial reference against which the parallel in-place
+ * rule is compared bit for bit.  Results do not depend on the cap.  Returns
+ * TRIA_OK or TRIA_E_INVAL for a negative value. */
+int tria_set_compaction_workgroups(tria_ctx *ctx, int32_t max_workgroups);
 int tria_set_compaction(tria_ctx *ctx, int32_t mode);
 
 /* ------------------------------------------------------------------------

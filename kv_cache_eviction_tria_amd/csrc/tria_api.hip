@@ -56,7 +56,7 @@ struct tria_ctx {
     size_t part_bytes = 0;
     int32_t* pb = nullptr;  // chunk prefix counts (selector -> compaction)
     size_t pb_bytes = 0;
-    CompactState cst = {nullptr, 0, 0, nullptr, nullptr};
+    CompactState cst = {nullptr, 0, 0, nullptr, nullptr, 0};
     size_t flag_bytes = 0;
     // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
     int keep_mode = TRIA_KEEP_PER_UNIT;
@@ -527,7 +527,8 @@ int64_t tria_evict_noalloc(tria_ctx* ctx, const tria_cache* cache, int64_t n_tok
     hipError_t e = launch_prep(cv, b, units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
                                ctx->w, ctx->omega, ctx->m_re, ctx->m_im, coef, stream);
     std::lock_guard<std::mutex> lk(g_na_mu);  // the device's epoch counter
-    CompactState cs = {flags, (int64_t)(kNaFlagBytes / 4), g_na[dev].epoch, ticket, ctx->cst.err};
+    CompactState cs = {flags, (int64_t)(kNaFlagBytes / 4), g_na[dev].epoch, ticket, ctx->cst.err,
+                       ctx->cst.max_groups};
     for (int l0 = 0; l0 < ctx->L && e == hipSuccess; l0 += lg) {
         const int lc = ctx->L - l0 < lg ? ctx->L - l0 : lg;
         const CacheView sv = sub_view(cv, l0, lc);
@@ -845,6 +846,12 @@ int tria_set_compaction(tria_ctx* ctx, int32_t mode) {
     if (!ctx) return TRIA_E_INVAL;
     if (mode != TRIA_COMPACT_ORDERED && mode != TRIA_COMPACT_HOLE_FILL) return TRIA_E_INVAL;
     ctx->compact_mode = mode;
+    return TRIA_OK;
+}
+
+int tria_set_compaction_workgroups(tria_ctx* ctx, int32_t max_workgroups) {
+    if (!ctx || max_workgroups < 0) return TRIA_E_INVAL;
+    ctx->cst.max_groups = max_workgroups;
     return TRIA_OK;
 }
 

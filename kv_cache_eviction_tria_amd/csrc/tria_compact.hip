@@ -349,9 +349,10 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
     }
     const int64_t tasks = chunks * n_units;
     if (tasks >= (int64_t)1 << 31) return hipErrorInvalidValue;
-    // as many workgroups as fit at once; residency is not required
+    // as many workgroups as fit at once (residency is not required), or the cap
     int grid = resident_groups(k, threads);
     if (grid <= 0) return hipErrorInvalidValue;
+    if (st.max_groups > 0 && st.max_groups < grid) grid = st.max_groups;
     const int64_t need = (tasks + kTicketTasks - 1) / kTicketTasks;
     if (need < grid) grid = (int)need;
     st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value

@@ -286,8 +286,9 @@ struct CompactState {
     uint32_t* flags;
     int64_t flag_words;
     uint32_t epoch;
-    uint32_t* ticket;  // task counters (one per layer group), reset by the selector
+    uint32_t* ticket;  // task counter, reset by the kernel before the compaction
     int* err;
+    int max_groups;    // > 0: at most this many workgroups (1: every task in order)
 };
 // pb: the selector's chunk prefix counts for these units, or nullptr to
 // derive them from keep (caller-provided kept indices).

@@ -6,6 +6,8 @@
   python -m kv_cache_eviction_tria_amd.profile_summary counters PATTERN DIR [DIR ...]
 
 `trace` lists the average duration of every kernel of a --kernel-trace run.
+`--skip-first N` (any mode) leaves out each library kernel's first N dispatches,
+e.g. the initial pass of the paged workload, whose rounds are what is measured.
 `counters` lists, for every kernel whose name contains PATTERN, the mean per
 dispatch of every counter the --pmc runs in the DIRs collected.
 `traffic` turns two --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)
@@ -52,16 +54,26 @@ def short(name):
     return n.split("(")[0]
 
 
-def trace(d):
+def _columns(c, table):
+    return [r[1] for r in c.execute("pragma table_info(%s)" % table)]
+
+
+def trace(d, skip=0):
+    """skip: leave out each kernel's first `skip` dispatches (e.g. a one-off first pass)."""
     rows = {}
     for db in _dbs(d):
         c = sqlite3.connect(db)
-        for name, n, avg, tot in c.execute(
-                "select name, count(*), avg(duration), sum(duration) from kernels group by name"):
+        cols = _columns(c, "kernels")
+        order = "start" if "start" in cols else "rowid"
+        seen = {}
+        for name, dur in c.execute("select name, duration from kernels order by %s" % order):
             k = short(name)
+            seen[k] = seen.get(k, 0) + 1
+            if k.startswith("tria::") and seen[k] <= skip:
+                continue
             a = rows.setdefault(k, [0, 0.0])
-            a[0] += n
-            a[1] += tot
+            a[0] += 1
+            a[1] += dur
     out = ["| kernel | calls | avg us | total us |", "|---|---|---|---|"]
     other = [0, 0.0]
     for k, (n, tot) in sorted(rows.items(), key=lambda x: -x[1][1]):
@@ -75,15 +87,24 @@ def trace(d):
     return "\n".join(out)
 
 
-def counter_means(d, counter):
-    """full kernel name -> (mean counter value per dispatch, dispatches)."""
-    acc = {}
+def counter_means(d, counter, skip=0):
+    """full kernel name -> (mean counter value per dispatch, dispatches), leaving out each
+    library kernel's first `skip` dispatches."""
+    vals = {}
     for db in _dbs(d):
         c = sqlite3.connect(db)
-        for name, v, n in c.execute(
-                "select kernel_name, avg(value), count(*) from counters_collection "
-                "where counter_name = ? group by kernel_name", (counter,)):
-            acc[name] = (float(v), int(n))
+        cols = _columns(c, "counters_collection")
+        order = "dispatch_id" if "dispatch_id" in cols else "rowid"
+        for name, v in c.execute(
+                "select kernel_name, value from counters_collection where counter_name = ? "
+                "order by %s" % order, (counter,)):
+            vals.setdefault(name, []).append(float(v))
+    acc = {}
+    for name, vs in vals.items():
+        if "tria::" in name:
+            vs = vs[skip:]
+        if vs:
+            acc[name] = (sum(vs) / len(vs), len(vs))
     return acc
 
 
@@ -105,9 +126,9 @@ def counters(pattern, dirs):
     return "\n".join(out)
 
 
-def traffic(fetch_dir, write_dir, workload, cal_bytes, out_dir):
-    fetch = counter_means(fetch_dir, "FETCH_SIZE")
-    write = counter_means(write_dir, "WRITE_SIZE")
+def traffic(fetch_dir, write_dir, workload, cal_bytes, out_dir, skip=0):
+    fetch = counter_means(fetch_dir, "FETCH_SIZE", skip)
+    write = counter_means(write_dir, "WRITE_SIZE", skip)
     cal_f = [v for k, (v, n) in fetch.items() if CAL_KERNEL in k]
     cal_w = [v for k, (v, n) in write.items() if CAL_KERNEL in k]
     if not cal_f or not cal_w:
@@ -140,11 +161,16 @@ def traffic(fetch_dir, write_dir, workload, cal_bytes, out_dir):
 
 
 if __name__ == "__main__":
+    skip = 0
+    if "--skip-first" in sys.argv:
+        i = sys.argv.index("--skip-first")
+        skip = int(sys.argv[i + 1])
+        del sys.argv[i:i + 2]
     if sys.argv[1] == "trace":
-        print(trace(sys.argv[2]))
+        print(trace(sys.argv[2], skip))
     elif sys.argv[1] == "counters":
         print(counters(sys.argv[2], sys.argv[3:]))
     elif sys.argv[1] == "traffic":
-        print(traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6]))
+        print(traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], skip))
     else:
         raise SystemExit(__doc__)

@@ -109,6 +109,8 @@ def lib():
                                                  i64, vp, vp]
             L.tria_set_keep_mode.restype = ctypes.c_int
             L.tria_set_keep_mode.argtypes = [vp, i32]
+            L.tria_set_compaction_workgroups.restype = ctypes.c_int
+            L.tria_set_compaction_workgroups.argtypes = [vp, i32]
             L.tria_set_compaction.restype = ctypes.c_int
             L.tria_set_compaction.argtypes = [vp, i32]
             L.tria_decode_attention.restype = ctypes.c_int
@@ -424,6 +426,12 @@ class TriaCalib:
 def tria_set_compaction(ctx: TriaCtx, mode: int) -> None:
     """TRIA_COMPACT_ORDERED (default gather) or TRIA_COMPACT_HOLE_FILL (variant)."""
     _check(lib().tria_set_compaction(ctx.handle, int(mode)), "tria_set_compaction")
+
+
+def tria_set_compaction_workgroups(ctx: TriaCtx, max_workgroups: int) -> None:
+    """0: as many compaction workgroups as fit (default); 1: one, every task in order."""
+    _check(lib().tria_set_compaction_workgroups(ctx.handle, int(max_workgroups)),
+           "tria_set_compaction_workgroups")
 
 
 def tria_device_status(ctx: TriaCtx) -> None:

@@ -76,6 +76,13 @@ def test_contiguous_entry_points_reject_bad_arguments():
         "attention null q": (lambda: L.tria_decode_attention(h, ctypes.byref(good), n, None,
                                                               ctypes.c_float(0.1), _p(out), s),
                              INVAL),
+        "noalloc n > cap": (lambda: L.tria_evict_noalloc(h, ctypes.byref(good), n + 1, 100, 4, 16,
+                                                          s), INVAL),
+        "noalloc budget < 0": (lambda: L.tria_evict_noalloc(h, ctypes.byref(good), n, -1, 4, 16,
+                                                             s), INVAL),
+        "compaction workgroups < 0": (lambda: L.tria_set_compaction_workgroups(h, -1), INVAL),
+        "compaction mode 7": (lambda: L.tria_set_compaction(h, 7), INVAL),
+        "keep mode 9": (lambda: L.tria_set_keep_mode(h, 9), INVAL),
     }
     for name, (call, code) in cases.items():
         pu.say("case %s" % name)

@@ -308,6 +308,46 @@ def test_compaction_patterns(pattern):
     ctx.close()
 
 
+@pytest.mark.parametrize("pattern", ["selected", "alternate", "tail", "random"])
+def test_serial_compaction_reference(pattern):
+    """The ordered compaction run by one workgroup (every chunk task in order, so no
+    task waits for another) and by the full grid leave byte-identical caches: the
+    forced serial path as the reference of the parallel in-place rule, on a 4 x 8 x 32K
+    q8_0 cache with the selector's kept rows and with adversarial patterns."""
+    wl = variant(WL["qwen3_8b_full_32k_q8"], name="serial", L=4)
+    n, B, S, W = wl.n, wl.budget, wl.sink, wl.window
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 21)
+    a = list(synth.gen_cache(wl.L, wl.Hkv, wl.hd, n, n, wl.k_type, wl.v_type, 21, DEV))
+    b = [t.clone() for t in a]
+    ctx = pu.make_ctx(wl, stats)
+    pu.say("case serial compaction %s" % pattern)
+    if pattern == "selected":
+        tria.tria_set_compaction_workgroups(ctx, 1)
+        Ka = tria.tria_evict(ctx, *a, n, B, S, W)
+        tria.tria_set_compaction_workgroups(ctx, 0)
+        Kb = tria.tria_evict(ctx, *b, n, B, S, W)
+    else:
+        rng = np.random.default_rng(5)
+        if pattern == "alternate":
+            keep1 = np.arange(1, n, 2)
+        elif pattern == "tail":
+            keep1 = np.arange(n - 3000, n)
+        else:
+            keep1 = np.sort(rng.choice(n, size=10000, replace=False))
+        Ka = Kb = len(keep1)
+        keep = torch.from_numpy(np.broadcast_to(keep1.astype(np.int32),
+                                                (wl.L, wl.Hkv, Ka)).copy()).to(DEV)
+        tria.tria_set_compaction_workgroups(ctx, 1)
+        tria.tria_compact(ctx, *a, n, keep, Ka)
+        tria.tria_set_compaction_workgroups(ctx, 0)
+        tria.tria_compact(ctx, *b, n, keep, Kb)
+    tria.tria_device_status(ctx)
+    assert Ka == Kb
+    for x, y, name in zip(a, b, ("k", "v", "pos")):
+        assert torch.equal(x[:, :, :Ka], y[:, :, :Ka]), name
+    ctx.close()
+
+
 def _oracle_layers(wl, stats, k0, p0, l0, nl):
     """The oracle's scores, aggregates and kept rows for layers [l0, l0 + nl) of a
     device cache, from host copies of just those layers (bounds host memory)."""
