@@ -15,7 +15,10 @@
 //      a finite score;
 //   2. one read of the raw scores, with the row's G scores in vector loads
 //      and eight rows per thread in flight: agg(r) = max_h (s_h - mu_h) /
-//      sigma_h (fp64, rounded once to fp32; -inf if any score is not finite),
+//      sigma_h in fp32 as ((s_h - mu_hi) - mu_lo) * (1/sigma_h), with mu_h held
+//      as a two-float sum and 1/sigma_h rounded once from fp64, so the head's
+//      common offset is removed before any rounding of the deviation (-inf if
+//      any score is not finite),
 //      mapped to an order-preserving 32-bit key (-0 folded into +0), and
 //      counted into a 2048-bin histogram that is linear in agg over [-8, 8)
 //      (clamped at both ends; the bin is a monotone function of the key);
