@@ -43,7 +43,7 @@ namespace tria {
 namespace {
 
 constexpr int kMaxFlowThreads = 1024;
-constexpr int kTicketTasks = 4;  // tasks taken per ticket
+constexpr int kTicketTasks = 2;  // tasks taken per ticket (2 beat 1, 4 and 8 on MI355X)
 constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus a short sleep)
 // Pieces per thread and array; the launch uses 256, 512 or 1024 threads so
 // that a chunk of either array needs at most this many.
@@ -91,6 +91,13 @@ struct ItemWalk {
 
 // One array's part of a task: the pieces of the chunk's rows, dealt to the
 // threads in row-major order (consecutive threads move consecutive pieces).
+//
+// A moved byte is read once and written once, so the loads carry the
+// non-temporal (streaming) cache hint, and so do the stores of 16-byte pieces
+// (rows of fp16 values).  Narrower pieces (rows of q8_0 blocks: 136-byte rows
+// straddle 128-byte lines) keep the normal store policy; on MI355X the hint
+// made those stores slower and the others faster.  The hint changes no
+// ordering: a read never needs a value written by the same pass.
 template <int PW, int CR>
 struct ArrayMove {
     using T = typename Piece<PW>::T;
@@ -102,7 +109,7 @@ struct ArrayMove {
         for (int k = 0; k < kItems; ++k) {
             if (w.r < CR) {
                 const int64_t s = src[w.r];
-                if (s >= 0) buf[k] = *reinterpret_cast<const T*>(base + s * rb + w.off);
+                if (s >= 0) buf[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + s * rb + w.off));
             }
             w.next();
         }
@@ -116,8 +123,13 @@ struct ArrayMove {
         ItemWalk w(rb / PW, PW);
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
-            if (w.r < CR && src[w.r] >= 0)
-                *reinterpret_cast<T*>(base + dst[w.r] * rb + w.off) = buf[k];
+            if (w.r < CR && src[w.r] >= 0) {
+                T* p = reinterpret_cast<T*>(base + dst[w.r] * rb + w.off);
+                if constexpr (PW == 16)
+                    __builtin_nontemporal_store(buf[k], p);
+                else
+                    *p = buf[k];
+            }
             w.next();
         }
     }
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
             mk.load(cv.k, cv.kb, src_row);
             mv.load(cv.v, cv.vb, src_row);
             const int64_t ps = t < CR ? src_row[t] : -1;
-            if (ps >= 0) pos = reinterpret_cast<const uint32_t*>(cv.pos)[ps];
+            if (ps >= 0) pos = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cv.pos) + ps);
             mk.wait();
             mv.wait();
             hold(pos);
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
             // 4. stores
             mk.store(cv.k, cv.kb, src_row, dst_row);
             mv.store(cv.v, cv.vb, src_row, dst_row);
-            if (ps >= 0) reinterpret_cast<uint32_t*>(cv.pos)[dst_row[t]] = pos;
+            if (ps >= 0) __builtin_nontemporal_store(pos, reinterpret_cast<uint32_t*>(cv.pos) + dst_row[t]);
             __syncthreads();  // the row tables are rewritten by the next task
         }
     }

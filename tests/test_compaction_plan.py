@@ -3,8 +3,8 @@ applies it.
 
 The kernel moves destination chunks of CR rows (CR = 256, 128 or 64, the widest
 whose pieces fit a workgroup's registers) of every unit as tasks numbered
-chunk * units + unit.  Workgroups take tasks four per ticket from a counter and
-run the tasks of a ticket one after another; a task loads its sources,
+chunk * units + unit.  Workgroups take a few tasks per ticket (the kernel's
+kTicketTasks) from a counter and run the tasks of a ticket one after another; a task loads its sources,
 publishes, waits for the earlier chunks of its unit that read its destination
 rows, and then stores.  The readers of chunk c's rows are found from the
 selector's prefix counts P[e] = (kept rows below row 64 e), e = 0 .. nb with
@@ -15,11 +15,14 @@ loads, publishes and stores over plain arrays; every interleaving the rule
 allows must leave the exact gather in every unit, and a model with the waits
 removed must fail on the same inputs (the test is not vacuous).
 """
+import os
+import re
+
 import numpy as np
 import pytest
 
 ROWS64 = 64          # granularity of the prefix counts
-TICKET_TASKS = 4     # tasks taken per ticket
+TICKET_SIZES = (1, 2, 4)  # tasks taken per ticket, modelled
 
 
 def prefix_counts(keep):
@@ -37,8 +40,8 @@ def wait_range(P, nb, c, cr):
     return p0 // cr, min(c - 1, (p1 - 1) // cr)
 
 
-def simulate(units, cr, n_workers, rng, respect_waits=True):
-    """units: list of (keep, n).  Workers take TICKET_TASKS consecutive tasks per ticket
+def simulate(units, cr, n_workers, rng, respect_waits=True, ticket_tasks=2):
+    """units: list of (keep, n).  Workers take ticket_tasks consecutive tasks per ticket
     and run them in order; a task's loads complete at any later time, and the steps of
     different workers interleave at random."""
     U = len(units)
@@ -87,8 +90,8 @@ def simulate(units, cr, n_workers, rng, respect_waits=True):
             break
         w, kind = choices[rng.integers(len(choices))]
         if kind == "ticket":
-            workers[w] = list(range(ticket, min(ticket + TICKET_TASKS, n_tasks)))
-            ticket += TICKET_TASKS
+            workers[w] = list(range(ticket, min(ticket + ticket_tasks, n_tasks)))
+            ticket += ticket_tasks
         elif kind == "begin":
             task = workers[w].pop(0)
             if live(task):
@@ -133,23 +136,32 @@ def unit_sets(seed):
         yield "+".join(p[0] for p in trio), [(p[1].astype(np.int64), p[2]) for p in trio]
 
 
+def test_the_kernel_takes_a_modelled_ticket_size():
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "kv_cache_eviction_tria_amd", "csrc", "tria_compact.hip")).read()
+    m = re.search(r"constexpr int kTicketTasks = (\d+);", src)
+    assert m and int(m.group(1)) in TICKET_SIZES
+
+
+@pytest.mark.parametrize("tt", TICKET_SIZES)
 @pytest.mark.parametrize("cr", [64, 128, 256])
 @pytest.mark.parametrize("seed", range(3))
-def test_rule_gives_the_exact_gather(cr, seed):
-    rng = np.random.default_rng(100 + seed)
+def test_rule_gives_the_exact_gather(cr, seed, tt):
+    rng = np.random.default_rng(100 + seed + 10 * tt)
     for name, units in unit_sets(seed):
-        got, want = simulate(units, cr, 5, rng)
+        got, want = simulate(units, cr, 5, rng, ticket_tasks=tt)
         for g, w in zip(got, want):
-            assert np.array_equal(g, w), (name, cr)
+            assert np.array_equal(g, w), (name, cr, tt)
 
 
+@pytest.mark.parametrize("tt", TICKET_SIZES)
 @pytest.mark.parametrize("cr", [64, 128, 256])
-def test_without_waits_it_breaks(cr):
+def test_without_waits_it_breaks(cr, tt):
     rng = np.random.default_rng(11)
     broken = 0
     for seed in range(3):
         for name, units in unit_sets(seed):
-            got, want = simulate(units, cr, 5, rng, respect_waits=False)
+            got, want = simulate(units, cr, 5, rng, respect_waits=False, ticket_tasks=tt)
             broken += sum(not np.array_equal(g, w) for g, w in zip(got, want))
     assert broken > 0
 
