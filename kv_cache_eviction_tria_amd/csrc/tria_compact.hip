@@ -43,7 +43,7 @@ namespace tria {
 namespace {
 
 constexpr int kMaxFlowThreads = 1024;
-constexpr int kTicketTasks = 2;  // tasks taken per ticket (2 beat 1, 4 and 8 on MI355X)
+constexpr int kTicketTasks = 2;  // tasks taken per ticket (2 beat 4 and 8 on MI355X)
 constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus a short sleep)
 // Pieces per thread and array; the launch uses 256, 512 or 1024 threads so
 // that a chunk of either array needs at most this many.
