@@ -28,9 +28,10 @@
 // row and no task waits on anything but loads that are already in flight.
 //
 // Tasks are handed out in increasing order from a ticket counter (a few at a
-// time), task = chunk * units + unit, so the chunks of a unit are taken in
-// order and a task only waits on smaller tasks, all of which are held by
-// workgroups that are already running.  The smallest unfinished task never
+// time), ordered by chunk, then unit, and numbered densely: only the chunks a
+// unit has are tasks (sequences of a batch keep different row counts).  So
+// the chunks of a unit are taken in order and a task only waits on smaller
+// tasks, all of which are held by workgroups that are already running.  The smallest unfinished task never
 // waits, whatever subset of the grid is resident (other kernels may share
 // the GPU).  Each wait is also bounded: a workgroup that gives up records an
 // error (see tria_device_status) and stores anyway.  The counter is reset by
@@ -43,7 +44,6 @@ namespace tria {
 namespace {
 
 constexpr int kMaxFlowThreads = 1024;
-constexpr int kTicketTasks = 2;  // tasks taken per ticket (2 beat 4 and 8 on MI355X)
 constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus a short sleep)
 // Pieces per thread and array; the launch uses 256, 512 or 1024 threads so
 // that a chunk of either array needs at most this many.
@@ -139,30 +139,99 @@ struct ArrayMove {
 template <int CR>
 __host__ __device__ inline int64_t flow_chunks(int64_t kept) { return (kept + CR - 1) / CR; }
 
+// Chunks of CR rows a unit of the sequence moves (0 when nothing is evicted).
+__host__ __device__ inline int seq_chunks(const SeqDesc& sd, int cr) {
+    return (sd.kept > 0 && sd.kept < sd.n) ? (int)((sd.kept + cr - 1) / cr) : 0;
+}
+
+// Dense task numbering.  With the sequences sorted by chunk count v_0 >= v_1
+// >= ... (ties by index) and P = units per sequence, chunk level c holds the
+// sequences with v_i > c, P units each, and tasks run level by level.  Segment
+// k covers levels [v_{k+1}, v_k), where sorted sequences 0 .. k are present;
+// it starts at task P ((k + 1) v_{k+1} + sum_{i > k} v_i).
+struct TaskPlan {
+    uint32_t t0[kMaxSeq];  // first task of segment k (non-increasing in k)
+    int c0[kMaxSeq];       // first level of segment k
+    int seq[kMaxSeq];      // sorted position -> sequence
+    int segs;              // sequences with at least one chunk
+};
+
+// A value every lane holds alike, as a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// Called by every thread of the workgroup; the first wavefront (one lane per
+// sequence, n_seq <= 64) does the work.  The caller synchronises before use.
+template <int CR>
+__device__ void build_plan(const Batch& b, TaskPlan& tp, int* sorted_v) {
+    const int i = threadIdx.x;
+    if (i < 64) {
+        const int v = i < b.n_seq ? seq_chunks(b.seq[i], CR) : -1;
+        int rank = 0, segs = 0;  // rank: position in the sorted order
+        for (int j = 0; j < b.n_seq; ++j) {
+            const int vj = __shfl(v, j);
+            rank += (vj > v) || (vj == v && j < i);
+            segs += vj > 0;
+        }
+        if (i < b.n_seq) {
+            sorted_v[rank] = v;
+            tp.seq[rank] = i;
+        }
+        if (i == 0) tp.segs = segs;
+    }
+    __syncthreads();
+    if (i < tp.segs) {
+        int64_t tail = 0;  // sum of v over sorted positions > i
+        for (int j = i + 1; j < tp.segs; ++j) tail += sorted_v[j];
+        const int v1 = i + 1 < tp.segs ? sorted_v[i + 1] : 0;
+        tp.t0[i] = (uint32_t)((int64_t)(i + 1) * v1 + tail);  // in units of P
+        tp.c0[i] = v1;
+    }
+}
+
 template <int PK, int PV, int CR>
 __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
     CacheView cv, Batch b, const int32_t* __restrict__ keep, const int32_t* __restrict__ pb,
-    uint32_t* flags, int max_chunks, uint32_t epoch, int n_units, uint32_t* ticket, int* err) {
+    uint32_t* flags, int max_chunks, uint32_t epoch, uint32_t n_tasks, int ticket_tasks,
+    uint32_t* ticket, int* err) {
     constexpr int kPerP = CR / kChunkRows;  // prefix-count entries per chunk
     __shared__ int64_t src_row[CR];  // physical source row, -1 if the row stays
     __shared__ int64_t dst_row[CR];
     __shared__ uint32_t first_sh;
+    __shared__ TaskPlan tp;
+    __shared__ int sorted_v[kMaxSeq];
     const int t = threadIdx.x;
-    const uint32_t n_tasks = (uint32_t)max_chunks * (uint32_t)n_units;
+    const int per_seq = cv.L * cv.Hkv;
+    build_plan<CR>(b, tp, sorted_v);
     while (true) {
-        if (t == 0) first_sh = atomicAdd(ticket, (uint32_t)kTicketTasks);
-        __syncthreads();
-        const uint32_t first = first_sh;
+        if (t == 0) first_sh = atomicAdd(ticket, (uint32_t)ticket_tasks);
+        __syncthreads();  // also publishes the plan on the first round
+        const uint32_t first = uniform(first_sh);
         __syncthreads();
         if (first >= n_tasks) break;
-        const uint32_t last = first + kTicketTasks < n_tasks ? first + kTicketTasks : n_tasks;
+        const uint32_t last = n_tasks - first > (uint32_t)ticket_tasks ? first + ticket_tasks : n_tasks;
         for (uint32_t task = first; task < last; ++task) {
-            const int c = (int)(task / n_units);
-            const int u = (int)(task - (int64_t)c * n_units);
+            // segment: the smallest k with P t0[k] <= task (t0[segs - 1] == 0); the
+            // plan is uniform, so the decode stays in scalar registers
+            int lo = 0, hi = uniform(tp.segs) - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((uint64_t)uniform(tp.t0[mid]) * per_seq <= task) hi = mid;
+                else lo = mid + 1;
+            }
+            const uint32_t rel = task - uniform(tp.t0[lo]) * (uint32_t)per_seq;
+            const uint32_t level = (uint32_t)(lo + 1) * (uint32_t)per_seq;  // tasks per level
+            const int c = uniform(tp.c0[lo]) + (int)(rel / level);
+            const uint32_t r = rel % level;
+            const int u = uniform(tp.seq[r / per_seq]) * per_seq + (int)(r % per_seq);
             const UnitId id = unit_id(cv, u);
             const SeqDesc& sd = b.seq[id.seq];
             const int kept = (int)sd.kept, n = (int)sd.n;
-            if (kept <= 0 || kept >= n) continue;  // nothing evicted: no row moves
+            // never taken (only the chunks a unit moves are tasks); kept as guards,
+            // which also hold the kernel to fewer registers
+            if (kept <= 0 || kept >= n) continue;
             if (c >= (int)flow_chunks<CR>(kept)) continue;
             const int uu = id.l * cv.Hkv + id.g;
             const int32_t* idx = keep + sd.keep_off + (int64_t)uu * kept;
@@ -267,7 +336,7 @@ int piece_width(int rb) {
 }
 
 using FlowKernel = void (*)(CacheView, Batch, const int32_t*, const int32_t*, uint32_t*, int,
-                            uint32_t, int, uint32_t*, int*);
+                            uint32_t, uint32_t, int, uint32_t*, int*);
 
 template <int PK, int CR>
 FlowKernel flow_for_v(int pv) {
@@ -299,6 +368,14 @@ int resident_groups(FlowKernel k, int threads) {
                                                      threads, 0) != hipSuccess)
         return 0;
     return cus * per_cu;
+}
+
+// Tasks taken per ticket: two while a workgroup has few tasks (the last
+// tickets balance the workgroups' ends), more when it has hundreds (a batch
+// of sequences): each ticket is a round trip to one counter.
+int ticket_size(int64_t tasks, int grid) {
+    int64_t tt = tasks / ((int64_t)grid * 16);
+    return (int)(tt < 2 ? 2 : (tt > 16 ? 16 : tt));
 }
 
 // 64-row chunks of the largest kept count (flags are sized for these; a launch
@@ -354,22 +431,27 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
     int threads = 256;
     while ((int64_t)threads * kItems < pieces) threads *= 2;
     if (threads > kMaxFlowThreads) return hipErrorInvalidValue;
-    int64_t chunks = 0;  // chunks of cr rows of the largest kept count
+    int64_t chunks = 0, sum_chunks = 0;  // chunks of cr rows: the largest count, the sum
     for (int i = 0; i < b.n_seq; ++i) {
-        const int64_t c = (b.seq[i].kept + cr - 1) / cr;
+        const int64_t c = seq_chunks(b.seq[i], cr);
         chunks = c > chunks ? c : chunks;
+        sum_chunks += c;
     }
-    const int64_t tasks = chunks * n_units;
+    const int64_t per_seq = (int64_t)cv.L * cv.Hkv;
+    if (per_seq * b.n_seq != n_units) return hipErrorInvalidValue;
+    const int64_t tasks = sum_chunks * per_seq;
+    if (tasks == 0) return hipSuccess;  // nothing evicted anywhere
     if (tasks >= (int64_t)1 << 31) return hipErrorInvalidValue;
     // as many workgroups as fit at once (residency is not required), or the cap
     int grid = resident_groups(k, threads);
     if (grid <= 0) return hipErrorInvalidValue;
     if (st.max_groups > 0 && st.max_groups < grid) grid = st.max_groups;
-    const int64_t need = (tasks + kTicketTasks - 1) / kTicketTasks;
+    const int tt = ticket_size(tasks, grid);
+    const int64_t need = (tasks + tt - 1) / tt;
     if (need < grid) grid = (int)need;
     st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value
     hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, s, cv, b, keep, pb, st.flags,
-                       (int)chunks, st.epoch, n_units, ticket, st.err);
+                       (int)chunks, st.epoch, (uint32_t)tasks, tt, ticket, st.err);
     return hipGetLastError();
 }
 

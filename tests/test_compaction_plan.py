@@ -2,9 +2,10 @@
 applies it.
 
 The kernel moves destination chunks of CR rows (CR = 256, 128 or 64, the widest
-whose pieces fit a workgroup's registers) of every unit as tasks numbered
-chunk * units + unit.  Workgroups take a few tasks per ticket (the kernel's
-kTicketTasks) from a counter and run the tasks of a ticket one after another; a task loads its sources,
+whose pieces fit a workgroup's registers) of every unit as tasks ordered by
+chunk, then unit, and numbered densely (only the chunks a unit moves are
+tasks).  Workgroups take a few tasks per ticket (2 to 16, chosen by the host) from a
+counter and run the tasks of a ticket one after another; a task loads its sources,
 publishes, waits for the earlier chunks of its unit that read its destination
 rows, and then stores.  The readers of chunk c's rows are found from the
 selector's prefix counts P[e] = (kept rows below row 64 e), e = 0 .. nb with
@@ -22,7 +23,7 @@ import numpy as np
 import pytest
 
 ROWS64 = 64          # granularity of the prefix counts
-TICKET_SIZES = (1, 2, 4)  # tasks taken per ticket, modelled
+TICKET_SIZES = (1, 2, 4, 16)  # tasks taken per ticket, modelled
 
 
 def prefix_counts(keep):
@@ -52,19 +53,16 @@ def simulate(units, cr, n_workers, rng, respect_waits=True, ticket_tasks=2):
         wants.append(rows[keep])
         P, nb = prefix_counts(keep)
         plans.append((keep, n, P, nb))
-    max_chunks = max((len(k) + cr - 1) // cr for k, _ in units)
-    n_tasks = max_chunks * U
+    # the kernel's dense numbering (each unit its own sequence here): only the
+    # chunks a unit moves are tasks, level by level
+    chunks = [(len(k) + cr - 1) // cr if 0 < len(k) < n else 0 for k, n in units]
+    n_tasks = sum(chunks)
+    order = [decode(t, dense_plan(chunks, 1), 1) for t in range(n_tasks)]
     published = set()
     ticket = 0
     workers = [[] for _ in range(n_workers)]  # pending tasks of a worker's ticket
     state = [None] * n_workers  # (task, stage, loaded values)
     done = 0
-
-    def live(task):
-        c, u = divmod(task, U)
-        keep, n, P, nb = plans[u]
-        K = len(keep)
-        return 0 < K < n and c < (K + cr - 1) // cr
 
     while True:
         choices = []
@@ -79,10 +77,10 @@ def simulate(units, cr, n_workers, rng, respect_waits=True, ticket_tasks=2):
                 if stage == "issued":
                     choices.append((w, "arrive"))
                 else:  # published: store once every reader of its rows has loaded
-                    c, u = divmod(task, U)
+                    c, u = order[task]
                     keep, n, P, nb = plans[u]
                     rng_ = wait_range(P, nb, c, cr)
-                    ready = rng_ is None or all((cc * U + u) in published
+                    ready = rng_ is None or all((cc, u) in published
                                                 for cc in range(rng_[0], rng_[1] + 1))
                     if ready or not respect_waits:
                         choices.append((w, "store"))
@@ -94,21 +92,18 @@ def simulate(units, cr, n_workers, rng, respect_waits=True, ticket_tasks=2):
             ticket += ticket_tasks
         elif kind == "begin":
             task = workers[w].pop(0)
-            if live(task):
-                state[w] = (task, "issued", None)
-            else:
-                done += 1  # nothing to move in this unit / chunk
+            state[w] = (task, "issued", None)
         elif kind == "arrive":
             task, _, _ = state[w]
-            c, u = divmod(task, U)
+            c, u = order[task]
             keep = plans[u][0]
             d = np.arange(c * cr, min((c + 1) * cr, len(keep)))
             vals = mems[u][keep[d]].copy()
-            published.add(task)
+            published.add((c, u))
             state[w] = (task, "published", (d, vals))
         else:
             task, _, (d, vals) = state[w]
-            c, u = divmod(task, U)
+            c, u = order[task]
             mems[u][d] = vals
             state[w] = None
             done += 1
@@ -137,10 +132,13 @@ def unit_sets(seed):
 
 
 def test_the_kernel_takes_a_modelled_ticket_size():
+    """The host picks the tasks per ticket within bounds the model covers."""
     src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                             "kv_cache_eviction_tria_amd", "csrc", "tria_compact.hip")).read()
-    m = re.search(r"constexpr int kTicketTasks = (\d+);", src)
-    assert m and int(m.group(1)) in TICKET_SIZES
+    m = re.search(r"return \(int\)\(tt < (\d+) \? \d+ : \(tt > (\d+) \? \d+ : tt\)\);", src)
+    assert m
+    lo, hi = int(m.group(1)), int(m.group(2))
+    assert lo >= min(TICKET_SIZES) and hi <= max(TICKET_SIZES)
 
 
 @pytest.mark.parametrize("tt", TICKET_SIZES)
@@ -183,3 +181,65 @@ def test_readers_of_a_chunk_are_earlier_or_itself(cr):
                 assert readers.min() >= P[per * c], name
                 assert readers.max() <= P[min(per * c + per, nb)] - 1, name
                 assert readers.max() // cr <= c, name
+
+
+def dense_plan(chunks, per_seq):
+    """The kernel's dense task numbering, restated: sequences sorted by chunk count
+    (descending, ties by index); segment k covers levels [v[k+1], v[k]) with the
+    first k + 1 sorted sequences present and starts at task
+    per_seq * ((k + 1) v[k+1] + sum(v[k+1:]))."""
+    order = sorted(range(len(chunks)), key=lambda i: (-chunks[i], i))
+    v = [chunks[i] for i in order if chunks[i] > 0]
+    segs = len(v)
+    t0 = [per_seq * ((k + 1) * (v[k + 1] if k + 1 < segs else 0) + sum(v[k + 1:]))
+          for k in range(segs)]
+    c0 = [v[k + 1] if k + 1 < segs else 0 for k in range(segs)]
+    return order, t0, c0, segs
+
+
+def decode(task, plan, per_seq):
+    order, t0, c0, segs = plan
+    lo, hi = 0, segs - 1  # smallest k with t0[k] <= task
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if t0[mid] <= task:
+            hi = mid
+        else:
+            lo = mid + 1
+    rel = task - t0[lo]
+    level = (lo + 1) * per_seq
+    c = c0[lo] + rel // level
+    r = rel % level
+    return c, order[r // per_seq] * per_seq + r % per_seq
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_dense_task_numbering_is_a_level_ordered_bijection(seed):
+    """Every (chunk, unit) a batch moves is exactly one task, tasks run level by
+    level (so a chunk's waits are on smaller tasks), and no task is empty."""
+    rng = np.random.default_rng(seed)
+    n_seq = int(rng.integers(1, 65))
+    per_seq = int(rng.integers(1, 9)) * int(rng.integers(1, 5))
+    chunks = [int(x) for x in rng.integers(0, 40, size=n_seq)]
+    if seed % 5 == 0:
+        chunks = [chunks[0]] * n_seq  # all equal
+    if seed % 7 == 0:
+        chunks[int(rng.integers(0, n_seq))] = 0
+    total = per_seq * sum(chunks)
+    if total == 0:
+        return
+    plan = dense_plan(chunks, per_seq)
+    seen = set()
+    last_level = 0
+    for task in range(total):
+        c, u = decode(task, plan, per_seq)
+        assert 0 <= u < n_seq * per_seq
+        assert 0 <= c < chunks[u // per_seq], (task, c, u)
+        assert c >= last_level
+        last_level = c
+        seen.add((c, u))
+    assert len(seen) == total
+    if n_seq == 1 or len(set(chunks)) == 1:  # one chunk count: task = c * units + u
+        units = n_seq * per_seq
+        for task in range(total):
+            assert decode(task, plan, per_seq) == (task // units, task % units)
