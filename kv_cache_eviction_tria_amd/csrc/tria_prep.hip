@@ -79,13 +79,21 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
         // stored row (zero at the block scales), four per stored word.
         const int W = cg.W, RB = 34 * cg.NB;
         __shared__ int ex_sh[64];
+        // each head's largest |coefficient| (NaN left out), one (head, pair) per
+        // thread: non-negative doubles order as their bit patterns
+        __shared__ unsigned long long mx_sh[64];
+        for (int j = threadIdx.x; j < G; j += kPrepThreads) mx_sh[j] = 0ull;
+        __syncthreads();
+        for (int i = threadIdx.x; i < F * G; i += kPrepThreads) {
+            const int j = i / F, f = i - j * F;
+            const int64_t s = stat0 + (int64_t)j * F + f;
+            const double qr = q_re[s], qi = q_im[s];
+            const double v = fmax(fabs(qr * a_re[f] - qi * a_im[f]), fabs(qr * a_im[f] + qi * a_re[f]));
+            if (v > 0.0) atomicMax(&mx_sh[j], (unsigned long long)__double_as_longlong(v));
+        }
+        __syncthreads();
         for (int j = threadIdx.x; j < G; j += kPrepThreads) {
-            const int64_t s0 = stat0 + (int64_t)j * F;
-            double m = 0.0;
-            for (int f = 0; f < F; ++f) {
-                const double qr = q_re[s0 + f], qi = q_im[s0 + f];
-                m = fmax(m, fmax(fabs(qr * a_re[f] - qi * a_im[f]), fabs(qr * a_im[f] + qi * a_re[f])));
-            }
+            const double m = __longlong_as_double((long long)mx_sh[j]);
             int ex = 0;
             if (m > 0.0 && isfinite(m)) ex = 14 - ilogb(m);
             ex = ex > 100 ? 100 : (ex < -100 ? -100 : ex);
