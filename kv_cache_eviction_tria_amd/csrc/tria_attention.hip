@@ -222,7 +222,8 @@ __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
         if constexpr (VEC) {
             for (int rr = ro; rr < nt; rr += RPI) {
                 const uint8_t* vrow = cv.v + row_index(cv, id, t0 + rr) * vb;
-                const u32x4 x = reinterpret_cast<const u32x4*>(vrow)[dg];
+                // V is read once per step: streaming (non-temporal) loads
+                const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow) + dg);
                 const uint32_t w[4] = {x.x, x.y, x.z, x.w};
                 float vv[8];
 #pragma unroll

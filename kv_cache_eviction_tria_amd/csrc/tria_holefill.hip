@@ -92,6 +92,10 @@ __device__ __forceinline__ void use(const T& x) {
 // move), every piece loaded and stored by the same thread (no move reads a row
 // another one writes), pieces dealt row-major so that threads touch
 // consecutive bytes.
+// Moved bytes are read once and written once: loads carry the non-temporal
+// (streaming) hint, and so do stores of 16-byte pieces (fp16 rows); narrower
+// pieces (q8_0 rows straddle cache lines) keep the normal store policy, as in
+// the ordered compaction.
 template <int PW>
 __device__ __forceinline__ void copy_direct(uint8_t* base, int rb, const int64_t* src,
                                             const int64_t* dst) {
@@ -101,8 +105,9 @@ __device__ __forceinline__ void copy_direct(uint8_t* base, int rb, const int64_t
         const int r = i / ppr;
         if (src[r] >= 0) {
             const int off = (i - r * ppr) * PW;
-            const T x = *reinterpret_cast<const T*>(base + src[r] * rb + off);
-            *reinterpret_cast<T*>(base + dst[r] * rb + off) = x;
+            const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + src[r] * rb + off));
+            if constexpr (PW == 16) __builtin_nontemporal_store(x, reinterpret_cast<T*>(base + dst[r] * rb + off));
+            else *reinterpret_cast<T*>(base + dst[r] * rb + off) = x;
         }
     }
 }
@@ -121,7 +126,7 @@ struct RowsMove {
             const int i = (int)threadIdx.x + k * kHoleThreads;
             const int r = i / ppr;
             if (r < rows && src[r] >= 0)
-                buf[k] = *reinterpret_cast<const T*>(base + src[r] * rb + (i - r * ppr) * PW);
+                buf[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + src[r] * rb + (i - r * ppr) * PW));
         }
     }
     __device__ __forceinline__ void wait() {
@@ -136,7 +141,11 @@ struct RowsMove {
             const int i = (int)threadIdx.x + k * kHoleThreads;
             const int r = i / ppr;
             if (r < rows && src[r] >= 0)
-                *reinterpret_cast<T*>(base + dst[r] * rb + (i - r * ppr) * PW) = buf[k];
+            {
+                T* q = reinterpret_cast<T*>(base + dst[r] * rb + (i - r * ppr) * PW);
+                if constexpr (PW == 16) __builtin_nontemporal_store(buf[k], q);
+                else *q = buf[k];
+            }
         }
     }
 };
