@@ -86,22 +86,26 @@ __device__ __forceinline__ void sync_acc(float (&acc)[GT]) {
     }
 }
 
+// Raw scores are written once and read once, by the selector: streaming
+// (non-temporal) stores (the q8_0 scorer measured 3-5 % faster with them).
 template <int GT>
 __device__ __forceinline__ void store_scores(float* dst, const float (&acc)[GT], bool packed) {
+    typedef float f2e __attribute__((ext_vector_type(2)));
+    typedef float f4e __attribute__((ext_vector_type(4)));
     if (packed) {
         if constexpr (GT == 1) {
-            dst[0] = acc[0];
+            __builtin_nontemporal_store(acc[0], dst);
         } else if constexpr (GT == 2) {
-            *reinterpret_cast<float2*>(dst) = make_float2(acc[0], acc[1]);
+            __builtin_nontemporal_store(f2e{acc[0], acc[1]}, reinterpret_cast<f2e*>(dst));
         } else if constexpr (GT == 4) {
-            *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            __builtin_nontemporal_store(f4e{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f4e*>(dst));
         } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            __builtin_nontemporal_store(f4e{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f4e*>(dst));
+            __builtin_nontemporal_store(f4e{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<f4e*>(dst + 4));
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < GT; ++j) dst[j] = acc[j];
+        for (int j = 0; j < GT; ++j) __builtin_nontemporal_store(acc[j], dst + j);
     }
 }
 
@@ -698,11 +702,13 @@ __global__ __launch_bounds__(kMfmaThreads) void score_f16_mfma_kernel(
         const bool row_ok = r_out < n;
         if (row_ok) {
             if (vec_store) {
-                *reinterpret_cast<float4*>(rout + r_out * G + 4 * kg) = make_float4(v[0], v[1], v[2], v[3]);
+                typedef float f4e __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f4e{v[0], v[1], v[2], v[3]},
+                                            reinterpret_cast<f4e*>(rout + r_out * G + 4 * kg));
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (4 * kg + i < gc) rout[r_out * G + 4 * kg + i] = v[i];
+                    if (4 * kg + i < gc) __builtin_nontemporal_store(v[i], rout + r_out * G + 4 * kg + i);
             }
         }
         if (part) {

@@ -130,17 +130,25 @@ struct RowLoad {
     float4 v[GV == 0 ? 1 : (GV + 3) / 4];
 };
 
+// The raw scores are read once per pass (the few rows of the cutoff bin are
+// read again): streaming (non-temporal) loads.  On MI355X this made the pass
+// about 1 % faster, the gain showing in the compaction that follows.
 template <int GV>
 __device__ __forceinline__ void load_row(RowLoad<GV>& x, const float* R, int64_t r) {
     if constexpr (GV == 1) {
-        x.v[0].x = R[r];
+        x.v[0].x = __builtin_nontemporal_load(R + r);
     } else if constexpr (GV == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(R + r * 2);
+        typedef float f2e __attribute__((ext_vector_type(2)));
+        const f2e t = __builtin_nontemporal_load(reinterpret_cast<const f2e*>(R + r * 2));
         x.v[0].x = t.x;
         x.v[0].y = t.y;
     } else if constexpr (GV >= 4) {
 #pragma unroll
-        for (int i = 0; i < GV / 4; ++i) x.v[i] = reinterpret_cast<const float4*>(R + r * GV)[i];
+        for (int i = 0; i < GV / 4; ++i) {
+            typedef float f4e __attribute__((ext_vector_type(4)));
+            const f4e t = __builtin_nontemporal_load(reinterpret_cast<const f4e*>(R + r * GV) + i);
+            x.v[i] = make_float4(t.x, t.y, t.z, t.w);
+        }
     }
 }
 
