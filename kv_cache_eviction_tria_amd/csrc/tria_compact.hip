@@ -31,9 +31,9 @@
 // time), ordered by chunk, then unit, and numbered densely: only the chunks a
 // unit has are tasks (sequences of a batch keep different row counts).  So
 // the chunks of a unit are taken in order and a task only waits on smaller
-// tasks, all of which are held by workgroups that are already running.  The smallest unfinished task never
-// waits, whatever subset of the grid is resident (other kernels may share
-// the GPU).  Each wait is also bounded: a workgroup that gives up records an
+// tasks, all of which are held by workgroups that are already running.  The
+// smallest unfinished task never waits, whatever subset of the grid is
+// resident (other kernels may share the GPU).  Each wait is also bounded: a workgroup that gives up records an
 // error (see tria_device_status) and stores anyway.  The counter is reset by
 // the kernel that runs before the compaction on the same stream (the
 // selector, or the prefix-count kernel for caller-provided indices).
