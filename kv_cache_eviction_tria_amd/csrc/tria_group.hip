@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_agg_kernel(
         if constexpr (GV > 0) {
 #pragma unroll
             for (int q = 0; q < GV / 4; ++q) {
-                const float4 v = reinterpret_cast<const float4*>(R)[q];
+                // raw scores are read once here: streaming (non-temporal) loads
+                typedef float f4e __attribute__((ext_vector_type(4)));
+                const f4e v = __builtin_nontemporal_load(reinterpret_cast<const f4e*>(R) + q);
                 const float sv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
