@@ -164,6 +164,7 @@ __device__ __forceinline__ uint32_t uniform(uint32_t x) {
 
 // Called by every thread of the workgroup; the first wavefront (one lane per
 // sequence, n_seq <= 64) does the work.  The caller synchronises before use.
+static_assert(kMaxSeq <= 64, "one lane of a wavefront per sequence");
 template <int CR>
 __device__ void build_plan(const Batch& b, TaskPlan& tp, int* sorted_v) {
     const int i = threadIdx.x;
