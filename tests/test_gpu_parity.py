@@ -348,6 +348,34 @@ def test_serial_compaction_reference(pattern):
     ctx.close()
 
 
+@pytest.mark.parametrize("groups", [1, 3])
+def test_paged_batch_compaction_on_a_small_grid(groups):
+    """A paged batch whose sequences move different numbers of chunks (one moves
+    none): the compaction's densely numbered tasks, taken by 1 or 3 workgroups,
+    leave the pools byte-identical to the full grid's."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged_grid", L=5, Hkv=2, Hq=8, hd=128)
+    lens = [3000, 517, 1200, 64, 2048, 4100]
+    budgets = [900, 150, 1200, 70, 600, 1000]  # seq 3 keeps everything
+    S, W = 0, 128
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 91)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 9)
+    pu.say("case paged compaction on %d workgroups" % groups)
+    outs = []
+    for g in (groups, 0):
+        ctx = pu.make_ctx(wl, stats)
+        tria.tria_set_compaction_workgroups(ctx, g)
+        dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+        kept = tria.tria_evict_paged_batch(ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"],
+                                           dev["block_table"], lens, budgets, S, W)
+        tria.tria_device_status(ctx)
+        outs.append((kept, [dev[k].cpu() for k in ("k_pool", "v_pool", "pos_pool")]))
+        ctx.close()
+    (ka, a), (kb, b) = outs
+    assert ka == kb
+    for x, y, name in zip(a, b, ("k", "v", "pos")):
+        assert torch.equal(x, y), name
+
+
 def _oracle_layers(wl, stats, k0, p0, l0, nl):
     """The oracle's scores, aggregates and kept rows for layers [l0, l0 + nl) of a
     device cache, from host copies of just those layers (bounds host memory)."""
