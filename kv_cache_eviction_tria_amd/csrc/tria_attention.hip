@@ -220,6 +220,11 @@ __global__ __launch_bounds__(kAttThreads) void attention_split_kernel(
         //    its own later reads: one wavefront, in order)
         const int nt = (int)(r_hi - t0 < 64 ? r_hi - t0 : 64);
         if constexpr (VEC) {
+            // unrolled so that several V loads of a tile are in flight together
+            // (two per pass, as the compiler left the loop, ran at 5.0 TB/s
+            // against 6.1 with four; eight per pass cost G = 8 a wave per SIMD)
+            constexpr int kVUnroll = GT <= 4 ? 4 : 2;
+#pragma unroll kVUnroll
             for (int rr = ro; rr < nt; rr += RPI) {
                 const uint8_t* vrow = cv.v + row_index(cv, id, t0 + rr) * vb;
                 // V is read once per step: streaming (non-temporal) loads
