@@ -109,7 +109,8 @@ struct ArrayMove {
         for (int k = 0; k < kItems; ++k) {
             if (w.r < CR) {
                 const int64_t s = src[w.r];
-                if (s >= 0) buf[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + s * rb + w.off));
+                if (s >= 0)
+                    buf[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + s * rb + w.off));
             }
             w.next();
         }

@@ -106,8 +106,9 @@ __device__ __forceinline__ void copy_direct(uint8_t* base, int rb, const int64_t
         if (src[r] >= 0) {
             const int off = (i - r * ppr) * PW;
             const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + src[r] * rb + off));
-            if constexpr (PW == 16) __builtin_nontemporal_store(x, reinterpret_cast<T*>(base + dst[r] * rb + off));
-            else *reinterpret_cast<T*>(base + dst[r] * rb + off) = x;
+            T* d = reinterpret_cast<T*>(base + dst[r] * rb + off);
+            if constexpr (PW == 16) __builtin_nontemporal_store(x, d);
+            else *d = x;
         }
     }
 }
@@ -126,7 +127,8 @@ struct RowsMove {
             const int i = (int)threadIdx.x + k * kHoleThreads;
             const int r = i / ppr;
             if (r < rows && src[r] >= 0)
-                buf[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(base + src[r] * rb + (i - r * ppr) * PW));
+                buf[k] = __builtin_nontemporal_load(
+                    reinterpret_cast<const T*>(base + src[r] * rb + (i - r * ppr) * PW));
         }
     }
     __device__ __forceinline__ void wait() {
@@ -140,8 +142,7 @@ struct RowsMove {
         for (int k = 0; k < kHoleItems; ++k) {
             const int i = (int)threadIdx.x + k * kHoleThreads;
             const int r = i / ppr;
-            if (r < rows && src[r] >= 0)
-            {
+            if (r < rows && src[r] >= 0) {
                 T* q = reinterpret_cast<T*>(base + dst[r] * rb + (i - r * ppr) * PW);
                 if constexpr (PW == 16) __builtin_nontemporal_store(buf[k], q);
                 else *q = buf[k];
