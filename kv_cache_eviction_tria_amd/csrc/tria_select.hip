@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     }
 
     __shared__ HeadNorm norm_sh[64];
-    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t hist[kBins + 64];  // + one spare bin per lane, never read
     __shared__ uint32_t list[kListCap];
     __shared__ uint32_t rhist[kWaves][256];
     __shared__ uint32_t tot[256];
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
         const HeadNorm hn = part ? merge_head_norm(P, tiles, G, h) : HeadNorm{0.0f, 0.0f, 1.0f};
         if (lane == 0) norm_sh[h] = hn;
     }
-    for (int i = t; i < kBins; i += kSelThreads) hist[i] = 0;
+    for (int i = t; i < kBins + 64; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     Norms<GV> nrm;
     nrm.load(norm_sh);
@@ -280,29 +280,50 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     constexpr int kBatch = kBatchRows<GV>;
     constexpr int kNB = (RPT + kBatch - 1) / kBatch;
     constexpr int kUB = kRegKeys ? kNB : 1;
+    // Two copies of this loop: one for units whose every owned row exists (and
+    // no aggregate output), with no branch per row (rows that are not
+    // candidates count into a spare bin of their lane's own), and one for the
+    // rest.  The row count and the candidate range are re-read through empty
+    // asm statements and each packed bin word is fixed once written, so that
+    // the compiler keeps neither these per-row conditions nor every row's bin
+    // in registers of their own for the later phases.
+    auto histogram = [&](auto all_rows) {
+        constexpr bool kAll = decltype(all_rows)::value;
+        int n2 = n, clo = cand_lo;
+        asm volatile("" : "+s"(n2), "+s"(clo));
 #pragma unroll kUB
-    for (int j0 = 0; j0 < RPT; j0 += kBatch) {
-        RowLoad<GV> x[kBatch];
+        for (int j0 = 0; j0 < RPT; j0 += kBatch) {
+            RowLoad<GV> x[kBatch];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int r = row_of(j0 + q);
-            if (j0 + q < RPT && r < n) load_row<GV>(x[q], R, r);
-        }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int j = j0 + q;
-            if (j >= RPT) break;
-            const int r = row_of(j);
-            if (r < n) {
-                const float a = agg_of<GV>(x[q], R, r, G, nrm, norm_sh);
-                if (AG) AG[r] = a;
-                const int bn = bin_of(a);
-                if (is_cand(r)) atomicAdd(&hist[bn], 1u);
-                if constexpr (kRegKeys) binw[j >> 1] |= (uint32_t)bn << (16 * (j & 1));
-                else KS[r] = order_key(a);
+            for (int q = 0; q < kBatch; ++q) {
+                const int r = row_of(j0 + q);
+                if (j0 + q < RPT && (kAll || r < n2)) load_row<GV>(x[q], R, r);
             }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int j = j0 + q;
+                if (j >= RPT) break;
+                const int r = row_of(j);
+                if (kAll || r < n2) {
+                    const float a = agg_of<GV>(x[q], R, r, G, nrm, norm_sh);
+                    if (!kAll && AG) AG[r] = a;
+                    const int bn = bin_of(a);
+                    const bool cand = (unsigned)(r - clo) < (unsigned)n_cand;
+                    if constexpr (kAll) atomicAdd(&hist[cand ? bn : kBins + lane], 1u);
+                    else if (cand) atomicAdd(&hist[bn], 1u);
+                    if constexpr (kRegKeys) {
+                        binw[j >> 1] |= (uint32_t)bn << (16 * (j & 1));
+                        if ((j & 1) || j + 1 == RPT) asm volatile("" : "+v"(binw[j >> 1]));
+                    } else {
+                        KS[r] = order_key(a);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    if (!AG && n >= RPT * kSelThreads) histogram(std::true_type{});
+    else histogram(std::false_type{});
     __syncthreads();
     // the key of row r recomputed exactly as above
     auto key_at = [&](int r) -> uint32_t {

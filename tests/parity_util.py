@@ -131,8 +131,14 @@ def gpu_pass(ctx, k, v, pos, n, budget, sink, window, G):
     tria.tria_score(ctx, k, v, pos, n, raw)
     K2 = tria.tria_select(ctx, raw, n, budget, sink, window, keep, agg)
     assert K2 == K
+    # without the aggregate output the selector takes its own histogram loop where
+    # every owned row exists (n a multiple of its 1024 threads): the same rows
+    keep_noagg = torch.empty_like(keep)
+    assert tria.tria_select(ctx, raw, n, budget, sink, window, keep_noagg) == K
     tria.tria_compact(ctx, k, v, pos, n, keep, K)
     torch.cuda.synchronize()
+    assert torch.equal(keep_noagg[:, :, :K], keep[:, :, :K]), \
+        "kept rows differ without the aggregate output"
     return dict(raw=host(raw)[:, :, :n], agg=host(agg)[:, :, :n], keep=host(keep)[:, :, :K], K=K)
 
 
