@@ -59,7 +59,7 @@ extern "C" {
 
 /* Error codes. */
 #define TRIA_OK 0
-#define TRIA_E_INVAL (-1)       /* null pointer, size out of range, negative budget/sink/window,
+#define TRIA_E_INVAL (-1)       /* null or misaligned pointer, size out of range, negative budget/sink/window,
                                    offsets not strictly ascending and positive */
 #define TRIA_E_UNSUPPORTED (-2) /* shape outside the GPU scorer's eligibility gate */
 #define TRIA_E_HIP (-3)         /* a HIP runtime call failed; see tria_last_hip_error */
@@ -95,7 +95,9 @@ typedef struct tria_model_desc {
     const int64_t *offsets;/* host: future query offsets, strictly ascending, > 0 */
 } tria_model_desc;
 
-/* Contiguous cache (device pointers, caller-owned). */
+/* Contiguous cache (device pointers, caller-owned).  k and v start on a
+ * 16-byte boundary, pos on a 4-byte one (TRIA_E_INVAL otherwise): the kernels
+ * move rows in pieces of up to 16 bytes. */
 typedef struct tria_cache {
     void *k;
     void *v;
@@ -103,7 +105,8 @@ typedef struct tria_cache {
     int64_t cap; /* rows per unit */
 } tria_cache;
 
-/* Paged cache (device pointers, caller-owned). */
+/* Paged cache (device pointers, caller-owned).  k_pool and v_pool start on a
+ * 16-byte boundary, pos_pool and block_table on a 4-byte one. */
 typedef struct tria_paged_cache {
     void *k_pool;
     void *v_pool;
@@ -146,7 +149,7 @@ int64_t tria_row_bytes(int32_t kv_type, int32_t head_dim);
 int64_t tria_kept_count(int64_t n_tokens, int64_t budget, int64_t sink, int64_t window);
 
 /* Raw per-query-head scores of the first n_tokens rows of every unit.
- *   raw_scores : device [L][Hkv][n_tokens][G] fp32, written.
+ *   raw_scores : device [L][Hkv][n_tokens][G] fp32, written; 16-byte aligned.
  * 0 <= n_tokens <= cache->cap, n_tokens <= TRIA_MAX_ROWS.  Returns TRIA_OK or
  * an error code. */
 int tria_score(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, float *raw_scores,
@@ -157,9 +160,9 @@ int tria_score(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens, float *
  * (sigma = 0 gives z = 0); agg = max over the group, or -inf if any of the
  * row's scores is not finite; keep the protected rows plus the highest-agg
  * candidates (ties to the lower row index) up to tria_kept_count.
- *   raw_scores : device [L][Hkv][n_tokens][G], read.
- *   keep_idx   : device [L][Hkv][kept], written (ascending rows).
- *   agg_out    : device [L][Hkv][n_tokens] fp32, written if not NULL.
+ *   raw_scores : device [L][Hkv][n_tokens][G], read; 16-byte aligned.
+ *   keep_idx   : device [L][Hkv][kept], written (ascending rows); 4-byte aligned.
+ *   agg_out    : device [L][Hkv][n_tokens] fp32, written if not NULL; 4-byte aligned.
  * n_tokens <= TRIA_MAX_ROWS.  Returns the kept count (>= 0) or an error code. */
 int64_t tria_select(tria_ctx *ctx, const float *raw_scores, int64_t n_tokens, int64_t budget,
                     int64_t sink, int64_t window, int32_t *keep_idx, float *agg_out,
@@ -169,8 +172,8 @@ int64_t tria_select(tria_ctx *ctx, const float *raw_scores, int64_t n_tokens, in
  * "Phase B" step 4; [WL], "What was implemented": GPU gather/repack):
  *   row d <- row keep_idx[d] for d < kept, in every unit.  Bytes are copied
  *   exactly; rows >= kept are left unspecified.
- * keep_idx must be strictly ascending per unit (as tria_select writes it).
- * An entry outside [d, n_tokens) is skipped (row d is left as it was).
+ * keep_idx (4-byte aligned) must be strictly ascending per unit (as
+ * tria_select writes it).  An entry outside [d, n_tokens) is skipped (row d is left as it was).
  * Indices that are not ascending never cause an access out of bounds, but the
  * result is then unspecified. */
 int tria_compact(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
@@ -331,8 +334,9 @@ int64_t tria_decode_step(tria_ctx *ctx, const tria_cache *cache, const tria_poli
  * g*G + j (KV head g):
  *   out_h = sum_r softmax_r(scale * q_h . k_r) v_r   over the unit's n rows.
  * Row order does not matter (ordered or hole-filled caches alike).
- *   q, out : device fp32 [L][Hq][head_dim] (q already rotated for its
- *            position; the keys are stored rotated); n_tokens = 0 gives zeros.
+ *   q, out : device fp32 [L][Hq][head_dim], 4-byte aligned (q already rotated
+ *            for its position; the keys are stored rotated); n_tokens = 0 gives
+ *            zeros.
  * fp32 arithmetic; every K and V row is read once.  Scratch (per-range
  * partial results) is owned by the context. */
 int tria_decode_attention(tria_ctx *ctx, const tria_cache *cache, int64_t n_tokens,
@@ -369,7 +373,9 @@ int tria_calib_create(tria_calib **out, int32_t n_layers, int32_t n_q_heads, int
 /* Adds n_tokens query rows of one layer: q (device) holds row t at element
  * t * row_stride, head h's head_dim values at + h * head_dim (row_stride >=
  * n_q_heads * head_dim, e.g. the query slice of a fused projection), type
- * TRIA_Q_*.  Stream-ordered; q must stay valid until the work has run.  One
+ * TRIA_Q_*, q aligned to its element size.  Rows whose base and stride allow
+ * it are read in 16-byte (fp32) or 8-byte pieces.  Stream-ordered; q must stay
+ * valid until the work has run.  One
  * kernel launch, no allocation.  Calls on one object must use one stream (or
  * be ordered by the caller): they add into the same accumulators. */
 int tria_calib_add(tria_calib *c, int32_t layer, const void *q, int32_t q_type, int64_t n_tokens,

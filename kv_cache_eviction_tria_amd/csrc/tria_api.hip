@@ -213,8 +213,13 @@ Batch one_seq(int64_t n, const Protect& p) {
     return b;
 }
 
+// The kernels move rows in pieces of up to 16 bytes and scores in vectors of up
+// to 16 bytes: the arrays must start on those boundaries (rows then keep them).
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 int check_cache(const tria_cache* c, int64_t n) {
     if (!c || !c->k || !c->v || !c->pos) return TRIA_E_INVAL;
+    if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->pos, 4)) return TRIA_E_INVAL;
     if (n < 0 || c->cap < 0 || n > c->cap || n > kMaxRows) return n > kMaxRows ? TRIA_E_UNSUPPORTED : TRIA_E_INVAL;
     return TRIA_OK;
 }
@@ -553,6 +558,7 @@ int64_t tria_evict_noalloc(tria_ctx* ctx, const tria_cache* cache, int64_t n_tok
 int tria_decode_attention(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, const float* q,
                           float scale, float* out, hipStream_t stream) {
     if (!ctx || !q || !out) return TRIA_E_INVAL;
+    if (!aligned(q, 4) || !aligned(out, 4)) return TRIA_E_INVAL;
     int rc = check_cache(cache, n_tokens);
     if (rc) return rc;
     Protect p;
@@ -566,7 +572,11 @@ int tria_decode_attention_paged_batch(tria_ctx* ctx, const tria_paged_cache* cac
                                       const int64_t* n_tokens, const float* q, float scale,
                                       float* out, hipStream_t stream) {
     if (!ctx || !cache || !n_tokens || !q || !out) return TRIA_E_INVAL;
+    if (!aligned(q, 4) || !aligned(out, 4)) return TRIA_E_INVAL;
     if (!cache->k_pool || !cache->v_pool || !cache->pos_pool || !cache->block_table)
+        return TRIA_E_INVAL;
+    if (!aligned(cache->k_pool, 16) || !aligned(cache->v_pool, 16) ||
+        !aligned(cache->pos_pool, 4) || !aligned(cache->block_table, 4))
         return TRIA_E_INVAL;
     if (n_seq < 1 || n_seq > TRIA_MAX_SEQ || cache->n_blocks < 1 || cache->max_blocks < 1)
         return TRIA_E_INVAL;
@@ -722,6 +732,7 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
 int tria_score(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens, float* raw_scores,
                hipStream_t stream) {
     if (!ctx || !raw_scores) return TRIA_E_INVAL;
+    if (!aligned(raw_scores, 16)) return TRIA_E_INVAL;
     int rc = check_cache(cache, n_tokens);
     if (rc) return rc;
     if (n_tokens == 0) return TRIA_OK;
@@ -734,6 +745,8 @@ int64_t tria_select(tria_ctx* ctx, const float* raw_scores, int64_t n_tokens, in
                     int64_t sink, int64_t window, int32_t* keep_idx, float* agg_out,
                     hipStream_t stream) {
     if (!ctx || !raw_scores || !keep_idx) return TRIA_E_INVAL;
+    if (!aligned(raw_scores, 16) || !aligned(keep_idx, 4) || !aligned(agg_out, 4))
+        return TRIA_E_INVAL;
     if (n_tokens < 0 || budget < 0 || sink < 0 || window < 0) return TRIA_E_INVAL;
     if (n_tokens > kMaxRows) return TRIA_E_UNSUPPORTED;
     if (n_tokens == 0) return 0;
@@ -746,6 +759,7 @@ int64_t tria_select(tria_ctx* ctx, const float* raw_scores, int64_t n_tokens, in
 int tria_compact(tria_ctx* ctx, const tria_cache* cache, int64_t n_tokens,
                  const int32_t* keep_idx, int64_t kept, hipStream_t stream) {
     if (!ctx || !keep_idx) return TRIA_E_INVAL;
+    if (!aligned(keep_idx, 4)) return TRIA_E_INVAL;
     int rc = check_cache(cache, n_tokens);
     if (rc) return rc;
     if (kept < 0 || kept > n_tokens) return TRIA_E_INVAL;
@@ -788,6 +802,9 @@ int tria_evict_paged_batch(tria_ctx* ctx, const tria_paged_cache* cache, int32_t
                            int64_t window, int64_t* kept_out, hipStream_t stream) {
     if (!ctx || !cache || !n_tokens || !budget || !kept_out) return TRIA_E_INVAL;
     if (!cache->k_pool || !cache->v_pool || !cache->pos_pool || !cache->block_table)
+        return TRIA_E_INVAL;
+    if (!aligned(cache->k_pool, 16) || !aligned(cache->v_pool, 16) ||
+        !aligned(cache->pos_pool, 4) || !aligned(cache->block_table, 4))
         return TRIA_E_INVAL;
     if (n_seq < 1 || n_seq > TRIA_MAX_SEQ || sink < 0 || window < 0) return TRIA_E_INVAL;
     if (cache->n_blocks < 1 || cache->max_blocks < 1) return TRIA_E_INVAL;

@@ -234,6 +234,7 @@ int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, 
     if (row_stride < (int64_t)c->Hq * c->hd) return TRIA_E_INVAL;
     if (q_type != TRIA_Q_F32 && q_type != TRIA_Q_F16 && q_type != TRIA_Q_BF16)
         return TRIA_E_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(q) % (q_type == TRIA_Q_F32 ? 4 : 2) != 0) return TRIA_E_INVAL;
     if (n_tokens == 0) return TRIA_OK;
     const int64_t chunks = (n_tokens + kCalTok - 1) / kCalTok;
     const unsigned S = (unsigned)(chunks < kCalSlots ? chunks : kCalSlots);

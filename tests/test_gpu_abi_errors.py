@@ -15,8 +15,10 @@ DEV = "cuda:0"
 INVAL, UNSUP = tria.TRIA_E_INVAL, tria.TRIA_E_UNSUPPORTED
 
 
-def _p(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+def _p(t, off=0):
+    """Device address of a tensor, moved by off bytes (a misaligned pointer is
+    refused before anything is read through it)."""
+    return ctypes.c_void_p(t.data_ptr() + off) if t is not None else None
 
 
 def _stream():
@@ -39,8 +41,39 @@ def test_contiguous_entry_points_reject_bad_arguments():
     h = ctx.handle
     good = tria.Cache(_p(k), _p(v), _p(pos), n)
     no_k = tria.Cache(None, _p(v), _p(pos), n)
+    k_off8 = tria.Cache(_p(k, 8), _p(v), _p(pos), n)
+    v_off2 = tria.Cache(_p(k), _p(v, 2), _p(pos), n)
+    pos_off2 = tria.Cache(_p(k), _p(v), _p(pos, 2), n)
     s = _stream()
     cases = {
+        "evict k not 16-byte aligned": (
+            lambda: L.tria_evict(h, ctypes.byref(k_off8), n, 100, 4, 16, s), INVAL),
+        "evict v not 16-byte aligned": (
+            lambda: L.tria_evict(h, ctypes.byref(v_off2), n, 100, 4, 16, s), INVAL),
+        "evict pos not 4-byte aligned": (
+            lambda: L.tria_evict(h, ctypes.byref(pos_off2), n, 100, 4, 16, s), INVAL),
+        "noalloc k not 16-byte aligned": (
+            lambda: L.tria_evict_noalloc(h, ctypes.byref(k_off8), n, 100, 4, 16, s), INVAL),
+        "score raw not 16-byte aligned": (
+            lambda: L.tria_score(h, ctypes.byref(good), n, _p(raw, 4), s), INVAL),
+        "score k not 16-byte aligned": (
+            lambda: L.tria_score(h, ctypes.byref(k_off8), n, _p(raw), s), INVAL),
+        "select raw not 16-byte aligned": (
+            lambda: L.tria_select(h, _p(raw, 8), n, 100, 4, 16, _p(keep), None, s), INVAL),
+        "select keep not 4-byte aligned": (
+            lambda: L.tria_select(h, _p(raw), n, 100, 4, 16, _p(keep, 2), None, s), INVAL),
+        "select agg not 4-byte aligned": (
+            lambda: L.tria_select(h, _p(raw), n, 100, 4, 16, _p(keep), _p(out, 2), s), INVAL),
+        "compact keep not 4-byte aligned": (
+            lambda: L.tria_compact(h, ctypes.byref(good), n, _p(keep, 1), 10, s), INVAL),
+        "compact v not 16-byte aligned": (
+            lambda: L.tria_compact(h, ctypes.byref(v_off2), n, _p(keep), 10, s), INVAL),
+        "attention q not 4-byte aligned": (
+            lambda: L.tria_decode_attention(h, ctypes.byref(good), n, _p(q, 2), ctypes.c_float(0.1),
+                                            _p(out), s), INVAL),
+        "attention out not 4-byte aligned": (
+            lambda: L.tria_decode_attention(h, ctypes.byref(good), n, _p(q), ctypes.c_float(0.1),
+                                            _p(out, 1), s), INVAL),
         "evict n > cap": (lambda: L.tria_evict(h, ctypes.byref(good), n + 1, 100, 4, 16, s), INVAL),
         "evict n < 0": (lambda: L.tria_evict(h, ctypes.byref(good), -1, 100, 4, 16, s), INVAL),
         "evict budget < 0": (lambda: L.tria_evict(h, ctypes.byref(good), n, -1, 4, 16, s), INVAL),
@@ -112,6 +145,10 @@ def test_paged_batch_rejects_bad_arguments():
                          _p(bt), bt.shape[1])
     no_bt = tria.PagedCache(_p(pg["k_pool"]), _p(pg["v_pool"]), _p(pg["pos_pool"]),
                             pg["n_blocks"], None, bt.shape[1])
+    k_off = tria.PagedCache(_p(pg["k_pool"], 4), _p(pg["v_pool"]), _p(pg["pos_pool"]),
+                            pg["n_blocks"], _p(bt), bt.shape[1])
+    bt_off = tria.PagedCache(_p(pg["k_pool"]), _p(pg["v_pool"]), _p(pg["pos_pool"]),
+                             pg["n_blocks"], _p(bt, 2), bt.shape[1])
 
     def arr(vals):
         return (ctypes.c_int64 * len(vals))(*vals)
@@ -139,6 +176,12 @@ def test_paged_batch_rejects_bad_arguments():
                              INVAL),
         "null kept_out": (lambda: L.tria_evict_paged_batch(h, ctypes.byref(pc), 3, arr(lens),
                                                            arr([100] * 3), 0, 16, None, s), INVAL),
+        "k_pool not 16-byte aligned": (
+            lambda: L.tria_evict_paged_batch(h, ctypes.byref(k_off), 3, arr(lens), arr([100] * 3),
+                                             0, 16, kept, s), INVAL),
+        "block table not 4-byte aligned": (
+            lambda: L.tria_evict_paged_batch(h, ctypes.byref(bt_off), 3, arr(lens),
+                                             arr([100] * 3), 0, 16, kept, s), INVAL),
     }
     for name, (call, code) in cases.items():
         pu.say("case paged %s" % name)
@@ -152,3 +195,23 @@ def test_paged_batch_rejects_bad_arguments():
     assert got == [200, 300, 400]
     tria.tria_device_status(ctx)
     ctx.close()
+
+
+def test_calibration_rejects_misaligned_queries():
+    """Query rows must start on their element size; a refused add leaves the
+    accumulators and the token count as they were."""
+    hd, Hq = 64, 4
+    cal = tria.TriaCalib(1, Hq, hd)
+    q32 = torch.randn(9, Hq * hd, dtype=torch.float32, device=DEV)
+    q16 = q32.to(torch.float16)
+    L = tria.lib()
+    s = _stream()
+    assert L.tria_calib_add(cal.handle, 0, _p(q32, 2), tria.TRIA_Q_F32, 8, Hq * hd, s) == INVAL
+    assert L.tria_calib_add(cal.handle, 0, _p(q16, 1), tria.TRIA_Q_F16, 8, Hq * hd, s) == INVAL
+    assert cal.tokens(0) == 0
+    # element-aligned but not vector-aligned rows take the element-wise kernel
+    assert L.tria_calib_add(cal.handle, 0, _p(q16, 2), tria.TRIA_Q_F16, 8, Hq * hd, s) == 0
+    assert cal.tokens(0) == 8
+    torch.cuda.synchronize()
+    cal.close()
+
