@@ -48,6 +48,8 @@ constexpr int kSpinLimit = 1 << 18;  // polls (each a memory round trip plus a s
 // Pieces per thread and array; the launch uses 256, 512 or 1024 threads so
 // that a chunk of either array needs at most this many.
 constexpr int kItems = 8;
+// Piece code of an array moved in 4-byte words (HalfMove below).
+constexpr int kWords = 1;
 
 template <int PW>
 struct Piece;
@@ -136,6 +138,146 @@ struct ArrayMove {
     }
 };
 
+// An array whose row width is 2 modulo 4 (q8_0 rows at head_dim 32, 96, 160,
+// 224) has rows on 2-byte boundaries only.  Where its 2-byte pieces would not
+// fit 256-row chunks (rows over 64 bytes), it is moved in aligned 4-byte
+// destination words instead (piece code kWords): each 16-row group of the chunk
+// (contiguous in memory in both layouts) is one byte span, and lane l of the
+// group's wavefront(s) takes the span's words l, l + 64 W, ... (W wavefronts
+// per group).  A word's two halves may belong to two rows (a row boundary in
+// the middle of the word) and come from two source rows; each half is read
+// with the aligned 4-byte load that holds it (one load when both halves lie in
+// one aligned source word), and the word is stored whole when both halves
+// move, else as the one 2-byte half that does.  Every load holds a byte of a
+// moved source row and every store writes only bytes of moved destination rows
+// of this chunk, so neighbouring spans (other chunks, other units) are never
+// written.  Needs all kMaxFlowThreads threads.
+template <int CR>
+struct HalfMove {
+    static constexpr int kGroups = CR / kBlockRows;
+    static constexpr int kWavesPerGroup = (kMaxFlowThreads / 64) / kGroups;
+    static constexpr int kStep = 64 * kWavesPerGroup;  // words between a lane's items
+    static constexpr int kItems = 8;
+    static_assert(kGroups * kWavesPerGroup == kMaxFlowThreads / 64, "whole wavefronts per group");
+    uint32_t lo[kItems], hi[kItems];
+    // per item one byte: 1 half 0 moves, 2 half 1 moves, 4 half 0 is lo's upper
+    // half, 8 half 1 is the upper half (of lo if 16, else of hi)
+    uint64_t sel;
+
+    // Byte offset of this wavefront's span (its group's first row), -1 when no
+    // row of the group moves; the group's first row within the chunk.
+    __device__ __forceinline__ static int64_t span_start(const int64_t* grp, int rb, int* g0) {
+        const int g = (int)(threadIdx.x >> 6) / kWavesPerGroup;
+        *g0 = g * kBlockRows;
+        return grp[g] < 0 ? -1 : grp[g] * rb;
+    }
+    __device__ __forceinline__ static int first_word() {
+        return ((int)(threadIdx.x >> 6) % kWavesPerGroup) * 64 + (int)(threadIdx.x & 63);
+    }
+    __device__ __forceinline__ void load(const uint8_t* base, int rb, const int64_t* src,
+                                         const int64_t* grp) {
+        sel = 0;
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) lo[k] = hi[k] = 0u;
+        int g0;
+        const int64_t G = span_start(grp, rb, &g0);
+        if (G < 0) return;
+        const int span = kBlockRows * rb;
+        // span byte p of half 0 of the lane's first word (p >= -2) as row r and
+        // byte off (p = -2: r = -1, off = rb - 2); later words are 4 kStep bytes on
+        const int p0 = 4 * first_word() - (int)(G & 3);
+        int r = p0 < 0 ? -1 : p0 / rb;
+        int off = p0 - r * rb;
+        const int dr = (4 * kStep) / rb, doff = (4 * kStep) - dr * rb;
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int p = p0 + 4 * kStep * k;
+            if (p >= span) break;
+            const int64_t s0 = r >= 0 ? src[g0 + r] : -1;
+            int r1 = r, off1 = off + 2;
+            if (off1 == rb) {
+                ++r1;
+                off1 = 0;
+            }
+            const int64_t s1 = p + 2 >= span ? -1 : (r1 == r ? s0 : src[g0 + r1]);
+            const int64_t a0 = s0 >= 0 ? s0 * rb + off : -1;  // source bytes, -1: not moved
+            const int64_t a1 = s1 >= 0 ? s1 * rb + off1 : -1;
+            const bool m0 = a0 >= 0, m1 = a1 >= 0;
+            const bool one = m0 && m1 && r1 == r && (a0 & 3) == 0;  // one source word
+            if (m0)
+                lo[k] = __builtin_nontemporal_load(
+                    reinterpret_cast<const uint32_t*>(base + (a0 & ~(int64_t)3)));
+            if (m1 && !one)
+                hi[k] = __builtin_nontemporal_load(
+                    reinterpret_cast<const uint32_t*>(base + (a1 & ~(int64_t)3)));
+            const uint64_t bits = (m0 ? 1u : 0u) | (m1 ? 2u : 0u) | ((a0 & 2) ? 4u : 0u) |
+                                  ((a1 & 2) ? 8u : 0u) | (one ? 16u : 0u);
+            sel |= bits << (8 * k);
+            r += dr;
+            off += doff;
+            if (off >= rb) {
+                off -= rb;
+                ++r;
+            }
+        }
+    }
+    __device__ __forceinline__ void wait() {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            hold(lo[k]);
+            hold(hi[k]);
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* base, int rb, const int64_t* grp) const {
+        int g0;
+        const int64_t G = span_start(grp, rb, &g0);
+        if (G < 0) return;
+        const int64_t w0 = (G & ~(int64_t)3) + 4 * (int64_t)first_word();
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const uint32_t bits = (uint32_t)(sel >> (8 * k)) & 0xffu;
+            if ((bits & 3u) == 0u) continue;
+            const uint32_t h0 = (bits & 4u) ? (lo[k] >> 16) : (lo[k] & 0xffffu);
+            const uint32_t x1 = (bits & 16u) ? lo[k] : hi[k];
+            const uint32_t h1 = (bits & 8u) ? (x1 >> 16) : (x1 & 0xffffu);
+            uint8_t* w = base + w0 + 4 * (int64_t)kStep * k;
+            if ((bits & 3u) == 3u)
+                *reinterpret_cast<uint32_t*>(w) = h0 | (h1 << 16);
+            else if (bits & 1u)
+                *reinterpret_cast<uint16_t*>(w) = (uint16_t)h0;
+            else
+                *reinterpret_cast<uint16_t*>(w + 2) = (uint16_t)h1;
+        }
+    }
+};
+
+// The mover of one array: pieces of PW bytes, or 4-byte words (PW == kWords).
+template <int PW, int CR>
+struct MoverOf { using T = ArrayMove<PW, CR>; };
+template <int CR>
+struct MoverOf<kWords, CR> { using T = HalfMove<CR>; };
+
+template <int PW, int CR>
+__device__ __forceinline__ void move_load(ArrayMove<PW, CR>& m, const uint8_t* base, int rb,
+                                          const int64_t* src, const int64_t*) {
+    m.load(base, rb, src);
+}
+template <int CR>
+__device__ __forceinline__ void move_load(HalfMove<CR>& m, const uint8_t* base, int rb,
+                                          const int64_t* src, const int64_t* grp) {
+    m.load(base, rb, src, grp);
+}
+template <int PW, int CR>
+__device__ __forceinline__ void move_store(const ArrayMove<PW, CR>& m, uint8_t* base, int rb,
+                                           const int64_t* src, const int64_t* dst, const int64_t*) {
+    m.store(base, rb, src, dst);
+}
+template <int CR>
+__device__ __forceinline__ void move_store(const HalfMove<CR>& m, uint8_t* base, int rb,
+                                           const int64_t*, const int64_t*, const int64_t* grp) {
+    m.store(base, rb, grp);
+}
+
 // Destination chunks of CR rows per unit (a multiple of kChunkRows).
 template <int CR>
 __host__ __device__ inline int64_t flow_chunks(int64_t kept) { return (kept + CR - 1) / CR; }
@@ -201,6 +343,9 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
     constexpr int kPerP = CR / kChunkRows;  // prefix-count entries per chunk
     __shared__ int64_t src_row[CR];  // physical source row, -1 if the row stays
     __shared__ int64_t dst_row[CR];
+    constexpr bool kHalf = PK == kWords || PV == kWords;
+    // physical first row of each 16-row group (-1 past the kept rows)
+    __shared__ int64_t grp_row[kHalf ? CR / kBlockRows : 1];
     __shared__ uint32_t first_sh;
     __shared__ TaskPlan tp;
     __shared__ int sorted_v[kMaxSeq];
@@ -254,12 +399,16 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
                 src_row[t] = sr;
                 dst_row[t] = dr;
             }
+            if (kHalf && t < CR / kBlockRows) {
+                const int d = d0 + kBlockRows * t;
+                grp_row[t] = d < kept ? row_index(cv, id, d) : -1;
+            }
             __syncthreads();
-            ArrayMove<PK, CR> mk;
-            ArrayMove<PV, CR> mv;
+            typename MoverOf<PK, CR>::T mk;
+            typename MoverOf<PV, CR>::T mv;
             uint32_t pos = 0;
-            mk.load(cv.k, cv.kb, src_row);
-            mv.load(cv.v, cv.vb, src_row);
+            move_load(mk, cv.k, cv.kb, src_row, grp_row);
+            move_load(mv, cv.v, cv.vb, src_row, grp_row);
             const int64_t ps = t < CR ? src_row[t] : -1;
             if (ps >= 0) pos = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(cv.pos) + ps);
             mk.wait();
@@ -297,8 +446,8 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
             __syncthreads();
 
             // 4. stores
-            mk.store(cv.k, cv.kb, src_row, dst_row);
-            mv.store(cv.v, cv.vb, src_row, dst_row);
+            move_store(mk, cv.k, cv.kb, src_row, dst_row, grp_row);
+            move_store(mv, cv.v, cv.vb, src_row, dst_row, grp_row);
             if (ps >= 0) __builtin_nontemporal_store(pos, reinterpret_cast<uint32_t*>(cv.pos) + dst_row[t]);
             __syncthreads();  // the row tables are rewritten by the next task
         }
@@ -346,7 +495,8 @@ FlowKernel flow_for_v(int pv) {
         case 16: return compact_flow_kernel<PK, 16, CR>;
         case 8: return compact_flow_kernel<PK, 8, CR>;
         case 4: return compact_flow_kernel<PK, 4, CR>;
-        default: return compact_flow_kernel<PK, 2, CR>;
+        case 2: return compact_flow_kernel<PK, 2, CR>;
+        default: return compact_flow_kernel<PK, kWords, CR>;
     }
 }
 
@@ -356,7 +506,8 @@ FlowKernel flow_kernel(int pk, int pv) {
         case 16: return flow_for_v<16, CR>(pv);
         case 8: return flow_for_v<8, CR>(pv);
         case 4: return flow_for_v<4, CR>(pv);
-        default: return flow_for_v<2, CR>(pv);
+        case 2: return flow_for_v<2, CR>(pv);
+        default: return flow_for_v<kWords, CR>(pv);
     }
 }
 
@@ -417,21 +568,45 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
         if (e != hipSuccess) return e;
         pb = pb_scratch;
     }
-    const int pk = piece_width(cv.kb), pv = piece_width(cv.vb);
+    // the piece width of each array; rows of 2-byte pieces that would not fit
+    // 256-row chunks move in 4-byte words
+    auto code = [](int64_t rb) {
+        const int pw = piece_width((int)rb);
+        return pw == 2 && 4 * kChunkRows * (rb / 2) > (int64_t)kMaxFlowThreads * kItems ? kWords
+                                                                                      : pw;
+    };
+    const int pk = code(cv.kb), pv = code(cv.vb);
     // the widest chunk (256, 128 or 64 rows) whose pieces fit kItems per thread
     // of a kMaxFlowThreads workgroup: fewer barriers and flag waits per byte and
-    // more bytes in flight per workgroup
-    const int64_t ppr = cv.kb / pk > cv.vb / pv ? cv.kb / pk : cv.vb / pv;
-    const int64_t room = (int64_t)kMaxFlowThreads * kItems;
-    const int cr = 4 * kChunkRows * ppr <= room ? 4 * kChunkRows
-                 : (2 * kChunkRows * ppr <= room ? 2 * kChunkRows : kChunkRows);
+    // more bytes in flight per workgroup.  In 4-byte words a 16-row group spans
+    // at most 4 rb + 1 words, and its (kMaxFlowThreads / 64) / (rows / 16)
+    // wavefronts take kItems per lane.
+    auto fits = [&](int64_t rows) {
+        for (int a = 0; a < 2; ++a) {
+            const int64_t rb = a ? cv.vb : cv.kb;
+            const int pw = a ? pv : pk;
+            const int64_t waves = (kMaxFlowThreads / 64) / (rows / kBlockRows);
+            if (pw == kWords ? 4 * rb + 1 > (int64_t)kItems * 64 * waves
+                             : rows * (rb / pw) > (int64_t)kMaxFlowThreads * kItems)
+                return false;
+        }
+        return true;
+    };
+    const int cr = fits(4 * kChunkRows) ? 4 * kChunkRows
+                 : (fits(2 * kChunkRows) ? 2 * kChunkRows : kChunkRows);
+    if (!fits(cr)) return hipErrorInvalidValue;
     const FlowKernel k = cr == 4 * kChunkRows   ? flow_kernel<4 * kChunkRows>(pk, pv)
                        : cr == 2 * kChunkRows ? flow_kernel<2 * kChunkRows>(pk, pv)
                                               : flow_kernel<kChunkRows>(pk, pv);
     // threads such that each array's chunk is at most kItems pieces per thread
+    // (all of them for 4-byte words)
+    int64_t ppr = 0;
+    if (pk != kWords) ppr = cv.kb / pk;
+    if (pv != kWords && cv.vb / pv > ppr) ppr = cv.vb / pv;
     const int64_t pieces = (int64_t)cr * ppr;
     int threads = 256;
     while ((int64_t)threads * kItems < pieces) threads *= 2;
+    if (pk == kWords || pv == kWords) threads = kMaxFlowThreads;
     if (threads > kMaxFlowThreads) return hipErrorInvalidValue;
     int64_t chunks = 0, sum_chunks = 0;  // chunks of cr rows: the largest count, the sum
     for (int i = 0; i < b.n_seq; ++i) {

@@ -266,12 +266,17 @@ def test_evict_equals_the_three_stages(L):
 
 
 @pytest.mark.parametrize("pattern", ["alternate", "tail", "head_run", "random", "invalid"])
-def test_compaction_patterns(pattern):
-    """Adversarial keep patterns for the in-place gather, K/V/pos of several row sizes."""
+@pytest.mark.parametrize("hd,n,v_type", [(96, 5000, F16), (160, 4999, Q8), (32, 3001, F16)],
+                         ids=["hd96", "hd160_q8v_odd_cap", "hd32_odd_cap"])
+def test_compaction_patterns(pattern, hd, n, v_type):
+    """Adversarial keep patterns for the in-place gather, K/V/pos of several row sizes.
+    q8_0 rows at these widths (102, 170, 34 bytes) move in aligned 4-byte words; an
+    odd row count per unit puts every other unit's rows on 2-byte offsets."""
     rng = np.random.default_rng(7)
-    L, Hkv, hd, n = 2, 3, 96, 5000
-    wl = variant(WL["tiny_1x1_4k_f16"], name="compact", L=L, Hkv=Hkv, Hq=Hkv, hd=hd, k_type=Q8)
-    kb, vb = synth.row_bytes(Q8, hd), synth.row_bytes(F16, hd)
+    L, Hkv = 2, 3
+    wl = variant(WL["tiny_1x1_4k_f16"], name="compact", L=L, Hkv=Hkv, Hq=Hkv, hd=hd, k_type=Q8,
+                 v_type=v_type)
+    kb, vb = synth.row_bytes(Q8, hd), synth.row_bytes(v_type, hd)
     k = torch.from_numpy(rng.integers(0, 256, size=(L, Hkv, n, kb), dtype=np.uint8))
     v = torch.from_numpy(rng.integers(0, 256, size=(L, Hkv, n, vb), dtype=np.uint8))
     pos = torch.from_numpy(np.broadcast_to(np.arange(n, dtype=np.int32), (L, Hkv, n)).copy())
@@ -283,6 +288,7 @@ def test_compaction_patterns(pattern):
         keep1 = np.concatenate([np.arange(0, 900), np.arange(1000, n, 3)])
     else:
         keep1 = np.sort(rng.choice(n, size=1234, replace=False))
+    pu.say("case compaction %s hd %d n %d v%d" % (pattern, hd, n, v_type))
     K = len(keep1)
     keep = np.broadcast_to(keep1.astype(np.int32), (L, Hkv, K)).copy()
     if pattern == "invalid":
@@ -493,13 +499,15 @@ def test_rows_past_the_maximum_are_refused():
     ctx.close()
 
 
-@pytest.mark.parametrize("k_type", [Q8, F16])
-def test_paged_batch(k_type):
+@pytest.mark.parametrize("k_type,hd,v_type", [(Q8, 128, F16), (F16, 128, F16), (Q8, 96, Q8)],
+                         ids=["q8", "f16", "q8_hd96_q8v"])
+def test_paged_batch(k_type, hd, v_type):
     """Paged cache, 16-row blocks in shuffled physical order, several sequences of
     different lengths (one with nothing to evict) in one batched pass; every
-    sequence checked against the oracle on its logical rows."""
-    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged", L=7, Hkv=2, Hq=8, hd=128,
-                 k_type=k_type)
+    sequence checked against the oracle on its logical rows (q8_0 rows of 102 bytes
+    move in aligned 4-byte words)."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged", L=7, Hkv=2, Hq=8, hd=hd,
+                 k_type=k_type, v_type=v_type)
     lens = [3000, 517, 1200, 64, 2048]
     budgets = [900, 150, 1200, 70, 600]  # seq 3: budget >= n keeps everything
     S, W = 0, 128
