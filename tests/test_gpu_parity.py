@@ -314,6 +314,44 @@ def test_compaction_patterns(pattern, hd, n, v_type):
     ctx.close()
 
 
+def test_two_contexts_on_two_streams():
+    """Two contexts, each on its own stream, run passes over their own caches at the
+    same time (one ordered, one hole-filling; their persistent compaction grids then
+    share the device): both leave the caches a pass alone on one stream leaves."""
+    wl = variant(WL["qwen3_8b_full_32k_q8"], name="streams", L=6)
+    n, B, S, W = wl.n, wl.budget, wl.sink, wl.window
+    caches, ctxs, want = [], [], []
+    for i, mode in enumerate((tria.TRIA_COMPACT_ORDERED, tria.TRIA_COMPACT_HOLE_FILL)):
+        stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 40 + i)
+        c = list(synth.gen_cache(wl.L, wl.Hkv, wl.hd, n, n, wl.k_type, wl.v_type, 40 + i, DEV))
+        ctx = pu.make_ctx(wl, stats)
+        tria.tria_set_compaction(ctx, mode)
+        ref = [t.clone() for t in c]
+        assert tria.tria_evict(ctx, *ref, n, B, S, W) == B
+        torch.cuda.synchronize()
+        caches.append(c)
+        ctxs.append(ctx)
+        want.append([t[:, :, :B].clone() for t in ref])
+        del ref
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    work = [[t.clone() for t in c] for c in caches]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        pu.say("case two streams rep %d" % rep)
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                for t, t0 in zip(work[i], caches[i]):
+                    t.copy_(t0)
+                assert tria.tria_evict(ctxs[i], *work[i], n, B, S, W, streams[i]) == B
+        torch.cuda.synchronize()
+        for i in (0, 1):
+            tria.tria_device_status(ctxs[i])
+            for t, w, name in zip(work[i], want[i], ("k", "v", "pos")):
+                assert torch.equal(t[:, :, :B], w), (i, rep, name)
+    for ctx in ctxs:
+        ctx.close()
+
+
 @pytest.mark.parametrize("pattern", ["selected", "alternate", "tail", "random"])
 def test_serial_compaction_reference(pattern):
     """The ordered compaction run by one workgroup (every chunk task in order, so no
