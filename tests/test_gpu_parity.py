@@ -583,6 +583,55 @@ def test_paged_batch(k_type, hd, v_type):
     ctx.close()
 
 
+def test_paged_batch_of_the_most_sequences():
+    """The largest batch one call takes (TRIA_MAX_SEQ sequences), with an empty
+    sequence, a one-row sequence and one whose budget covers it among seeded ragged
+    lengths; every sequence checked against the oracle on its logical rows."""
+    rng = np.random.default_rng(64)
+    n_seq = tria.TRIA_MAX_SEQ
+    lens = [int(x) for x in rng.integers(2, 700, size=n_seq)]
+    lens[5], lens[17] = 0, 1
+    budgets = [int(0.3 * n) for n in lens]
+    budgets[40] = lens[40] + 3  # keeps everything
+    S, W = 2, 32
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="paged64", L=2, Hkv=2, Hq=6, hd=64,
+                 k_type=Q8, v_type=F16)
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 64)
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 9)
+    before = [(synth.paged_rows(pg["k_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["v_pool"], pg["block_table"][s], n).numpy().copy(),
+               synth.paged_rows(pg["pos_pool"], pg["block_table"][s], n).numpy().copy())
+              for s, n in enumerate(lens)]
+    pu.say("case paged batch of %d sequences" % n_seq)
+    ctx = pu.make_ctx(wl, stats)
+    dev = {k: pg[k].to(DEV) for k in ("k_pool", "v_pool", "pos_pool", "block_table")}
+    kept = tria.tria_evict_paged_batch(ctx, dev["k_pool"], dev["v_pool"], dev["pos_pool"],
+                                       dev["block_table"], lens, budgets, S, W)
+    tria.tria_device_status(ctx)
+    bt = dev["block_table"].cpu()
+    for s, n in enumerate(lens):
+        K = oracle.kept_count(n, budgets[s], S, W)
+        assert kept[s] == K, s
+        if n == 0:
+            continue
+        k0, v0, p0 = before[s]
+        o = oracle.evict(wl.k_type, wl.v_type, wl.L, wl.Hkv, wl.Hq, wl.hd, wl.theta,
+                         list(wl.offsets), k0.copy(), v0.copy(), p0.copy(), n, budgets[s], S, W,
+                         *stats, compact=False)
+        ka = synth.paged_rows(dev["k_pool"].cpu(), bt[s], n).numpy()
+        va = synth.paged_rows(dev["v_pool"].cpu(), bt[s], n).numpy()
+        pa = synth.paged_rows(dev["pos_pool"].cpu(), bt[s], n).numpy()
+        for l in range(wl.L):
+            for h in range(wl.Hkv):
+                keep = pa[l, h, :K]
+                where = "paged64 seq %d unit (%d,%d)" % (s, l, h)
+                pu.check_kept(keep, o["keep_idx"][l, h], o["agg"][l, h], n, budgets[s], S, W,
+                              where)
+                pu.check_gather(k0[l, h], ka[l, h], keep, K, where + " K")
+                pu.check_gather(v0[l, h], va[l, h], keep, K, where + " V")
+    ctx.close()
+
+
 def _pre_rows_of(post_pos, pre_pos):
     """Row of the pre-pass cache that holds each position (positions are unique within
     a unit): [..., K] positions, [..., n] pre-pass positions -> [..., K] rows."""
