@@ -85,6 +85,9 @@ SHAPES = [
     (192, 2, 10, F16, F16, 777, 200, 1, 50),
     (128, 1, 12, F16, Q8, 2049, 512, 0, 128),
     (64, 1, 20, F16, F16, 1300, 333, 3, 100),
+    # the largest GQA ratio a model may have (64 query heads per KV head)
+    (128, 1, 64, Q8, F16, 700, 200, 2, 64),
+    (256, 2, 128, F16, F16, 500, 100, 0, 32),
 ]
 
 
