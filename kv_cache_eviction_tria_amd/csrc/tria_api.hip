@@ -56,7 +56,7 @@ struct tria_ctx {
     size_t part_bytes = 0;
     int32_t* pb = nullptr;  // chunk prefix counts (selector -> compaction)
     size_t pb_bytes = 0;
-    CompactState cst = {nullptr, 0, 0, nullptr, nullptr, 0};
+    CompactState cst = {nullptr, 0, nullptr, nullptr, 0};
     size_t flag_bytes = 0;
     // shared keep sets (tria_set_keep_mode): norms, group scores, kept rows
     int keep_mode = TRIA_KEEP_PER_UNIT;
@@ -422,7 +422,7 @@ void log_gate_once(const tria_model_desc* d, const char* why) {
 //   [0, kNaFlagBytes)                compaction flags (only ever written with
 //                                    compaction epochs, so a stale word never
 //                                    equals a later epoch)
-//   [kNaFlagBytes, + 256)            the compaction's task counter
+//   [kNaFlagBytes, + 256)            the compaction's task counter and flag epoch
 //   [kNaDataOff, kNoAllocScratchBytes) coefficient tables of every unit, then
 //                                    one group of layers' raw scores, moment
 //                                    partials, kept indices, chunk prefix
@@ -433,7 +433,6 @@ constexpr int kNaMaxDevices = 64;
 
 struct NoAllocDevice {
     uint8_t* ptr = nullptr;  // device address of `scratch` on this GPU
-    uint32_t epoch = 0;      // last compaction epoch stamped into its flags
 };
 std::mutex g_na_mu;
 NoAllocDevice g_na[kNaMaxDevices];
@@ -531,8 +530,7 @@ int64_t tria_evict_noalloc(tria_ctx* ctx, const tria_cache* cache, int64_t n_tok
     const int units = ctx->L * ctx->Hkv;
     hipError_t e = launch_prep(cv, b, units, ctx->k_type, ctx->G, ctx->hd, ctx->q_re, ctx->q_im,
                                ctx->w, ctx->omega, ctx->m_re, ctx->m_im, coef, stream);
-    std::lock_guard<std::mutex> lk(g_na_mu);  // the device's epoch counter
-    CompactState cs = {flags, (int64_t)(kNaFlagBytes / 4), g_na[dev].epoch, ticket, ctx->cst.err,
+    CompactState cs = {flags, (int64_t)(kNaFlagBytes / 4), ticket, ctx->cst.err,
                        ctx->cst.max_groups};
     for (int l0 = 0; l0 < ctx->L && e == hipSuccess; l0 += lg) {
         const int lc = ctx->L - l0 < lg ? ctx->L - l0 : lg;
@@ -550,7 +548,6 @@ int64_t tria_evict_noalloc(tria_ctx* ctx, const tria_cache* cache, int64_t n_tok
         else if (e == hipSuccess)
             e = launch_compact(sv, gb, gu, keep, pb, nullptr, cs, ticket, stream);
     }
-    g_na[dev].epoch = cs.epoch;
     if (e != hipSuccess) return hip_fail(ctx, e);
     return p.kept;
 }
@@ -711,8 +708,8 @@ int tria_load_stats(tria_ctx** out, const tria_model_desc* d, const float* q_re,
     // error word of the compaction's bounded waits, and its task ticket
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.err), sizeof(int));
     if (e == hipSuccess) e = hipMemset(ctx->cst.err, 0, sizeof(int));
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), sizeof(uint32_t));
-    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&ctx->cst.ticket), 2 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(ctx->cst.ticket, 0, 2 * sizeof(uint32_t));
     if (e != hipSuccess) {
         const int rc = e == hipErrorOutOfMemory ? TRIA_E_NOMEM : TRIA_E_HIP;
         tria_free(ctx);

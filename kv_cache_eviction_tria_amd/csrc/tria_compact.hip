@@ -338,8 +338,8 @@ __device__ void build_plan(const Batch& b, TaskPlan& tp, int* sorted_v) {
 template <int PK, int PV, int CR>
 __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
     CacheView cv, Batch b, const int32_t* __restrict__ keep, const int32_t* __restrict__ pb,
-    uint32_t* flags, int max_chunks, uint32_t epoch, uint32_t n_tasks, int ticket_tasks,
-    uint32_t* ticket, int* err) {
+    uint32_t* flags, int max_chunks, uint32_t n_tasks, int ticket_tasks, uint32_t* ticket,
+    int* err) {
     constexpr int kPerP = CR / kChunkRows;  // prefix-count entries per chunk
     __shared__ int64_t src_row[CR];  // physical source row, -1 if the row stays
     __shared__ int64_t dst_row[CR];
@@ -351,6 +351,7 @@ __global__ __launch_bounds__(kMaxFlowThreads) void compact_flow_kernel(
     __shared__ int sorted_v[kMaxSeq];
     const int t = threadIdx.x;
     const int per_seq = cv.L * cv.Hkv;
+    const uint32_t epoch = uniform(ticket[1]);  // set by the kernel before this one
     build_plan<CR>(b, tp, sorted_v);
     while (true) {
         if (t == 0) first_sh = atomicAdd(ticket, (uint32_t)ticket_tasks);
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(256) void chunk_bounds_kernel(CacheView cv, Batch b
                                                            int32_t* __restrict__ pb, int n_units,
                                                            int max_bounds, uint32_t* ticket) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i == 0) *ticket = 0;  // for the compaction that follows on this stream
+    if (i == 0) reset_ticket(ticket);  // for the compaction that follows on this stream
     if (i >= (int64_t)n_units * max_bounds) return;
     const int u = (int)(i / max_bounds), e = (int)(i - (int64_t)u * max_bounds);
     const UnitId id = unit_id(cv, u);
@@ -487,7 +488,7 @@ int piece_width(int rb) {
 }
 
 using FlowKernel = void (*)(CacheView, Batch, const int32_t*, const int32_t*, uint32_t*, int,
-                            uint32_t, uint32_t, int, uint32_t*, int*);
+                            uint32_t, int, uint32_t*, int*);
 
 template <int PK, int CR>
 FlowKernel flow_for_v(int pv) {
@@ -626,9 +627,8 @@ hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, cons
     const int tt = ticket_size(tasks, grid);
     const int64_t need = (tasks + tt - 1) / tt;
     if (need < grid) grid = (int)need;
-    st.epoch = st.epoch + 1 == 0 ? 1 : st.epoch + 1;  // 0 is the flags' initial value
     hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, s, cv, b, keep, pb, st.flags,
-                       (int)chunks, st.epoch, (uint32_t)tasks, tt, ticket, st.err);
+                       (int)chunks, (uint32_t)tasks, tt, ticket, st.err);
     return hipGetLastError();
 }
 

@@ -281,15 +281,27 @@ hipError_t launch_score(const CacheView& cv, const Batch& b, int n_units, int k_
                         int hd, const int32_t* coef, float* raw, PartRec* part, hipStream_t s);
 // Compaction state owned by a context: per-(unit, chunk) flags (zeroed once
 // when allocated, then stamped with a new epoch by every launch), the task
-// ticket counter and an error word set by a workgroup that gave up waiting.
+// counter and epoch words, and an error word set by a workgroup that gave up
+// waiting.
 struct CompactState {
     uint32_t* flags;
     int64_t flag_words;
-    uint32_t epoch;
-    uint32_t* ticket;  // task counter, reset by the kernel before the compaction
+    uint32_t* ticket;  // [0] task counter, [1] flag epoch (see reset_ticket)
     int* err;
     int max_groups;    // > 0: at most this many workgroups (1: every task in order)
 };
+
+// Run by one thread of the kernel that precedes a compaction on its stream
+// (the selector, or the prefix-count kernel): the task counter restarts and
+// the epoch the compaction stamps its flags with advances (0, the flags'
+// initial value, is skipped).  The epoch lives on the device, not in a kernel
+// argument, so that a captured graph replayed many times still gives every
+// compaction a new epoch and stale flags of an earlier replay never match.
+__device__ __forceinline__ void reset_ticket(uint32_t* ticket) {
+    ticket[0] = 0u;
+    const uint32_t e = ticket[1] + 1u;
+    ticket[1] = e ? e : 1u;
+}
 // pb: the selector's chunk prefix counts for these units, or nullptr to
 // derive them from keep (caller-provided kept indices).
 hipError_t launch_compact(const CacheView& cv, const Batch& b, int n_units, const int32_t* keep,

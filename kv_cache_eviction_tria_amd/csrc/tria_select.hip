@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(kSe
     const PartRec* __restrict__ part, int32_t* __restrict__ keep, float* __restrict__ agg_out,
     uint32_t* __restrict__ key_scratch, int32_t* __restrict__ chunk_pb, uint32_t* ticket) {
     constexpr bool kRegKeys = kBinsInRegs<RPT>;
-    // the compaction that follows on this stream takes its tasks from *ticket
-    if (ticket && blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
+    // the compaction that follows on this stream takes its tasks from ticket[0]
+    if (ticket && blockIdx.x == 0 && threadIdx.x == 0) reset_ticket(ticket);
     const int u = blockIdx.x;
     const int seq = u / units_per_seq;
     const int uu = u - seq * units_per_seq;

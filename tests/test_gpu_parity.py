@@ -317,6 +317,41 @@ def test_compaction_patterns(pattern, hd, n, v_type):
     ctx.close()
 
 
+@pytest.mark.parametrize("entry", ["evict", "noalloc"])
+def test_captured_pass_replays(entry):
+    """A whole pass captured in a HIP graph (after one eager call, so that nothing is
+    allocated while capturing) and replayed several times, the cache restored by eager
+    copies between replays: every replay leaves the eager pass's cache.  The epoch the
+    compaction stamps its flags with advances on the device, so a replay never takes
+    the flags of the replay before it for its own."""
+    wl = variant(WL["qwen3_8b_full_32k_q8"], name="graph", L=4)
+    n, B, S, W = wl.n, wl.budget, wl.sink, wl.window
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 31)
+    k, v, pos = synth.gen_cache(wl.L, wl.Hkv, wl.hd, n, n, wl.k_type, wl.v_type, 31, DEV)
+    k0, v0, p0 = k.clone(), v.clone(), pos.clone()
+    ctx = pu.make_ctx(wl, stats)
+    fn = tria.tria_evict if entry == "evict" else tria.tria_evict_noalloc
+    assert fn(ctx, k, v, pos, n, B, S, W) == B
+    torch.cuda.synchronize()
+    want = [t[:, :, :B].clone() for t in (k, v, pos)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(ctx, k, v, pos, n, B, S, W)
+    for rep in range(4):
+        pu.say("case graph %s replay %d" % (entry, rep))
+        k.copy_(k0)
+        v.copy_(v0)
+        pos.copy_(p0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        tria.tria_device_status(ctx)
+        for t, w, name in zip((k, v, pos), want, ("k", "v", "pos")):
+            assert torch.equal(t[:, :, :B], w), (entry, rep, name)
+    del g
+    ctx.close()
+
+
 def test_two_contexts_on_two_streams():
     """Two contexts, each on its own stream, run passes over their own caches at the
     same time (one ordered, one hole-filling; their persistent compaction grids then
