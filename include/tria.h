@@ -30,14 +30,14 @@
  * - Key rows are stored already rotated (RoPE applied, rotate-half layout:
  *   pair f is (x[f], x[f + head_dim/2])).  Row n-1 of every unit must hold the
  *   newest token when a pass starts (its position is the phase reference).
- * - A tria_evict or tria_evict_noalloc pass may be captured in a HIP graph and
- *   the graph replayed any number of times on one stream: the pass enqueues
- *   kernels only (no copy, memset or host wait), and the state one launch hands
- *   the next (task counter, compaction epoch) lives on the device.  Capture
- *   tria_evict after an eager call of the same or a larger shape on the
- *   context, so that it does not allocate while capturing; tria_evict_noalloc
- *   never allocates.  Replays use the shapes, budgets and pointers of the
- *   capture.
+ * - A tria_evict, tria_evict_noalloc or tria_evict_paged_batch pass may be
+ *   captured in a HIP graph and the graph replayed any number of times on one
+ *   stream: the pass enqueues kernels only (no copy, memset or host wait), and
+ *   the state one launch hands the next (task counter, compaction epoch) lives
+ *   on the device.  Capture tria_evict or tria_evict_paged_batch after an eager
+ *   call of the same or a larger shape on the context, so that it does not
+ *   allocate while capturing; tria_evict_noalloc never allocates.  Replays use
+ *   the shapes, budgets and pointers of the capture.
  *
  * Layouts
  * -------

@@ -352,6 +352,48 @@ def test_captured_pass_replays(entry):
     ctx.close()
 
 
+def test_captured_paged_batch_replays():
+    """A batched pass over a paged cache captured in a HIP graph after one eager call
+    and replayed with the pools restored between replays: every replay leaves the
+    eager pass's pools (in both compaction modes)."""
+    wl = variant(WL["paged16_qwen3_8b_q8"], name="graph_paged", L=4, Hkv=4, Hq=16, hd=128)
+    lens = [4000, 1500, 2600, 700]
+    budgets = [1200, 500, 800, 700]
+    stats = synth.gen_stats(wl.L, wl.Hq, wl.hd, 12)
+    pg = synth.gen_paged(wl.L, wl.Hkv, wl.hd, wl.k_type, wl.v_type, lens, 12, DEV)
+    names = ("k_pool", "v_pool", "pos_pool")
+    pristine = {x: pg[x].clone() for x in names}
+    for mode in (tria.TRIA_COMPACT_ORDERED, tria.TRIA_COMPACT_HOLE_FILL):
+        ctx = pu.make_ctx(wl, stats)
+        tria.tria_set_compaction(ctx, mode)
+        for x in names:
+            pg[x].copy_(pristine[x])
+        args = (ctx, pg["k_pool"], pg["v_pool"], pg["pos_pool"], pg["block_table"], lens, budgets,
+                wl.sink, wl.window)
+        kept = [tria.tria_kept_count(n, bgt, wl.sink, wl.window) for n, bgt in zip(lens, budgets)]
+        assert tria.tria_evict_paged_batch(*args) == kept
+        torch.cuda.synchronize()
+        want = {x: pg[x].clone() for x in names}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            tria.tria_evict_paged_batch(*args)
+        for rep in range(3):
+            pu.say("case graph paged mode %d replay %d" % (mode, rep))
+            for x in names:
+                pg[x].copy_(pristine[x])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            tria.tria_device_status(ctx)
+            for s, n in enumerate(lens):
+                for x in names:
+                    got = synth.paged_rows(pg[x], pg["block_table"][s], kept[s])
+                    exp = synth.paged_rows(want[x], pg["block_table"][s], kept[s])
+                    assert torch.equal(got, exp), (mode, rep, s, x)
+        del g
+        ctx.close()
+
+
 def test_two_contexts_on_two_streams():
     """Two contexts, each on its own stream, run passes over their own caches at the
     same time (one ordered, one hole-filling; their persistent compaction grids then
