@@ -4,8 +4,7 @@
 One step = one call of tria_evict (score -> aggregate/select -> in-place
 compaction of every layer and KV head) over a synthetic cache resident in
 HBM, timed with HIP events recorded on the caller's stream around the call
-(the library's second stream joins that stream before the call returns).
-Between steps the cache is restored from a pristine device copy and the
+(every kernel of the pass runs on that stream).  Between steps the cache is restored from a pristine device copy and the
 256 MB Infinity Cache is flushed by reading 512 MB of another buffer; neither
 is timed.  The read leaves the Infinity Cache holding clean lines of that
 buffer, as after decode steps that only read the cache.  (Writing the 512 MB
@@ -19,7 +18,10 @@ run without them (the pass time with them is reported beside); the kernel with
 the largest total time is reported against the HBM roofline with its
 algorithmic bytes:  score = every cached K row read once; compaction = every
 moved row (keep_idx[d] != d) read and written (K + V + pos).  A sequential
-breakdown (the three stages one after another) is reported beside it.
+breakdown (the three stages one after another) is reported beside it, and,
+after the steps, a plain device-to-device copy of 1 GiB (`copy_reference`):
+the bandwidth a kernel that reads and writes every byte once reaches on the
+same GPU in the same run.
 
 Default workload: the full Qwen3-8B-shaped cache at 32K context (36 layers x
 8 KV / 32 query heads, head_dim 128, q8_0 K / fp16 V, budget 25%, window 512).
@@ -57,6 +59,9 @@ def parse():
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="between steps, read (default) or write 512 MB to evict the Infinity "
                          "Cache, or leave it as the restore left it")
+    ap.add_argument("--copy-reference-bytes", type=int, default=1 << 30,
+                    help="after the timed steps, time a plain device-to-device copy of this "
+                         "many bytes as the reference a data-moving kernel can reach (0: skip)")
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="run one plain streaming kernel (uint8 xor) over this many bytes before "
                          "the timed steps, as the byte reference for profiler counters")
@@ -143,6 +148,35 @@ def calibrate(nbytes):
 
 def log(msg):
     print("# " + msg, file=sys.stderr, flush=True)
+
+
+def copy_reference(nbytes, reps=10):
+    """A plain device-to-device copy (torch's copy_ of one uint8 buffer into another)
+    of nbytes, median of reps, untimed relative to the pass: the bandwidth a kernel
+    that reads and writes every byte once reaches on this GPU, counted like the
+    pass's algorithmic bytes (bytes read + bytes written)."""
+    if nbytes <= 0:
+        return None
+    import numpy as np
+    import torch
+    src = torch.full((nbytes,), 3, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for i in range(reps + 2):
+        torch.cuda.synchronize()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"what": "torch copy_ of one device buffer into another", "bytes": nbytes, "ms": ms,
+            "GB_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
 
 
 def dtype_of(wl):
@@ -333,6 +367,7 @@ def bench_contiguous(args, wl):
         "cpu_baseline": cpu,
     }
     ctx.close()
+    out["copy_reference"] = copy_reference(args.copy_reference_bytes)
     return out
 
 
@@ -506,6 +541,7 @@ def bench_paged(args, wl):
         "cpu_baseline": cpu,
     }
     ctx.close()
+    out["copy_reference"] = copy_reference(args.copy_reference_bytes)
     return out
 
 
