@@ -389,6 +389,17 @@ int tria_calib_create(tria_calib **out, int32_t n_layers, int32_t n_q_heads, int
 int tria_calib_add(tria_calib *c, int32_t layer, const void *q, int32_t q_type, int64_t n_tokens,
                    int64_t row_stride, hipStream_t stream);
 
+/* tria_calib_add for n_layers consecutive layers layer0 .. layer0 + n_layers - 1
+ * at once (one kernel launch for all of them; per-layer launches of a few tens
+ * of MB are dominated by their start and tail): layer layer0 + i's rows start
+ * at element i * layer_stride of q (layer_stride >= n_tokens * row_stride when
+ * n_layers > 1, so that layers do not overlap).  Each layer's sums are formed
+ * exactly as by tria_calib_add, so the statistics are the same bit for bit.
+ * 1 <= n_layers <= n_layers of the object - layer0. */
+int tria_calib_add_layers(tria_calib *c, int32_t layer0, int32_t n_layers, const void *q,
+                          int32_t q_type, int64_t n_tokens, int64_t row_stride,
+                          int64_t layer_stride, hipStream_t stream);
+
 /* Tokens added so far to a layer (host count), or an error code. */
 int64_t tria_calib_tokens(const tria_calib *c, int32_t layer);
 

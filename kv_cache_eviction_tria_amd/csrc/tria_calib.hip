@@ -86,8 +86,10 @@ constexpr int kCalWaves = kCalThreads / 64;
 template <typename QT>
 __global__ __launch_bounds__(kCalThreads) void calib_partial4_kernel(
     const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
-    double* __restrict__ slot) {
+    double* __restrict__ slot, int64_t q_layer, int64_t slot_layer) {
     __shared__ double sums[kCalWaves][12][64];
+    q += (int64_t)blockIdx.z * q_layer;  // layer z of the call
+    slot += (int64_t)blockIdx.z * slot_layer;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p0 = blockIdx.x * 256 + 4 * lane;
     const bool in = p0 < HF;
@@ -132,7 +134,9 @@ __global__ __launch_bounds__(kCalThreads) void calib_partial4_kernel(
 template <typename QT>
 __global__ __launch_bounds__(kCalThreads) void calib_partial_kernel(
     const QT* __restrict__ q, int64_t T, int64_t stride, int F, int hd, int HF,
-    double* __restrict__ slot) {
+    double* __restrict__ slot, int64_t q_layer, int64_t slot_layer) {
+    q += (int64_t)blockIdx.z * q_layer;  // layer z of the call
+    slot += (int64_t)blockIdx.z * slot_layer;
     const int i = blockIdx.x * kCalThreads + threadIdx.x;
     if (i >= HF) return;
     const int h = i / F, f = i - h * F;
@@ -228,40 +232,54 @@ void tria_calib_free(tria_calib* c) {
     delete c;
 }
 
-int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, int64_t n_tokens,
-                   int64_t row_stride, hipStream_t stream) {
-    if (!c || !q || layer < 0 || layer >= c->L || n_tokens < 0) return TRIA_E_INVAL;
+int tria_calib_add_layers(tria_calib* c, int32_t layer0, int32_t n_layers, const void* q,
+                          int32_t q_type, int64_t n_tokens, int64_t row_stride,
+                          int64_t layer_stride, hipStream_t stream) {
+    if (!c || !q || layer0 < 0 || n_layers < 1 || n_layers > c->L - layer0 || n_tokens < 0)
+        return TRIA_E_INVAL;
     if (row_stride < (int64_t)c->Hq * c->hd) return TRIA_E_INVAL;
+    if (n_layers > 1 && layer_stride < n_tokens * row_stride) return TRIA_E_INVAL;
+    if (n_layers > 65535) return TRIA_E_UNSUPPORTED;
     if (q_type != TRIA_Q_F32 && q_type != TRIA_Q_F16 && q_type != TRIA_Q_BF16)
         return TRIA_E_UNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(q) % (q_type == TRIA_Q_F32 ? 4 : 2) != 0) return TRIA_E_INVAL;
     if (n_tokens == 0) return TRIA_OK;
     const int64_t chunks = (n_tokens + kCalTok - 1) / kCalTok;
     const unsigned S = (unsigned)(chunks < kCalSlots ? chunks : kCalSlots);
-    double* slot = c->acc + (int64_t)layer * kCalSlots * c->HF * 3;
+    double* slot = c->acc + (int64_t)layer0 * kCalSlots * c->HF * 3;
+    const int64_t slot_layer = (int64_t)kCalSlots * c->HF * 3;
+    const int64_t q_layer = n_layers > 1 ? layer_stride : 0;
     const bool vec = c->F % 4 == 0;
-    // 16-byte (8-byte) loads need the rows aligned: the base and the stride
+    // 16-byte (8-byte) loads need the rows aligned: the base and both strides
     const size_t esz = q_type == TRIA_Q_F32 ? 4 : 2;
-    const bool aligned = (reinterpret_cast<uintptr_t>(q) % (4 * esz)) == 0 && row_stride % 4 == 0;
-    // vector path: 256 pairs per block; scalar path: one pair per thread
+    const bool aligned = (reinterpret_cast<uintptr_t>(q) % (4 * esz)) == 0 && row_stride % 4 == 0 &&
+                         q_layer % 4 == 0;
+    // vector path: 256 pairs per block; scalar path: one pair per thread; one
+    // grid layer per query layer
     const dim3 grid(vec && aligned ? (unsigned)((c->HF + 255) / 256)
-                                   : (unsigned)((c->HF + kCalThreads - 1) / kCalThreads), S);
+                                   : (unsigned)((c->HF + kCalThreads - 1) / kCalThreads),
+                    S, (unsigned)n_layers);
     if (q_type == TRIA_Q_F32) {
         auto k = vec && aligned ? calib_partial4_kernel<float> : calib_partial_kernel<float>;
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const float*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot, q_layer, slot_layer);
     } else if (q_type == TRIA_Q_F16) {
         auto k = vec && aligned ? calib_partial4_kernel<_Float16> : calib_partial_kernel<_Float16>;
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const _Float16*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot, q_layer, slot_layer);
     } else {
         auto k = vec && aligned ? calib_partial4_kernel<uint16_t> : calib_partial_kernel<uint16_t>;
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const uint16_t*>(q),
-                           n_tokens, row_stride, c->F, c->hd, c->HF, slot);
+                           n_tokens, row_stride, c->F, c->hd, c->HF, slot, q_layer, slot_layer);
     }
     if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;
-    c->count[layer] += n_tokens;
+    for (int i = 0; i < n_layers; ++i) c->count[layer0 + i] += n_tokens;
     return TRIA_OK;
+}
+
+int tria_calib_add(tria_calib* c, int32_t layer, const void* q, int32_t q_type, int64_t n_tokens,
+                   int64_t row_stride, hipStream_t stream) {
+    return tria_calib_add_layers(c, layer, 1, q, q_type, n_tokens, row_stride, 0, stream);
 }
 
 int64_t tria_calib_tokens(const tria_calib* c, int32_t layer) {

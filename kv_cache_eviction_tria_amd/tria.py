@@ -132,6 +132,8 @@ def lib():
             L.tria_calib_create.argtypes = [ctypes.POINTER(vp), i32, i32, i32]
             L.tria_calib_add.restype = ctypes.c_int
             L.tria_calib_add.argtypes = [vp, i32, vp, i32, i64, i64, vp]
+            L.tria_calib_add_layers.restype = ctypes.c_int
+            L.tria_calib_add_layers.argtypes = [vp, i32, i32, vp, i32, i64, i64, i64, vp]
             L.tria_calib_tokens.restype = i64
             L.tria_calib_tokens.argtypes = [vp, i32]
             L.tria_calib_finish.restype = ctypes.c_int
@@ -399,6 +401,18 @@ class TriaCalib:
         _check(lib().tria_calib_add(self.handle, int(layer), ctypes.c_void_p(q.data_ptr()),
                                     _Q_TYPES[q.dtype], q.shape[0], q.stride(0), _stream(stream)),
                "tria_calib_add")
+
+    def add_layers(self, layer0: int, q, stream=None) -> None:
+        """q: device [n_layers, n_tokens, n_q_heads * head_dim (or more)], fp32/fp16/bf16,
+        layers layer0 .. layer0 + n_layers - 1 in one launch."""
+        if not isinstance(q, torch.Tensor) or not q.is_cuda or q.dim() != 3:
+            raise TypeError("q must be a 3-D CUDA tensor")
+        if q.dtype not in _Q_TYPES or q.stride(2) != 1:
+            raise TypeError("q must be fp32/fp16/bf16 with unit stride along a row")
+        _check(lib().tria_calib_add_layers(self.handle, int(layer0), q.shape[0],
+                                           ctypes.c_void_p(q.data_ptr()), _Q_TYPES[q.dtype],
+                                           q.shape[1], q.stride(1), q.stride(0),
+                                           _stream(stream)), "tria_calib_add_layers")
 
     def tokens(self, layer: int) -> int:
         return int(_check(lib().tria_calib_tokens(self.handle, int(layer)), "tria_calib_tokens"))

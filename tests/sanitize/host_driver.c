@@ -67,6 +67,11 @@ int main(void)
     acc += tria_set_compaction_workgroups(NULL, 0) + tria_device_status(NULL);
     acc += tria_timing_enable(NULL, 1) + tria_timing_read(NULL, NULL, NULL);
     acc += tria_last_hip_error(NULL);
+    acc += tria_calib_create(NULL, 1, 1, 2);
+    acc += tria_calib_add(NULL, 0, NULL, 0, 0, 0, 0);
+    acc += tria_calib_add_layers(NULL, 0, 1, NULL, 0, 0, 0, 0, 0);
+    acc += tria_calib_tokens(NULL, 0) + tria_calib_finish(NULL, NULL, NULL, NULL, NULL, 0);
+    tria_calib_free(NULL);
     tria_free(NULL);
     /* the eligibility gate and descriptor checks (all refused on the host) */
     static float stats[4096];

@@ -215,3 +215,33 @@ def test_calibration_rejects_misaligned_queries():
     torch.cuda.synchronize()
     cal.close()
 
+
+
+def test_calibration_add_layers_refusals():
+    """Layers past the object, no layers, and overlapping layers are refused and
+    leave every token count as it was."""
+    hd, Hq, L, T = 64, 4, 3, 8
+    cal = tria.TriaCalib(L, Hq, hd)
+    q = torch.randn(L, T, Hq * hd, dtype=torch.float32, device=DEV)
+    lib = tria.lib()
+    s = _stream()
+    row, lay = Hq * hd, T * Hq * hd
+    assert lib.tria_calib_add_layers(cal.handle, 1, L, _p(q, 0), tria.TRIA_Q_F32, T, row, lay,
+                                     s) == INVAL
+    assert lib.tria_calib_add_layers(cal.handle, -1, 2, _p(q, 0), tria.TRIA_Q_F32, T, row, lay,
+                                     s) == INVAL
+    assert lib.tria_calib_add_layers(cal.handle, 0, 0, _p(q, 0), tria.TRIA_Q_F32, T, row, lay,
+                                     s) == INVAL
+    assert lib.tria_calib_add_layers(cal.handle, 0, 2, _p(q, 0), tria.TRIA_Q_F32, T, row,
+                                     lay - 1, s) == INVAL
+    assert lib.tria_calib_add_layers(cal.handle, 0, 2, _p(q, 2), tria.TRIA_Q_F32, T, row, lay,
+                                     s) == INVAL
+    assert [cal.tokens(l) for l in range(L)] == [0, 0, 0]
+    # one layer ignores the layer stride
+    assert lib.tria_calib_add_layers(cal.handle, 2, 1, _p(q, 0), tria.TRIA_Q_F32, T, row, 0,
+                                     s) == 0
+    assert lib.tria_calib_add_layers(cal.handle, 0, 2, _p(q, 0), tria.TRIA_Q_F32, T, row, lay,
+                                     s) == 0
+    assert [cal.tokens(l) for l in range(L)] == [T, T, T]
+    torch.cuda.synchronize()
+    cal.close()

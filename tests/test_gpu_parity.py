@@ -1106,6 +1106,51 @@ def test_calib_stats_match_the_oracle(dtype):
     cal.close()
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("hd,layout", [(64, "dense"), (64, "padded"), (64, "odd_layer_stride"),
+                                       (36, "padded")])
+def test_calib_add_layers_equals_per_layer_adds(dtype, hd, layout):
+    """One tria_calib_add_layers call over four layers (and a two-call split of
+    them) gives the statistics of four tria_calib_add calls bit for bit, whatever
+    the strides: dense [L, T, Hq*hd], rows and layers padded, a layer stride that
+    is not a multiple of 4 elements (the element-wise kernel), and a head_dim
+    whose pair count is not a multiple of 4.  The per-layer result is checked
+    against the oracle as above."""
+    L, Hq, T = 4, 6, 700
+    row = Hq * hd
+    rng = np.random.default_rng(62)
+    pu.say("case calib_add_layers %s hd%d %s" % (dtype, hd, layout))
+    x = (rng.standard_normal((L, 1, Hq * hd)) * 0.7 +
+         rng.standard_normal((L, T, Hq * hd))).astype(np.float32)
+    rs = row if layout == "dense" else row + 40
+    ls = T * rs if layout == "dense" else (T + 3) * rs + (1 if layout == "odd_layer_stride" else 0)
+    flat = torch.zeros(L * ls + 64, dtype=dtype)
+    q = torch.as_strided(flat, (L, T, row), (ls, rs, 1))
+    q.copy_(torch.from_numpy(x).to(dtype))
+    qv = q.float().numpy().reshape(L, T, Hq, hd)  # the values added
+    dev = flat.to(DEV)
+    qd = torch.as_strided(dev, (L, T, row), (ls, rs, 1))
+    per, one, split = (tria.TriaCalib(L, Hq, hd) for _ in range(3))
+    for l in range(L):
+        per.add(l, qd[l])
+    one.add_layers(0, qd)
+    split.add_layers(0, qd[:1])
+    split.add_layers(1, qd[1:])
+    assert [one.tokens(l) for l in range(L)] == [T] * L == [split.tokens(l) for l in range(L)]
+    a, b, c = per.finish(), one.finish(), split.finish()
+    for name, ta, tb, tc in zip(("q_re", "q_im", "q_abs", "w"), a, b, c):
+        assert torch.equal(ta, tb), name
+        assert torch.equal(ta, tc), name
+    for l in (0, L - 1):
+        o = oracle.calib_stats(qv[l])
+        scale = np.maximum(o[2], 1e-3)
+        for g, oo, name in zip((pu.host(t)[l] for t in b), o, ("q_re", "q_im", "q_abs", "w")):
+            err = np.abs(g.astype(np.float64) - oo)
+            assert np.all(err <= 1e-6 * scale), "%s layer %d: max err %g" % (name, l, err.max())
+    for cal in (per, one, split):
+        cal.close()
+
+
 def test_calib_feeds_the_eviction_pass():
     """Statistics accumulated on the GPU load into a context and drive a pass that
     matches the oracle run with the same statistics."""
