@@ -238,6 +238,7 @@ int tria_calib_add_layers(tria_calib* c, int32_t layer0, int32_t n_layers, const
     if (!c || !q || layer0 < 0 || n_layers < 1 || n_layers > c->L - layer0 || n_tokens < 0)
         return TRIA_E_INVAL;
     if (row_stride < (int64_t)c->Hq * c->hd) return TRIA_E_INVAL;
+    if (n_tokens > INT64_MAX / row_stride) return TRIA_E_INVAL;  // rows past any address
     if (n_layers > 1 && layer_stride < n_tokens * row_stride) return TRIA_E_INVAL;
     if (n_layers > 65535) return TRIA_E_UNSUPPORTED;
     if (q_type != TRIA_Q_F32 && q_type != TRIA_Q_F16 && q_type != TRIA_Q_BF16)

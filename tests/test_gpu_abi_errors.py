@@ -236,6 +236,9 @@ def test_calibration_add_layers_refusals():
                                      lay - 1, s) == INVAL
     assert lib.tria_calib_add_layers(cal.handle, 0, 2, _p(q, 2), tria.TRIA_Q_F32, T, row, lay,
                                      s) == INVAL
+    # a row count whose span overflows 64 bits
+    assert lib.tria_calib_add_layers(cal.handle, 0, 2, _p(q, 0), tria.TRIA_Q_F32, 1 << 62, row,
+                                     lay, s) == INVAL
     assert [cal.tokens(l) for l in range(L)] == [0, 0, 0]
     # one layer ignores the layer stride
     assert lib.tria_calib_add_layers(cal.handle, 2, 1, _p(q, 0), tria.TRIA_Q_F32, T, row, 0,
