@@ -58,18 +58,30 @@ def _columns(c, table):
     return [r[1] for r in c.execute("pragma table_info(%s)" % table)]
 
 
+LIBRARY_KERNELS = ("tria::", "calib_")  # the library's kernels, as short() names them
+
+
+def _library(k):
+    return k.startswith(LIBRARY_KERNELS)
+
+
 def trace(d, skip=0):
-    """skip: leave out each kernel's first `skip` dispatches (e.g. a one-off first pass)."""
+    """skip: leave out each kernel's first `skip` dispatches (e.g. a one-off first pass).
+    Launches of one kernel with several grid layers (z > 1) are listed apart."""
     rows = {}
     for db in _dbs(d):
         c = sqlite3.connect(db)
         cols = _columns(c, "kernels")
         order = "start" if "start" in cols else "rowid"
+        z = "grid_z / max(workgroup_z, 1)" if "grid_z" in cols and "workgroup_z" in cols else "1"
         seen = {}
-        for name, dur in c.execute("select name, duration from kernels order by %s" % order):
+        for name, dur, gz in c.execute("select name, duration, %s from kernels order by %s" %
+                                       (z, order)):
             k = short(name)
+            if _library(k) and gz and gz > 1:
+                k += " (grid z %d)" % gz
             seen[k] = seen.get(k, 0) + 1
-            if k.startswith("tria::") and seen[k] <= skip:
+            if _library(k) and seen[k] <= skip:
                 continue
             a = rows.setdefault(k, [0, 0.0])
             a[0] += 1
@@ -77,7 +89,7 @@ def trace(d, skip=0):
     out = ["| kernel | calls | avg us | total us |", "|---|---|---|---|"]
     other = [0, 0.0]
     for k, (n, tot) in sorted(rows.items(), key=lambda x: -x[1][1]):
-        if k.startswith("tria::"):
+        if _library(k):
             out.append("| %s | %d | %.1f | %.1f |" % (k, n, tot / n / 1e3, tot / 1e3))
         else:
             other[0] += n

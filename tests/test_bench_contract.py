@@ -57,3 +57,29 @@ def test_committed_counter_summaries_are_well_formed():
         assert rec["stage"] in STAGE_SOURCES and f == "traffic_%s_%s.txt" % (rec["stage"],
                                                                               rec["workload"])
         assert rec["bytes_per_launch"] > 0 and len(rec["sources_sha256_16"]) == 16
+
+
+def test_trace_summary_lists_library_kernels_by_grid_layers(tmp_path):
+    """The trace table names the library's kernels (tria:: and the calibration
+    kernels), lists one-launch multi-layer calls apart, and folds the rest."""
+    import sqlite3
+
+    from kv_cache_eviction_tria_amd import profile_summary as ps
+    db = sqlite3.connect(str(tmp_path / "k_results.db"))
+    db.execute("create table kernels (name text, duration int, start int, grid_z int, "
+               "workgroup_z int)")
+    rows = [("void tria::prep_kernel(int)", 5000, 1, 1, 1),
+            ("void tria::prep_kernel(int)", 7000, 2, 1, 1),
+            ("void (anonymous namespace)::calib_partial4_kernel<float>(float const*)", 10000, 3, 1, 1),
+            ("void (anonymous namespace)::calib_partial4_kernel<float>(float const*)", 240000, 4, 36, 1),
+            ("void at::native::elementwise_kernel<int>(int)", 3000, 5, 1, 1)]
+    db.executemany("insert into kernels values (?, ?, ?, ?, ?)", rows)
+    db.commit()
+    db.close()
+    out = ps.trace(str(tmp_path)).splitlines()
+    assert "| tria::prep_kernel | 2 | 6.0 | 12.0 |" in out
+    assert "| calib_partial4_kernel<float> | 1 | 10.0 | 10.0 |" in out
+    assert "| calib_partial4_kernel<float> (grid z 36) | 1 | 240.0 | 240.0 |" in out
+    assert out[-1].endswith("| 1 | | 3.0 |")
+    skipped = ps.trace(str(tmp_path), skip=1).splitlines()
+    assert "| tria::prep_kernel | 1 | 7.0 | 7.0 |" in skipped
