@@ -420,8 +420,8 @@ int tria_device_status(tria_ctx *ctx);
 /* Per-kernel timing of the passes run through a context (a trace facility,
  * off by default).  While enabled, every score, select and compaction launch
  * made by the entry points above is bracketed by HIP events recorded on the
- * stream the kernel runs on (the context's second stream for overlapped
- * compactions).  At most TRIA_TIMED_MAX launches are recorded between two
+ * caller's stream, which every kernel of a pass runs on.  At most
+ * TRIA_TIMED_MAX launches are recorded between two
  * reads; later ones are counted in the read's return value and not timed.
  * enable: 1 turns timing on, 0 off (pending records are discarded). */
 #define TRIA_TIMED_MAX 256
