@@ -644,6 +644,25 @@ def bench_decode(args, wl):
         ctx.close()
     kb, vb = synth.row_bytes(wl.k_type, wl.hd), synth.row_bytes(wl.v_type, wl.hd)
     units = wl.L * wl.Hkv
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: oracle decode attention over whole units of the dense cache")
+        G, spent, nu = wl.Hq // wl.Hkv, 0.0, 0
+        scale = 1.0 / float(wl.hd) ** 0.5
+        while nu < units and (nu == 0 or spent < min(args.cpu_seconds, 10.0)):
+            l, g = divmod(nu, wl.Hkv)
+            kr, vr = k0[l, g, :n0].cpu().numpy(), v0[l, g, :n0].cpu().numpy()
+            qq = q[l, g * G:(g + 1) * G].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.decode_attention_unit(wl.k_type, wl.v_type, kr, vr, wl.hd, qq, scale)
+            spent += time.perf_counter() - t0
+            nu += 1
+        cpu = {"value": nu / (spent * units), "unit": "decode steps/s (dense attention, all layers)",
+               "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
+               "sample": "attention of %d of %d (layer, KV head) units over %d rows each, "
+                         "%.1f s; compare with dense.steps_per_s" % (nu, units, n0, spent)}
+    res["dense"]["steps_per_s"] = 1e3 / res["dense"]["ms_median"]
     dense_bytes = res["dense"]["mean_rows"] * units * (kb + vb)
     d_ms, t_ms = res["dense"]["ms_median"], res["tria"]["ms_per_step"]
     achieved = dense_bytes / (d_ms * 1e-3) / 1e9
@@ -671,7 +690,7 @@ def bench_decode(args, wl):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "alg_bytes_per_launch": dense_bytes,
                      "launches_per_step": 1, "avg_launch_ms": d_ms},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
 
 
