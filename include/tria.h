@@ -393,8 +393,11 @@ int tria_calib_add(tria_calib *c, int32_t layer, const void *q, int32_t q_type, 
  * at once (one kernel launch for all of them; per-layer launches of a few tens
  * of MB are dominated by their start and tail): layer layer0 + i's rows start
  * at element i * layer_stride of q (layer_stride >= n_tokens * row_stride when
- * n_layers > 1, so that layers do not overlap).  Each layer's sums are formed
- * exactly as by tria_calib_add, so the statistics are the same bit for bit.
+ * n_layers > 1, so that layers do not overlap).  A call over many layers
+ * spreads each layer's tokens over fewer accumulator slots than one-layer calls
+ * do (so that one launch holds a few thousand workgroups), so its sums may
+ * differ from those of per-layer calls in fp64 rounding; for a given sequence
+ * of calls every sum is formed in a fixed order.
  * 1 <= n_layers <= n_layers of the object - layer0. */
 int tria_calib_add_layers(tria_calib *c, int32_t layer0, int32_t n_layers, const void *q,
                           int32_t q_type, int64_t n_tokens, int64_t row_stride,

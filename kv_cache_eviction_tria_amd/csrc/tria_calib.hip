@@ -13,13 +13,17 @@
 // launch.  The layer keeps kCalSlots fp64 accumulators per (pair, sum); the
 // tokens are cut into chunks of 32, and workgroup (column, y) covers 256
 // (head, pair) slots of chunks y, y + S, y + 2S, ... (S = min(chunks,
-// kCalSlots)): four consecutive pairs per lane (one 16-byte load of the real
+// kCalSlots), and fewer when one call adds many layers, so that a launch
+// holds about kCalTargetBlocks workgroups: each slot's read-modify-write and
+// the finish's read of it are then spread over more tokens): four consecutive
+// pairs per lane (one 16-byte load of the real
 // halves and one of the imaginary halves per token; consecutive lanes read
 // consecutive bytes), the tokens dealt over its four wavefronts and their sums
 // combined in LDS in a fixed order, then added into accumulator slot y -- which
 // no other workgroup of the launch touches, and adds on one stream run in
-// order.  tria_calib_finish adds a layer's slots in slot order.  So every sum
-// is formed in an order fixed by the call sequence, never by scheduling.  The
+// order.  tria_calib_finish adds a layer's slots in slot order (the slots any
+// call used).  So every sum is formed in an order fixed by the call sequence,
+// never by scheduling.  The
 // pair magnitude is formed in fp32 (the inputs are at most fp32), the sums in
 // fp64.
 #include <new>
@@ -32,6 +36,7 @@ constexpr int kCalThreads = 256;
 constexpr int kCalTok = 32;    // tokens per chunk
 constexpr int kCalSlots = 64;  // accumulator slots per layer (workgroup rows of a launch)
 constexpr int kCalMaxLayers = 128;  // layers finished per launch
+constexpr int64_t kCalTargetBlocks = 4608;  // workgroups a many-layer add aims for
 
 template <typename QT>
 __device__ __forceinline__ float q_load(const QT* p);
@@ -161,6 +166,7 @@ __global__ __launch_bounds__(kCalThreads) void calib_partial_kernel(
 // Token counts of up to kCalMaxLayers layers, passed by value.
 struct CalCounts {
     int64_t n[kCalMaxLayers];
+    int slots[kCalMaxLayers];  // accumulator slots in use
 };
 
 // Outputs of layers l0 .. l0 + gridDim.y - 1 from their sums (zeros for a
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kCalThreads) void calib_finish_kernel(const double*
     // the layer's slots, in slot order
     const double* a = acc + ((int64_t)l * kCalSlots * HF + i) * 3;
     double sr = 0.0, si = 0.0, sa = 0.0;
-    for (int y = 0; y < kCalSlots; ++y) {
+    for (int y = 0; y < cnt.slots[blockIdx.y]; ++y) {
         sr += a[(int64_t)y * HF * 3];
         si += a[(int64_t)y * HF * 3 + 1];
         sa += a[(int64_t)y * HF * 3 + 2];
@@ -196,6 +202,7 @@ struct tria_calib {
     int L, Hq, hd, F, HF;
     double* acc = nullptr;      // [L][kCalSlots][HF][3]
     int64_t* count = nullptr;   // host [L]
+    int* slots = nullptr;       // host [L]: accumulator slots any add has used
 };
 
 extern "C" {
@@ -213,8 +220,9 @@ int tria_calib_create(tria_calib** out, int32_t n_layers, int32_t n_q_heads, int
     c->F = head_dim / 2;
     c->HF = n_q_heads * c->F;
     c->count = static_cast<int64_t*>(calloc((size_t)n_layers, sizeof(int64_t)));
+    c->slots = static_cast<int*>(calloc((size_t)n_layers, sizeof(int)));
     const size_t bytes = (size_t)n_layers * kCalSlots * c->HF * 3 * sizeof(double);
-    hipError_t e = c->count ? hipMalloc(reinterpret_cast<void**>(&c->acc), bytes) : hipErrorOutOfMemory;
+    hipError_t e = c->count && c->slots ? hipMalloc(reinterpret_cast<void**>(&c->acc), bytes) : hipErrorOutOfMemory;
     if (e == hipSuccess) e = hipMemset(c->acc, 0, bytes);
     if (e == hipSuccess) e = hipDeviceSynchronize();  // zeroed before any stream's add
     if (e != hipSuccess) {
@@ -229,6 +237,7 @@ void tria_calib_free(tria_calib* c) {
     if (!c) return;
     if (c->acc) (void)hipFree(c->acc);
     free(c->count);
+    free(c->slots);
     delete c;
 }
 
@@ -246,7 +255,6 @@ int tria_calib_add_layers(tria_calib* c, int32_t layer0, int32_t n_layers, const
     if (reinterpret_cast<uintptr_t>(q) % (q_type == TRIA_Q_F32 ? 4 : 2) != 0) return TRIA_E_INVAL;
     if (n_tokens == 0) return TRIA_OK;
     const int64_t chunks = (n_tokens + kCalTok - 1) / kCalTok;
-    const unsigned S = (unsigned)(chunks < kCalSlots ? chunks : kCalSlots);
     double* slot = c->acc + (int64_t)layer0 * kCalSlots * c->HF * 3;
     const int64_t slot_layer = (int64_t)kCalSlots * c->HF * 3;
     const int64_t q_layer = n_layers > 1 ? layer_stride : 0;
@@ -255,11 +263,13 @@ int tria_calib_add_layers(tria_calib* c, int32_t layer0, int32_t n_layers, const
     const size_t esz = q_type == TRIA_Q_F32 ? 4 : 2;
     const bool aligned = (reinterpret_cast<uintptr_t>(q) % (4 * esz)) == 0 && row_stride % 4 == 0 &&
                          q_layer % 4 == 0;
+    const int64_t cols = vec && aligned ? (c->HF + 255) / 256 : (c->HF + kCalThreads - 1) / kCalThreads;
+    int64_t want = (kCalTargetBlocks + cols * n_layers - 1) / (cols * n_layers);
+    want = want < kCalSlots ? want : kCalSlots;
+    const unsigned S = (unsigned)(chunks < want ? chunks : want);
     // vector path: 256 pairs per block; scalar path: one pair per thread; one
     // grid layer per query layer
-    const dim3 grid(vec && aligned ? (unsigned)((c->HF + 255) / 256)
-                                   : (unsigned)((c->HF + kCalThreads - 1) / kCalThreads),
-                    S, (unsigned)n_layers);
+    const dim3 grid((unsigned)cols, S, (unsigned)n_layers);
     if (q_type == TRIA_Q_F32) {
         auto k = vec && aligned ? calib_partial4_kernel<float> : calib_partial_kernel<float>;
         hipLaunchKernelGGL(k, grid, dim3(kCalThreads), 0, stream, static_cast<const float*>(q),
@@ -274,7 +284,10 @@ int tria_calib_add_layers(tria_calib* c, int32_t layer0, int32_t n_layers, const
                            n_tokens, row_stride, c->F, c->hd, c->HF, slot, q_layer, slot_layer);
     }
     if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;
-    for (int i = 0; i < n_layers; ++i) c->count[layer0 + i] += n_tokens;
+    for (int i = 0; i < n_layers; ++i) {
+        c->count[layer0 + i] += n_tokens;
+        if ((int)S > c->slots[layer0 + i]) c->slots[layer0 + i] = (int)S;
+    }
     return TRIA_OK;
 }
 
@@ -295,7 +308,10 @@ int tria_calib_finish(tria_calib* c, float* q_re, float* q_im, float* q_abs, flo
     for (int l0 = 0; l0 < c->L; l0 += kCalMaxLayers) {
         const int nl = c->L - l0 < kCalMaxLayers ? c->L - l0 : kCalMaxLayers;
         CalCounts cnt;
-        for (int j = 0; j < kCalMaxLayers; ++j) cnt.n[j] = j < nl ? c->count[l0 + j] : 0;
+        for (int j = 0; j < kCalMaxLayers; ++j) {
+            cnt.n[j] = j < nl ? c->count[l0 + j] : 0;
+            cnt.slots[j] = j < nl ? c->slots[l0 + j] : 0;
+        }
         hipLaunchKernelGGL(calib_finish_kernel, dim3(blocks, (unsigned)nl), dim3(kCalThreads), 0,
                            stream, c->acc, c->HF, l0, cnt, q_re, q_im, q_abs, norm_w);
         if (hipGetLastError() != hipSuccess) return TRIA_E_HIP;

@@ -1108,46 +1108,52 @@ def test_calib_stats_match_the_oracle(dtype):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("hd,layout", [(64, "dense"), (64, "padded"), (64, "odd_layer_stride"),
-                                       (36, "padded")])
+                                       (36, "padded"), (128, "many_layers")])
 def test_calib_add_layers_equals_per_layer_adds(dtype, hd, layout):
     """One tria_calib_add_layers call over four layers (and a two-call split of
-    them) gives the statistics of four tria_calib_add calls bit for bit, whatever
-    the strides: dense [L, T, Hq*hd], rows and layers padded, a layer stride that
-    is not a multiple of 4 elements (the element-wise kernel), and a head_dim
-    whose pair count is not a multiple of 4.  The per-layer result is checked
-    against the oracle as above."""
-    L, Hq, T = 4, 6, 700
+    them) gives the statistics of four tria_calib_add calls, whatever the
+    strides: dense [L, T, Hq*hd], rows and layers padded, a layer stride that is
+    not a multiple of 4 elements (the element-wise kernel), and a head_dim whose
+    pair count is not a multiple of 4.  The many-layer call may group the tokens
+    into fewer accumulator slots, so the bar is the oracle's (1e-6 * q_abs); the
+    same calls repeated give the same bits, and every layer is checked against
+    the oracle."""
+    # many_layers: 12 layers of 32 heads x 128, enough workgroups that the one
+    # call uses fewer accumulator slots than the per-layer calls
+    L, Hq, T = (12, 32, 2000) if layout == "many_layers" else (4, 6, 700)
     row = Hq * hd
     rng = np.random.default_rng(62)
     pu.say("case calib_add_layers %s hd%d %s" % (dtype, hd, layout))
     x = (rng.standard_normal((L, 1, Hq * hd)) * 0.7 +
          rng.standard_normal((L, T, Hq * hd))).astype(np.float32)
-    rs = row if layout == "dense" else row + 40
-    ls = T * rs if layout == "dense" else (T + 3) * rs + (1 if layout == "odd_layer_stride" else 0)
+    dense = layout in ("dense", "many_layers")
+    rs = row if dense else row + 40
+    ls = T * rs if dense else (T + 3) * rs + (1 if layout == "odd_layer_stride" else 0)
     flat = torch.zeros(L * ls + 64, dtype=dtype)
     q = torch.as_strided(flat, (L, T, row), (ls, rs, 1))
     q.copy_(torch.from_numpy(x).to(dtype))
     qv = q.float().numpy().reshape(L, T, Hq, hd)  # the values added
     dev = flat.to(DEV)
     qd = torch.as_strided(dev, (L, T, row), (ls, rs, 1))
-    per, one, split = (tria.TriaCalib(L, Hq, hd) for _ in range(3))
+    per, one, split, again = (tria.TriaCalib(L, Hq, hd) for _ in range(4))
     for l in range(L):
         per.add(l, qd[l])
     one.add_layers(0, qd)
+    again.add_layers(0, qd)
     split.add_layers(0, qd[:1])
     split.add_layers(1, qd[1:])
     assert [one.tokens(l) for l in range(L)] == [T] * L == [split.tokens(l) for l in range(L)]
-    a, b, c = per.finish(), one.finish(), split.finish()
-    for name, ta, tb, tc in zip(("q_re", "q_im", "q_abs", "w"), a, b, c):
-        assert torch.equal(ta, tb), name
-        assert torch.equal(ta, tc), name
-    for l in (0, L - 1):
+    outs = [[pu.host(t) for t in cal.finish()] for cal in (per, one, split)]
+    assert all(torch.equal(x, y) for x, y in zip(one.finish(), again.finish()))
+    for l in range(L):
         o = oracle.calib_stats(qv[l])
         scale = np.maximum(o[2], 1e-3)
-        for g, oo, name in zip((pu.host(t)[l] for t in b), o, ("q_re", "q_im", "q_abs", "w")):
-            err = np.abs(g.astype(np.float64) - oo)
-            assert np.all(err <= 1e-6 * scale), "%s layer %d: max err %g" % (name, l, err.max())
-    for cal in (per, one, split):
+        for which, out in zip(("per-layer", "one call", "split"), outs):
+            for g, oo, name in zip((t[l] for t in out), o, ("q_re", "q_im", "q_abs", "w")):
+                err = np.abs(g.astype(np.float64) - oo)
+                assert np.all(err <= 1e-6 * scale), "%s %s layer %d: max err %g" % (
+                    which, name, l, err.max())
+    for cal in (per, one, split, again):
         cal.close()
 
 
